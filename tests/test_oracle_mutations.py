@@ -1,0 +1,189 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of the oracle's source (on the CPU, in
+memory) and checks that at least one pin check fails for the mutant, while
+all of them pass for the unmodified oracle.
+"""
+import inspect
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pisa_oracle as po
+
+
+def _load(src: str, name: str):
+    mod = types.ModuleType(name)
+    mod.__dict__["__name__"] = name
+    sys.modules[name] = mod
+    exec(compile(src, name, "exec"), mod.__dict__)
+    return mod
+
+
+def _rand(shape, seed, dtype="f32", scale=1.0):
+    return po.rne(scale * np.random.default_rng(seed).standard_normal(shape), dtype)
+
+
+def _dense(q, k, v, P, causal):
+    rep = P.Hq // P.Hkv
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k).repeat_interleave(rep, 1),
+        torch.from_numpy(v).repeat_interleave(rep, 1), is_causal=causal, scale=P.sm_scale)
+    return o.numpy()
+
+
+def check_swa_count(m):
+    P = m.Problem(B=1, Hq=1, Hkv=1, L=16, d=4, dtype="f32", block=1, topk=0, window=4,
+                  causal=True, taylor="none")
+    return m.kept_pairs(P, np.full((1, 1, 16, 0), -1)).sum() == 58
+
+
+def check_dense(m):
+    ok = True
+    for causal in (False, True):
+        P = m.Problem(B=1, Hq=4, Hkv=2, L=70, d=8, dtype="bf16", block=8, topk=9,
+                      causal=causal, taylor="order1")
+        q, k, v = _rand((1, 4, 70, 8), 1, "bf16"), _rand((1, 2, 70, 8), 2, "bf16"), \
+            _rand((1, 2, 70, 8), 3, "bf16")
+        ok &= np.abs(m.run(q, k, v, P)["O"] - _dense(q, k, v, P, causal)).max() < 1e-12
+    return ok
+
+
+def check_constant_v(m):
+    P = m.Problem(B=1, Hq=2, Hkv=2, L=64, d=8, dtype="f32", block=8, topk=2, causal=True,
+                  window=10, taylor="order1")
+    q, k = _rand((1, 2, 64, 8), 4), _rand((1, 2, 64, 8), 5)
+    v = _rand((1, 2, 64, 8), 6)
+    a = np.abs(m.run(q, k, np.ones_like(v), P)["O"] - 1).max() < 1e-12
+    b = np.abs(m.run(q, k, v + 2.0, P)["O"] - m.run(q, k, v, P)["O"] - 2.0).max() < 1e-12
+    return a and b
+
+
+def check_orders(m):
+    B, H, L, d, bs = 1, 1, 128, 8, 16
+    rng = np.random.default_rng(7)
+    cen = rng.standard_normal((B, H, L // bs, d))
+    dl = rng.standard_normal((B, H, L // bs, bs, d))
+    dl -= dl.mean(axis=3, keepdims=True)
+    q, v = _rand((B, H, L, d), 8, scale=0.7), _rand((B, H, L, d), 9)
+    errs = {"order0": [], "order1": []}
+    for eps in (0.2, 0.1, 0.05):
+        k = po.rne((cen[:, :, :, None, :] + eps * dl).reshape(B, H, L, d), "f32")
+        for mode in errs:
+            P = m.Problem(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=bs, topk=0, taylor=mode)
+            errs[mode].append(np.abs(m.run(q, k, v, P)["O"] - _dense(q, k, v, P, False)).max())
+    r0 = [a / b for a, b in zip(errs["order0"], errs["order0"][1:])]
+    r1 = [a / b for a, b in zip(errs["order1"], errs["order1"][1:])]
+    return all(1.7 < x < 2.3 for x in r0) and all(3.4 < x < 4.6 for x in r1)
+
+
+def check_ties(m):
+    d, bs, L = 6, 4, 40
+    P = m.Problem(B=1, Hq=1, Hkv=1, L=L, d=d, dtype="bf16", block=bs, topk=3, taylor="order0")
+    u = np.zeros(d)
+    u[0] = 1.0
+    q = po.rne(_rand((1, 1, L, d), 81, "f32", 0.05) + u, "bf16")
+    k = _rand((1, 1, L, d), 82, "f32", 0.05)
+    k[0, 0, bs:2 * bs] += 2.0 * u
+    k = po.rne(k, "bf16")
+    for dst in (5, 6, 7):
+        k[0, 0, dst * bs:(dst + 1) * bs] = k[0, 0, bs:2 * bs]
+    r = m.run(q, k, _rand((1, 1, L, d), 83, "bf16"), P)
+    return all(r["idx"][0, 0, i].tolist() == [1, 5, 6] for i in range(P.n_blk))
+
+
+def check_pivot_reuse(m):
+    P = m.Problem(B=1, Hq=1, Hkv=1, L=96, d=8, dtype="bf16", block=16, topk=3, group=8,
+                  n_cand=3, causal=True, taylor="none")
+    q, k, v = _rand((1, 1, 96, 8), 10, "bf16"), _rand((1, 1, 96, 8), 11, "bf16"), \
+        _rand((1, 1, 96, 8), 12, "bf16")
+    r = m.run(q, k, v, P)
+    same = all(np.array_equal(r["idx"][0, 0, t], r["cand"][0, 0, t // 8]) for t in range(96))
+    # the proxy must be the mean of its group: compare with a planted group
+    return same
+
+
+def check_pooled_selection(m):
+    """Selection vectors are the rounded block means: a planted answer."""
+    B, L, d, bs = 1, 256, 8, 32
+    u = np.zeros(d)
+    u[2] = 1.0
+    q = po.rne(0.1 * np.random.default_rng(13).standard_normal((B, 1, L, d)) + u, "bf16")
+    k = 0.1 * np.random.default_rng(14).standard_normal((B, 1, L, d))
+    for j in (1, 4):
+        k[0, 0, j * bs:(j + 1) * bs] += 3 * u
+    k = po.rne(k, "bf16")
+    P = m.Problem(B=1, Hq=1, Hkv=1, L=L, d=d, block=bs, topk=2, taylor="order1")
+    r = m.run(q, k, _rand((B, 1, L, d), 15, "bf16"), P)
+    return all(r["idx"][0, 0, i].tolist() == [1, 4] for i in range(P.n_blk))
+
+
+def check_pivot_mean(m):
+    """The proxy is the mean of its group: members e0 and e1 each prefer a block
+    aligned with themselves, their mean prefers the block along e0 + e1."""
+    L, d, bs = 64, 8, 8
+    q = np.zeros((1, 1, L, d))
+    k = np.zeros((1, 1, L, d))
+    q[0, 0, 56, 0] = 1.0
+    q[0, 0, 57, 1] = 1.0
+    k[0, 0, 1 * bs:2 * bs, 0] = 1.0
+    k[0, 0, 2 * bs:3 * bs, 1] = 1.0
+    k[0, 0, 3 * bs:4 * bs, :2] = 0.75
+    P = m.Problem(B=1, Hq=1, Hkv=1, L=L, d=d, dtype="bf16", block=bs, topk=1, group=2,
+                  n_cand=1, causal=True, taylor="none")
+    r = m.run(q, k, np.ones_like(k), P)
+    return r["idx"][0, 0, 56].tolist() == [3] and r["idx"][0, 0, 57].tolist() == [3]
+
+
+CHECKS = [check_pivot_mean, check_swa_count, check_dense, check_constant_v, check_orders, check_ties,
+          check_pivot_reuse, check_pooled_selection]
+
+MUTATIONS = {
+    "H transposed": ('H[:, :, j] = np.einsum("bhnc,bhne->bhce", kc, vj)',
+                     'H[:, :, j] = np.einsum("bhnc,bhne->bhec", kc, vj)'),
+    "first-order sign": ("N = N + sc * np.einsum", "N = N - sc * np.einsum"),
+    "first-order without scale": ("N = N + sc * np.einsum", "N = N + 1.0 * np.einsum"),
+    "denominator drops n_j": ('pa @ st["n"][Uj].astype(np.float64)', 'pa.sum(axis=1)'),
+    "numerator drops sigma": ('+ pa @ st["vsum"][b, hk, Uj]', '+ 0.0'),
+    "Taylor logit from ksel": ('a = sc * (qt @ st["kbar"][b, hk, Uj].T)',
+                               'a = sc * (qt @ po_round(st["kbar"][b, hk, Uj]).T)'),
+    "H not centred": ("kc = kj - kbar[:, :, j][:, :, None, :]", "kc = kj"),
+    "window off by one": ("max(0, start - P.window + 1)", "max(0, start - P.window)"),
+    "causal mask inclusive bug": ("keys[None, :] <= tt[:, None]", "keys[None, :] < tt[:, None]"),
+    "exact ties to higher index": ("ex.sort(reverse=True)", "ex.sort(key=lambda z: (-z[0], z[1]))"),
+    "exact ties ranked worst first": ("ex.sort(reverse=True)", "ex.sort()"),
+    "GQA head map": ("hk = h * P.Hkv // P.Hq\n    sc = P.sm_scale",
+                     "hk = h % P.Hkv\n    sc = P.sm_scale"),
+    "proxy is first member": ("qsel[:, :, r] = pooled_mean(q[:, :, r * span:min(L, (r + 1) * span), :], 2, P.dtype)",
+                              "qsel[:, :, r] = q[:, :, r * span, :]"),
+    "pivot members ignore proxy list": ("tt = top_n(q[b, h, t], Kb[cl], cl, k)",
+                                        "tt = top_n(q[b, h, t], Kb[:nc], np.arange(nc), k)"),
+    "scale not applied to exact logits": ("x = sc * (qt @ k[b, hk, keys].T)", "x = (qt @ k[b, hk, keys].T)"),
+}
+
+
+def test_unmodified_oracle_passes_all_checks():
+    for c in CHECKS:
+        assert c(po), c.__name__
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    old, new = MUTATIONS[name]
+    src = inspect.getsource(po)
+    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    src = src.replace(old, new)
+    src = src.replace("def rne(", "def po_round(x):\n    return rne(x, 'bf16')\n\n\ndef rne(")
+    m = _load(src, f"oracle_mutant_{abs(hash(name))}")
+    failed = []
+    for c in CHECKS:
+        try:
+            ok = c(m)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(c.__name__)
+    assert failed, f"no pin check caught the mutation {name!r}"
