@@ -1,0 +1,188 @@
+/*
+ * pisa.h -- C ABI of libpisa, block-sparse attention with training-free block
+ * selection for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the forward pass the following pages describe together:
+ *   [PISA]  "PISA: Piecewise Sparse Attention Is Wiser for Efficient Diffusion
+ *           Transformers" -- technical summary, section 2 (core algorithm:
+ *           o_t = N_t / D_t with exact terms over the selected blocks and a
+ *           block-level Taylor term around the mean key for every other
+ *           block, inside both N_t and D_t; hardware implementation:
+ *           precompute centroids and value sums, then one fused
+ *           online-softmax kernel).
+ *   [PIVOT] "PIVOT slashes sparse-attention indexer cost 4x ..." -- section
+ *           "Two observations behind PIVOT", steps 1-4 (one averaged proxy
+ *           query per group of g consecutive queries scores the blocks; the
+ *           proxy's candidate list is re-ranked per member).
+ *   [SWA]   "Sliding Window Attention" -- causal window 0 <= t - s < w
+ *           (section "How the window widens with depth"); window-aware kernels
+ *           skip blocks outside the kept set entirely (related term
+ *           "FlashAttention").
+ *
+ * Three calls make one forward pass, all asynchronous on the caller's stream:
+ *   pisa_block_stats     mean-pooled block statistics (stage A)
+ *   pisa_indexer_topk    block scores and top-k selection (stage B)
+ *   pisa_sparse_attn_fwd exact attention over kept blocks + per-block
+ *                        first-order Taylor tail for the rest (stage C)
+ *
+ * Conventions shared by every call
+ *   Layout   Q: [B, Hq, L, d]; K, V: [B, Hkv, L, d]; O like Q.  Contiguous,
+ *            d fastest, base pointers 16-byte aligned.  Query head h uses KV
+ *            head h * Hkv / Hq (consecutive query heads share a KV head).
+ *   Blocks   bs = block; n_blk = ceil(L / bs); block j holds tokens
+ *            [j*bs, min(L, (j+1)*bs)) and n_j of them.
+ *   Memory   The caller allocates and owns every buffer (inputs, statistics,
+ *            index lists, outputs, workspace).  The library allocates no
+ *            device memory, keeps no global state other than a thread-local
+ *            error text, and is re-entrant.
+ *   Errors   Every precondition is checked on the host before anything is
+ *            launched.  On failure a call returns a non-zero status, writes
+ *            nothing and launches nothing; pisa_last_error() gives the
+ *            reason.  A failed launch returns PISA_E_HIP.
+ *   Async    Calls only enqueue kernels on `stream`; no host synchronisation
+ *            and no host<->device copies happen inside.
+ *   Results  Deterministic: bitwise identical from run to run.
+ *   Inputs   Q, K, V values must be finite.
+ */
+#ifndef PISA_H
+#define PISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PISA_ABI_VERSION 1
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_E_ARG = 1,          /* invalid argument (null, shape, range, alignment) */
+  PISA_E_UNSUPPORTED = 2,  /* valid but not implemented (d, block size, ...) */
+  PISA_E_WORKSPACE = 3,    /* workspace missing or too small */
+  PISA_E_HIP = 4           /* a HIP launch failed; see pisa_last_error() */
+} pisa_status;
+
+typedef enum { PISA_BF16 = 0, PISA_F32 = 1 } pisa_dtype;
+
+/* Treatment of non-kept candidate blocks ([PISA] section 2). */
+typedef enum {
+  PISA_TAYLOR_NONE = 0,    /* drop them (keep-or-drop block sparsity) */
+  PISA_TAYLOR_ORDER0 = 1,  /* exp(q.kbar_j) * sum_n v_n ; exp(q.kbar_j) * n_j */
+  PISA_TAYLOR_ORDER1 = 2   /* adds exp(q.kbar_j) * q H_j to the numerator */
+} pisa_taylor;
+
+/* Problem statement.  Supported today: d in {64, 128}; block in {64, 128};
+ * 1 <= Hq/Hkv <= 8 with Hq % Hkv == 0; n_blk <= 1024; topk <= 64;
+ * n_cand <= 256. */
+typedef struct {
+  int32_t B, Hq, Hkv, L, d;
+  int32_t dtype;    /* pisa_dtype of Q, K, V and O */
+  int32_t block;    /* bs: key and query block size in tokens */
+  int32_t topk;     /* k kept blocks per row beyond the window / own block; 0 allowed */
+  int32_t window;   /* causal window w in tokens (0 = none); requires causal */
+  int32_t group;    /* 0: one selection row per query block (mean-pooled query);
+                       g >= 1: one selection row per token, PIVOT proxies of g
+                       consecutive queries (block % g == 0); g = 1 with
+                       n_cand >= n_blk is the dense per-token indexer */
+  int32_t n_cand;   /* PIVOT proxy list length C >= topk (C == topk: PIVOT-Reuse) */
+  int32_t causal;   /* 0 or 1 */
+  int32_t taylor;   /* pisa_taylor */
+  float scale;      /* softmax scale; <= 0 selects 1/sqrt(d) */
+} pisa_params;
+
+/* Block statistics ([PISA] precompute; [PIVOT] step 2).  Caller-allocated,
+ * sizes from pisa_stats_layout().
+ *   qsel  dtype [B, Hq, n_sel, d]: RNE_dtype(float64 mean of the query rows of
+ *         block i) for group == 0 (n_sel = n_blk), or of the g queries of
+ *         PIVOT group gamma (n_sel = ceil(L / g); a last partial group
+ *         averages its actual members)
+ *   ksel  dtype [B, Hkv, n_blk, d]: RNE_dtype(float64 mean key of block j)
+ *   kbar  fp32 [B, Hkv, n_blk, d]: the mean key, rounded to fp32 (Taylor term)
+ *   vsum  fp32 [B, Hkv, n_blk, d]: sum of the block's value rows
+ *   HT    [B, Hkv, n_blk, d, d], bf16 for bf16 inputs and fp32 for fp32
+ *         inputs: the transposed first-order matrix,
+ *         HT[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c)
+ * kbar, vsum and HT are read only when taylor != NONE and may be NULL then. */
+typedef struct {
+  void *qsel;
+  void *ksel;
+  float *kbar;
+  float *vsum;
+  void *HT;
+} pisa_stats;
+
+/* ---- host-only queries (no GPU needed) ---------------------------------- */
+
+/* Check a problem statement; PISA_OK if every call can run it. */
+pisa_status pisa_validate(const pisa_params *p);
+
+/* Byte sizes of the five statistics buffers, in pisa_stats field order
+ * (qsel, ksel, kbar, vsum, HT). */
+pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]);
+
+/* Byte sizes of the index list idx (int32 [B, Hq, n_rows, topk], n_rows =
+ * n_blk for group == 0 else L) and of the PIVOT proxy list cand (int32
+ * [B, Hq, ceil(L / g), n_cand]; 0 when group == 0). */
+pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]);
+
+/* Workspace bytes call `op` needs (0 = block_stats, 1 = indexer_topk,
+ * 2 = sparse_attn_fwd).  All three need none today; a non-NULL workspace of
+ * at least PISA_DIAG_BYTES passed to pisa_indexer_topk receives diagnostic
+ * counters (int32: rows, rows decided by exact rational re-scoring,
+ * candidates re-scored exactly). */
+#define PISA_DIAG_BYTES 64
+pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes);
+
+/* ---- the hot path ------------------------------------------------------- */
+
+/* Stage A.  Reads Q, K, V; writes every non-NULL statistics buffer of *out
+ * (qsel and ksel are required; kbar, vsum, HT when taylor != NONE). */
+pisa_status pisa_block_stats(const pisa_params *p, const void *Q, const void *K,
+                             const void *V, const pisa_stats *out, void *ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Stage B ([PISA] covariance-free routing by attention score; [PIVOT] steps
+ * 1-4; [SWA] window).  Per selection row r the score of candidate block j is
+ * the exact real dot product qsel_r . ksel_j (PIVOT members: q_t . ksel_j);
+ * the kept set T_r is the top-min(k, |cand_r|) candidates, ties to the lower
+ * block index.  Candidates: every block when non-causal; when causal, blocks
+ * [0, lo_r) where lo_r = blk(max(0, start_r - w + 1)) (w > 0) or the row's
+ * own block (w = 0), start_r being the first token of the row; the range
+ * [lo_r, own block] is kept implicitly and not stored.  PIVOT: the proxy of
+ * group gamma keeps the top-min(C, |cand|) of its first member's candidates;
+ * each member keeps the top-min(k, C') of that list by its own score.
+ * Writes idx (ascending, -1 padded) and, if non-NULL, cand. */
+pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_stats *stats,
+                              int32_t *idx, int32_t *cand, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Stage C ([PISA] section 2 with the per-block first-order term).  For token
+ * t in selection row r, with q_s = scale * q_t:
+ *   E_t = tokens of the blocks in T_r u [lo_r, own] (s <= t when causal)
+ *   U_t = candidates of r not in T_r (empty when taylor == NONE)
+ *   N_t = sum_{s in E_t} e^{q_s.k_s} v_s
+ *       + sum_{j in U_t} e^{q_s.kbar_j} (vsum_j + [ORDER1] q_s H_j)
+ *   D_t = sum_{s in E_t} e^{q_s.k_s} + sum_{j in U_t} e^{q_s.kbar_j} n_j
+ *   O_t = N_t / D_t rounded to nearest-even in dtype;
+ *   lse_t = max-shifted ln D_t (fp32 [B, Hq, L]) if lse != NULL.
+ * idx may come from pisa_indexer_topk or from the caller (e.g. lists reused
+ * from another layer); entries must be ascending, -1 padded, and lie in the
+ * row's candidate range. */
+pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void *K,
+                                 const void *V, const pisa_stats *stats, const int32_t *idx,
+                                 void *O, float *lse, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* ---- errors and version -------------------------------------------------- */
+const char *pisa_status_string(pisa_status s);
+const char *pisa_last_error(void);  /* thread-local detail of the last failure */
+int pisa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PISA_H */

@@ -1,0 +1,58 @@
+// Internal interface between the host layer (pisa_host.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// Problem geometry derived from pisa_params on the host, passed by value to
+// every kernel.
+struct PisaDims {
+  int B, Hq, Hkv, L, d;
+  int dtype;       // 0 bf16, 1 fp32
+  int bs;          // block size
+  int n_blk;       // ceil(L / bs)
+  int topk;
+  int window;
+  int group;       // 0: block rows; >= 1 PIVOT
+  int n_cand;
+  int causal;
+  int taylor;      // 0 none, 1 order0, 2 order1
+  int ratio;       // Hq / Hkv
+  int n_sel;       // rows of qsel
+  int n_rows;      // rows of idx
+  float scale;     // softmax scale (resolved)
+};
+
+// Selection-row geometry shared by the indexer and the attention kernels.
+// Returns the number of candidate blocks; *own and *lo receive the row's own
+// block and the first block of its exact window range (lo == own without a
+// window; non-causal rows have no range and lo = n_blk).
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline int pisa_row_geometry(const PisaDims &dm, int start_token, int *own, int *lo) {
+  const int o = start_token / dm.bs;
+  *own = o;
+  if (!dm.causal) {
+    *lo = dm.n_blk;
+    return dm.n_blk;
+  }
+  int l = o;
+  if (dm.window > 0) {
+    int s = start_token - dm.window + 1;
+    l = (s > 0 ? s : 0) / dm.bs;
+  }
+  *lo = l;
+  return l;
+}
+
+// launchers (return the hipError_t of the launch)
+hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, const void *V,
+                              void *qsel, void *ksel, float *kbar, float *vsum, void *HT,
+                              hipStream_t st);
+hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
+                          int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);
+hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const void *V,
+                       const float *kbar, const float *vsum, const void *HT, const int32_t *idx,
+                       void *O, float *lse, hipStream_t st);

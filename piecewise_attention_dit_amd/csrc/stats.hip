@@ -1,0 +1,348 @@
+// Stage A: mean-pooled block statistics (PISA page, section 2: precompute of
+// block centroids, value sums and per-block first-order matrices; PIVOT page,
+// step 2: the proxy query is the mean of its group).
+//
+//   kv_stats_*   one workgroup per (b, kv head, key block j):
+//                ksel_j = RNE_dtype(mean key), kbar_j = fp32(mean key),
+//                vsum_j = sum of value rows, HT_j[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c)
+//   q_pool       one thread per (selection row, 16-byte column chunk):
+//                qsel = RNE_dtype(mean of the row's queries)
+//
+// The means are float64 cascaded sums divided once (IEEE division) and rounded
+// once into the dtype.  HBM-bound: Q, K and V are read exactly once.
+#include "device_common.h"
+
+namespace {
+
+constexpr int kStatsThreads = 256;
+
+// ---------------------------------------------------------------------------
+// bf16 K/V statistics with the moment GEMM on MFMA.
+//
+// LDS holds K and V transposed (feature rows, token columns, padded pitch) so
+// that every MFMA operand lane reads 8 consecutive tokens of one feature:
+//   HT[e][c] = sum_n VT[e][n] * KcT[c][n]   (A = VT, B = KcT^T, k = tokens)
+template <int D, int BS>
+__global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, const uint16_t *__restrict__ K,
+                                                              const uint16_t *__restrict__ V,
+                                                              uint16_t *__restrict__ ksel,
+                                                              float *__restrict__ kbar,
+                                                              float *__restrict__ vsum,
+                                                              uint16_t *__restrict__ HT) {
+  constexpr int P = BS + 8;              // LDS pitch in bf16 elements (16-byte pad)
+  constexpr int PARTS = kStatsThreads / D;  // threads per feature in the column sums
+  constexpr int SEG = BS / PARTS;            // tokens per part
+  // kt and vt are carved from one array: the HT output staging (D x (D + 8))
+  // reuses both once the MFMA reads are done.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * D * P];
+  static_assert(2 * P >= D + 8, "output staging must fit in kt + vt");
+  uint16_t *kt = lds;
+  uint16_t *vt = lds + D * P;
+  __shared__ double red[2][PARTS][D][2];
+  __shared__ float kmean32[D];
+
+  const int tid = threadIdx.x;
+  const int bid = blockIdx.x;
+  const int j = bid % dm.n_blk;
+  const int bh = bid / dm.n_blk;  // b * Hkv + hk
+  const int n = min(BS, dm.L - j * BS);
+  const size_t base = ((size_t)bh * dm.L + (size_t)j * BS) * D;
+  const uint16_t *Kb = K + base;
+  const uint16_t *Vb = V + base;
+  const bool taylor = dm.taylor != 0;
+
+  // ---- load K (and V) transposed into LDS: token pairs x 8-feature chunks.
+  // Lanes run over token pairs fastest so the 4-byte transposed stores of one
+  // instruction spread over distinct banks.
+  constexpr int NPAIR = BS / 2, NCH = D / 8;
+  for (int u = tid; u < NPAIR * NCH; u += kStatsThreads) {
+    const int pr = u % NPAIR, ch = u / NPAIR;
+    const int t0 = 2 * pr;
+    u32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0}, va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+    if (t0 < n) {
+      a = *reinterpret_cast<const u32x4_t *>(Kb + (size_t)t0 * D + ch * 8);
+      if (taylor) va = *reinterpret_cast<const u32x4_t *>(Vb + (size_t)t0 * D + ch * 8);
+    }
+    if (t0 + 1 < n) {
+      b = *reinterpret_cast<const u32x4_t *>(Kb + (size_t)(t0 + 1) * D + ch * 8);
+      if (taylor) vb = *reinterpret_cast<const u32x4_t *>(Vb + (size_t)(t0 + 1) * D + ch * 8);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int f = ch * 8 + 2 * w;
+      // element f of tokens t0, t0+1 -> one 32-bit word; same for f+1
+      uint32_t k0 = (a[w] & 0xFFFFu) | (b[w] << 16);
+      uint32_t k1 = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+      *reinterpret_cast<uint32_t *>(&kt[f * P + t0]) = k0;
+      *reinterpret_cast<uint32_t *>(&kt[(f + 1) * P + t0]) = k1;
+      if (taylor) {
+        uint32_t v0 = (va[w] & 0xFFFFu) | (vb[w] << 16);
+        uint32_t v1 = (va[w] >> 16) | (vb[w] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t *>(&vt[f * P + t0]) = v0;
+        *reinterpret_cast<uint32_t *>(&vt[(f + 1) * P + t0]) = v1;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- column sums in float64 (exact cascaded sums), PARTS threads per feature
+  {
+    const int f = tid % D, part = tid / D;
+    DD sk = {0.0, 0.0}, sv = {0.0, 0.0};
+    const int t_lo = part * SEG;
+    for (int t = t_lo; t < t_lo + SEG; t += 8) {
+      u32x4_t kw = *reinterpret_cast<const u32x4_t *>(&kt[f * P + t]);
+      u32x4_t vw = taylor ? *reinterpret_cast<const u32x4_t *>(&vt[f * P + t]) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dd_add(sk, (double)bf16lo(kw[w]));
+        dd_add(sk, (double)bf16hi(kw[w]));
+        if (taylor) {
+          dd_add(sv, (double)bf16lo(vw[w]));
+          dd_add(sv, (double)bf16hi(vw[w]));
+        }
+      }
+    }
+    red[0][part][f][0] = sk.hi;
+    red[0][part][f][1] = sk.lo;
+    red[1][part][f][0] = sv.hi;
+    red[1][part][f][1] = sv.lo;
+  }
+  __syncthreads();
+  if (tid < D) {
+    const int f = tid;
+    DD sk = {red[0][0][f][0], red[0][0][f][1]}, sv = {red[1][0][f][0], red[1][0][f][1]};
+    for (int part = 1; part < PARTS; ++part) {
+      DD o = {red[0][part][f][0], red[0][part][f][1]};
+      dd_merge(sk, o);
+      DD ov = {red[1][part][f][0], red[1][part][f][1]};
+      dd_merge(sv, ov);
+    }
+    const double mean = dd_value(sk) / (double)n;
+    const size_t so = ((size_t)bh * dm.n_blk + j) * D + f;
+    ksel[so] = (uint16_t)f64_to_bf16_bits(mean);
+    const float m32 = (float)mean;
+    kmean32[f] = m32;
+    if (taylor) {
+      kbar[so] = m32;
+      vsum[so] = (float)dd_value(sv);
+    }
+  }
+  if (dm.taylor != 2) return;
+  __syncthreads();
+
+  // ---- centre the keys in place (bf16 of k - kbar, padded tokens stay zero)
+  for (int u = tid; u < D * (BS / 2); u += kStatsThreads) {
+    const int f = u / (BS / 2), t0 = 2 * (u % (BS / 2));
+    uint32_t w = *reinterpret_cast<const uint32_t *>(&kt[f * P + t0]);
+    const float m = kmean32[f];
+    float c0 = t0 < n ? bf16lo(w) - m : 0.f;
+    float c1 = t0 + 1 < n ? bf16hi(w) - m : 0.f;
+    *reinterpret_cast<uint32_t *>(&kt[f * P + t0]) = pack_bf16x2(c0, c1);
+  }
+  __syncthreads();
+
+  // ---- HT = VT * KcT^T on MFMA 32x32x16 (k = 16 tokens per step)
+  constexpr int NT = D / 32;                 // output tiles per dimension
+  constexpr int TILES = NT * NT;
+  constexpr int TPW = TILES / (kStatsThreads / 64);  // tiles per wave (4 or 1)
+  const int wave = tid >> 6, l = tid & 63;
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = f32x16_t{};
+  const int te = (TPW == NT) ? wave : wave / NT;     // e tile of this wave
+#pragma unroll
+  for (int ks = 0; ks < BS / 16; ++ks) {
+    const int tok = ks * 16 + (l >> 5) * 8;
+    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&vt[(te * 32 + (l & 31)) * P + tok]);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tc = (TPW == NT) ? i : wave % NT;
+      const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&kt[(tc * 32 + (l & 31)) * P + tok]);
+      acc[i] = mfma32(a, b, acc[i]);
+    }
+  }
+  __syncthreads();  // kt/vt are reused as the output staging buffer
+  // stage HT rows (e) with c contiguous: lane holds column c = tc*32 + l%32 and
+  // rows e = te*32 + 8*(r/4) + 4*(l/32) + r%4
+  constexpr int OP = D + 8;
+  uint16_t *ot = lds;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tc = (TPW == NT) ? i : wave % NT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = te * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      ot[e * OP + tc * 32 + (l & 31)] = (uint16_t)f32_to_bf16(acc[i][r]);
+    }
+  }
+  __syncthreads();
+  uint16_t *Hb = HT + ((size_t)bh * dm.n_blk + j) * D * D;
+  for (int u = tid; u < D * D / 8; u += kStatsThreads) {
+    const int e = u / (D / 8), c8 = (u % (D / 8)) * 8;
+    *reinterpret_cast<u32x4_t *>(Hb + (size_t)e * D + c8) = *reinterpret_cast<const u32x4_t *>(&ot[e * OP + c8]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 K/V statistics (VALU; the fp32 path has no MFMA moment GEMM).
+template <int D, int BS>
+__global__ __launch_bounds__(kStatsThreads) void kv_stats_f32(PisaDims dm, const float *__restrict__ K,
+                                                             const float *__restrict__ V,
+                                                             float *__restrict__ ksel,
+                                                             float *__restrict__ kbar,
+                                                             float *__restrict__ vsum,
+                                                             float *__restrict__ HT) {
+  constexpr int PARTS = kStatsThreads / D;
+  __shared__ double red[2][PARTS][D][2];
+  __shared__ float kmean[D];
+  const int tid = threadIdx.x;
+  const int bid = blockIdx.x;
+  const int j = bid % dm.n_blk;
+  const int bh = bid / dm.n_blk;
+  const int n = min(BS, dm.L - j * BS);
+  const size_t base = ((size_t)bh * dm.L + (size_t)j * BS) * D;
+  const float *Kb = K + base;
+  const float *Vb = V + base;
+  const bool taylor = dm.taylor != 0;
+  {
+    const int f = tid % D, part = tid / D;
+    DD sk = {0.0, 0.0}, sv = {0.0, 0.0};
+    for (int t = part; t < n; t += PARTS) {
+      dd_add(sk, (double)Kb[(size_t)t * D + f]);
+      if (taylor) dd_add(sv, (double)Vb[(size_t)t * D + f]);
+    }
+    red[0][part][f][0] = sk.hi;
+    red[0][part][f][1] = sk.lo;
+    red[1][part][f][0] = sv.hi;
+    red[1][part][f][1] = sv.lo;
+  }
+  __syncthreads();
+  if (tid < D) {
+    const int f = tid;
+    DD sk = {red[0][0][f][0], red[0][0][f][1]}, sv = {red[1][0][f][0], red[1][0][f][1]};
+    for (int part = 1; part < PARTS; ++part) {
+      DD o = {red[0][part][f][0], red[0][part][f][1]};
+      dd_merge(sk, o);
+      DD ov = {red[1][part][f][0], red[1][part][f][1]};
+      dd_merge(sv, ov);
+    }
+    const double mean = dd_value(sk) / (double)n;
+    const size_t so = ((size_t)bh * dm.n_blk + j) * D + f;
+    ksel[so] = (float)round_to_format(mean, 24);
+    kmean[f] = (float)mean;
+    if (taylor) {
+      kbar[so] = (float)mean;
+      vsum[so] = (float)dd_value(sv);
+    }
+  }
+  if (dm.taylor != 2) return;
+  __syncthreads();
+  // HT[e][c] = sum_n v[n][e] (k[n][c] - kbar_c): each thread owns outputs
+  // (e, c) with c = tid % D and e stepping by kStatsThreads / D.
+  float *Hb = HT + ((size_t)bh * dm.n_blk + j) * D * D;
+  const int c = tid % D;
+  const float mc = kmean[c];
+  for (int e = tid / D; e < D; e += PARTS) {
+    float s = 0.f;
+    for (int t = 0; t < n; ++t) s = fmaf(Vb[(size_t)t * D + e], Kb[(size_t)t * D + c] - mc, s);
+    Hb[(size_t)e * D + c] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// query pooling: one thread per (selection row, 16-byte chunk of the row)
+template <typename T, int D>
+__global__ __launch_bounds__(kStatsThreads) void q_pool(PisaDims dm, const T *__restrict__ Q, T *__restrict__ qsel) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per chunk
+  constexpr int CPR = D / EPC;         // chunks per row
+  const long long gid = (long long)blockIdx.x * kStatsThreads + threadIdx.x;
+  const long long total = (long long)dm.B * dm.Hq * dm.n_sel * CPR;
+  if (gid >= total) return;
+  const int ch = (int)(gid % CPR);
+  const long long sr = gid / CPR;          // (b*Hq + h) * n_sel + r
+  const int r = (int)(sr % dm.n_sel);
+  const long long bh = sr / dm.n_sel;
+  const int span = dm.group >= 1 ? dm.group : dm.bs;
+  const int t0 = r * span, t1 = min(dm.L, t0 + span);
+  const T *src = Q + ((size_t)bh * dm.L) * D + ch * EPC;
+  DD acc[EPC];
+#pragma unroll
+  for (int i = 0; i < EPC; ++i) acc[i] = DD{0.0, 0.0};
+  for (int t = t0; t < t1; ++t) {
+    u32x4_t w = *reinterpret_cast<const u32x4_t *>(src + (size_t)t * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        dd_add(acc[2 * i], (double)bf16lo(w[i]));
+        dd_add(acc[2 * i + 1], (double)bf16hi(w[i]));
+      } else {
+        dd_add(acc[i], (double)__uint_as_float(w[i]));
+      }
+    }
+  }
+  const double cnt = (double)(t1 - t0);
+  u32x4_t out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      uint32_t lo = f64_to_bf16_bits(dd_value(acc[2 * i]) / cnt);
+      uint32_t hi = f64_to_bf16_bits(dd_value(acc[2 * i + 1]) / cnt);
+      out[i] = lo | (hi << 16);
+    } else {
+      out[i] = __float_as_uint((float)round_to_format(dd_value(acc[i]) / cnt, 24));
+    }
+  }
+  *reinterpret_cast<u32x4_t *>(qsel + (size_t)sr * D + ch * EPC) = out;
+}
+
+template <typename T, int D>
+hipError_t launch_q_pool(const PisaDims &dm, const void *Q, void *qsel, hipStream_t st) {
+  constexpr int CPR = D / (16 / sizeof(T));
+  const long long total = (long long)dm.B * dm.Hq * dm.n_sel * CPR;
+  const unsigned grid = (unsigned)((total + kStatsThreads - 1) / kStatsThreads);
+  q_pool<T, D><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q), static_cast<T *>(qsel));
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_kv_bf16(const PisaDims &dm, const void *K, const void *V, void *ksel, float *kbar,
+                          float *vsum, void *HT, hipStream_t st) {
+  const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk;
+  kv_stats_bf16<D, BS><<<grid, kStatsThreads, 0, st>>>(
+      dm, static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V), static_cast<uint16_t *>(ksel),
+      kbar, vsum, static_cast<uint16_t *>(HT));
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_kv_f32(const PisaDims &dm, const void *K, const void *V, void *ksel, float *kbar,
+                         float *vsum, void *HT, hipStream_t st) {
+  const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk;
+  kv_stats_f32<D, BS><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const float *>(K),
+                                                      static_cast<const float *>(V), static_cast<float *>(ksel),
+                                                      kbar, vsum, static_cast<float *>(HT));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, const void *V, void *qsel,
+                              void *ksel, float *kbar, float *vsum, void *HT, hipStream_t st) {
+  hipError_t e;
+  const bool bf = dm.dtype == 0;
+  if (bf) {
+    if (dm.d == 64) e = dm.bs == 64 ? launch_kv_bf16<64, 64>(dm, K, V, ksel, kbar, vsum, HT, st)
+                                    : launch_kv_bf16<64, 128>(dm, K, V, ksel, kbar, vsum, HT, st);
+    else e = dm.bs == 64 ? launch_kv_bf16<128, 64>(dm, K, V, ksel, kbar, vsum, HT, st)
+                         : launch_kv_bf16<128, 128>(dm, K, V, ksel, kbar, vsum, HT, st);
+  } else {
+    if (dm.d == 64) e = dm.bs == 64 ? launch_kv_f32<64, 64>(dm, K, V, ksel, kbar, vsum, HT, st)
+                                    : launch_kv_f32<64, 128>(dm, K, V, ksel, kbar, vsum, HT, st);
+    else e = dm.bs == 64 ? launch_kv_f32<128, 64>(dm, K, V, ksel, kbar, vsum, HT, st)
+                         : launch_kv_f32<128, 128>(dm, K, V, ksel, kbar, vsum, HT, st);
+  }
+  if (e != hipSuccess) return e;
+  if (bf) return dm.d == 64 ? launch_q_pool<uint16_t, 64>(dm, Q, qsel, st) : launch_q_pool<uint16_t, 128>(dm, Q, qsel, st);
+  return dm.d == 64 ? launch_q_pool<float, 64>(dm, Q, qsel, st) : launch_q_pool<float, 128>(dm, Q, qsel, st);
+}

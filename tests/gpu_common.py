@@ -1,0 +1,83 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the CPU oracle on the same seeded inputs, and compare them."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import pisa_oracle as po
+from piecewise_attention_dit_amd import pisa
+
+# tolerances (float outputs), bit-exact for selections and pooled vectors
+TOL = {"bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse=1e-2, H=1e-2),
+       "f32": dict(max_abs=1e-4, mean_abs=1e-4, lse=1e-5, H=1e-5)}
+
+
+def problem(knobs: dict) -> po.Problem:
+    return po.Problem.from_knobs(**knobs)
+
+
+def run_gpu(knobs: dict, q, k, v, diag: bool = True) -> dict:
+    """The three library calls on cuda:0; returns CPU copies of everything."""
+    p = pisa.make_params(**knobs)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    st = pisa.block_stats(p, dq, dk, dv)
+    dg = torch.zeros(16, dtype=torch.int32, device="cuda") if diag else None
+    idx, cand = pisa.indexer_topk(p, dq, st, diag=dg)
+    out, lse = pisa.sparse_attn_fwd(p, dq, dk, dv, st, idx)
+    torch.cuda.synchronize()
+    res = dict(stats={k2: (t.cpu() if t is not None else None) for k2, t in st.items()},
+               idx=idx.cpu(), cand=cand.cpu() if cand is not None else None, O=out.cpu(), lse=lse.cpu(),
+               diag=dg.cpu() if dg is not None else None)
+    return res
+
+
+def to64(t):
+    return t.double().numpy()
+
+
+def compare_stats(g: dict, st: dict, P: po.Problem):
+    gs = g["stats"]
+    np.testing.assert_array_equal(to64(gs["qsel"]), st["qsel"], err_msg="qsel not bit-exact")
+    np.testing.assert_array_equal(to64(gs["ksel"]), st["ksel"], err_msg="ksel not bit-exact")
+    if P.taylor != "none":
+        np.testing.assert_array_equal(to64(gs["kbar"]), po.rne(st["kbar"], "f32"),
+                                      err_msg="kbar is not the fp32 rounding of the mean")
+        vs = st["vsum"]
+        err = np.abs(to64(gs["vsum"]) - vs).max() / max(1e-30, np.abs(vs).max())
+        assert err < 1e-5, f"vsum relative error {err}"
+    if P.taylor == "order1":
+        H = st["H"]                                    # [.., c, e]
+        HT = to64(gs["HT"])                            # [.., e, c]
+        num = np.linalg.norm((np.swapaxes(HT, -1, -2) - H).reshape(-1, P.d * P.d), axis=1)
+        den = np.linalg.norm(H.reshape(-1, P.d * P.d), axis=1) + 1e-30
+        rel = (num / den).max()
+        assert rel < TOL[P.dtype]["H"], f"H relative Frobenius error {rel}"
+
+
+def compare_idx(g: dict, idx: np.ndarray, cand, rows=None):
+    gi = g["idx"].numpy().astype(np.int64)
+    if rows is None:
+        bad = np.argwhere((gi != idx).any(axis=-1))
+        assert len(bad) == 0, f"{len(bad)} rows differ, first {bad[:5].tolist()}: " \
+                              f"gpu {gi[tuple(bad[0])]} oracle {idx[tuple(bad[0])]}"
+    else:
+        for (b, h, r) in rows:
+            assert np.array_equal(gi[b, h, r], idx[b, h, r]), (b, h, r, gi[b, h, r], idx[b, h, r])
+    if cand is not None:
+        gc = g["cand"].numpy().astype(np.int64)
+        assert np.array_equal(gc, cand), "PIVOT proxy lists differ"
+
+
+def compare_out(g: dict, O: np.ndarray, lse: np.ndarray, P: po.Problem, sel=None):
+    go, gl = to64(g["O"]), g["lse"].double().numpy()
+    if sel is not None:
+        go, gl = go[sel], gl[sel]
+    t = TOL[P.dtype]
+    d = np.abs(go - O)
+    assert np.isfinite(go).all(), "non-finite output"
+    assert d.max() <= t["max_abs"], f"max abs error {d.max()}"
+    assert d.mean() <= t["mean_abs"], f"mean abs error {d.mean()}"
+    dl = np.abs(gl - lse).max()
+    assert dl <= t["lse"], f"lse error {dl}"
+    return d.max(), d.mean()

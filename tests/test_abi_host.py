@@ -1,0 +1,117 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/pisa.h declares, sizes its buffers, and rejects bad arguments before
+any launch (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from piecewise_attention_dit_amd import pisa
+from piecewise_attention_dit_amd import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pisa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pisa.LIB_PATH), reason="libpisa.so not built")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pisa_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    L = pisa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    L = pisa.lib()
+    assert L.pisa_abi_version() == 1
+    assert L.pisa_status_string(pisa.PISA_E_UNSUPPORTED).decode() == "PISA_E_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("name", sorted(W.WORKLOADS) + sorted(W.PARITY_CASES))
+def test_workloads_validate(name):
+    wl = W.get(name)
+    p = pisa.make_params(**wl.knobs())
+    pisa.validate(p)
+
+
+def _p(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, L=1000, d=128, dtype="bf16", block=64, topk=4, window=0, group=0,
+                n_cand=0, causal=False, taylor="order1")
+    base.update(kw)
+    return pisa.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), pisa.PISA_E_ARG),
+    (dict(Hq=3), pisa.PISA_E_ARG),                       # Hq % Hkv
+    (dict(Hq=6, Hkv=2), pisa.PISA_E_UNSUPPORTED),        # ratio 3
+    (dict(d=96), pisa.PISA_E_UNSUPPORTED),
+    (dict(block=32), pisa.PISA_E_UNSUPPORTED),
+    (dict(dtype=7), pisa.PISA_E_ARG),
+    (dict(taylor=5), pisa.PISA_E_ARG),
+    (dict(topk=-1), pisa.PISA_E_ARG),
+    (dict(topk=65), pisa.PISA_E_UNSUPPORTED),
+    (dict(window=64, causal=False), pisa.PISA_E_UNSUPPORTED),
+    (dict(group=3, n_cand=8, causal=True), pisa.PISA_E_ARG),    # block % g
+    (dict(group=8, n_cand=2, causal=True), pisa.PISA_E_ARG),    # n_cand < topk
+    (dict(group=8, n_cand=300, causal=True), pisa.PISA_E_UNSUPPORTED),
+    (dict(topk=0, taylor="none", causal=False), pisa.PISA_E_ARG),
+    (dict(L=65536 + 64), pisa.PISA_E_UNSUPPORTED),        # more than 1024 blocks
+    (dict(scale=float("nan")), pisa.PISA_E_ARG),
+])
+def test_validation_errors(kw, status):
+    with pytest.raises(pisa.PisaError) as ei:
+        pisa.validate(_p(**kw))
+    assert ei.value.status == status
+
+
+def test_layouts():
+    p = _p(L=1000, group=0)
+    n_blk = 16
+    sizes = pisa.stats_layout(p)
+    assert sizes == [1 * 4 * n_blk * 128 * 2, 1 * 2 * n_blk * 128 * 2, 2 * n_blk * 128 * 4,
+                     2 * n_blk * 128 * 4, 2 * n_blk * 128 * 128 * 2]
+    assert pisa.index_layout(p) == [1 * 4 * n_blk * 4 * 4, 0]
+    q = _p(L=1000, group=8, n_cand=16, causal=True, dtype="f32")
+    sz = pisa.stats_layout(q)
+    assert sz[0] == 4 * 125 * 128 * 4 and sz[4] == 2 * n_blk * 128 * 128 * 4
+    assert pisa.index_layout(q) == [4 * 1000 * 4 * 4, 4 * 125 * 16 * 4]
+    for op in (0, 1, 2):
+        assert pisa.workspace_size(p, op) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _call_stats(p, Q=FAKE, K=FAKE, V=FAKE, st=None, ws=None, ws_bytes=0):
+    st = st or pisa.Stats(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return pisa.lib().pisa_block_stats(ctypes.byref(p), Q, K, V, ctypes.byref(st), ws, ws_bytes, None)
+
+
+def test_launch_calls_reject_before_launch():
+    L = pisa.lib()
+    p = _p()
+    assert _call_stats(p, Q=None) == pisa.PISA_E_ARG
+    assert b"Q is NULL" in L.pisa_last_error()
+    assert _call_stats(p, K=FAKE + 4) == pisa.PISA_E_ARG               # misaligned
+    assert b"aligned" in L.pisa_last_error()
+    assert _call_stats(p, st=pisa.Stats(FAKE, FAKE, None, FAKE, FAKE)) == pisa.PISA_E_ARG
+    assert _call_stats(p, ws=None, ws_bytes=128) == pisa.PISA_E_ARG
+    assert _call_stats(_p(d=80)) == pisa.PISA_E_UNSUPPORTED
+    assert L.pisa_block_stats(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, 0, None) == pisa.PISA_E_ARG
+    st = pisa.Stats(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.pisa_indexer_topk(ctypes.byref(p), FAKE, ctypes.byref(st), None, None, None, 0,
+                               None) == pisa.PISA_E_ARG           # idx NULL with topk > 0
+    assert L.pisa_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(st), FAKE, None,
+                                  None, None, 0, None) == pisa.PISA_E_ARG   # O NULL
+    assert L.pisa_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
+                                  0, None) == pisa.PISA_E_ARG     # stats NULL with Taylor
+    assert L.pisa_validate(None) == pisa.PISA_E_ARG
