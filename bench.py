@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the PISA block-sparse attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input resident in HBM:
+pisa_block_stats -> pisa_indexer_topk -> pisa_sparse_attn_fwd.
+Prints ONE JSON line.  Default workload: video-DiT self-attention, bf16,
+B=1, H=24, L=32760 (21 x 30 x 52 patches), d=128, 128-token blocks, 32 kept
+blocks per query block, first-order Taylor for the rest, non-causal.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
+    """Algorithmic FLOPs of the attention call and bytes of the stats call,
+    from the selections actually made (idx: [B, Hq, n_rows, k], -1 padded).
+      exact pairs  (t, s), s in a kept block (s <= t when causal): 4 d FLOPs
+      Taylor pairs (t, j), j a non-kept candidate block: 4 d (logit + zero
+      order) + 2 d^2 (first order) FLOPs
+      dense-equivalent: 4 d per (t, s) pair of full (causal) attention."""
+    B, Hq, Hkv, L, d, bs = (knobs[k] for k in ("B", "Hq", "Hkv", "L", "d", "block"))
+    causal, window, group, taylor = knobs["causal"], knobs["window"], knobs["group"], knobs["taylor"]
+    n_blk = -(-L // bs)
+    nj = np.minimum(bs, L - bs * np.arange(n_blk)).astype(np.int64)
+    exact = 0
+    taylor_pairs = 0
+    pivot = group >= 1
+    n_rows = idx.shape[2]
+    for r in range(n_rows):
+        tokens = np.array([r]) if pivot else np.arange(r * bs, min(L, (r + 1) * bs))
+        start = r if pivot else r * bs
+        own = start // bs
+        if causal:
+            lo = (max(0, start - window + 1) // bs) if window > 0 else own
+            nc = lo
+        else:
+            lo, nc = n_blk, n_blk
+        rows_idx = idx[:, :, r, :]                                      # [B, Hq, k]
+        valid = rows_idx >= 0
+        kept_keys = np.where(valid, nj[np.clip(rows_idx, 0, n_blk - 1)], 0).sum(axis=-1)  # [B, Hq]
+        n_kept = valid.sum(axis=-1)
+        if causal:
+            win_full = nj[lo:own].sum() if own > lo else 0
+            # own block: keys s <= t
+            own_pairs = ((tokens - own * bs) + 1).sum()
+            exact += int(kept_keys.sum()) * len(tokens) + (win_full * len(tokens) + own_pairs) * B * Hq
+        else:
+            exact += int(kept_keys.sum()) * len(tokens)
+        if taylor != "none":
+            taylor_pairs += int((nc - n_kept).sum()) * len(tokens)
+    flop_exact = 4 * d * exact
+    flop_t0 = 4 * d * taylor_pairs if taylor != "none" else 0
+    flop_t1 = 2 * d * d * taylor_pairs if taylor == "order1" else 0
+    dense_pairs = (L * (L + 1) // 2) if causal else L * L
+    dense = 4 * d * dense_pairs * B * Hq
+    es = 2 if knobs["dtype"] == "bf16" else 4
+    qkv = (B * Hq * L * d + 2 * B * Hkv * L * d) * es
+    n_sel = -(-L // group) if pivot else n_blk
+    stats_out = B * Hq * n_sel * d * es + B * Hkv * n_blk * d * es
+    if taylor != "none":
+        stats_out += 2 * B * Hkv * n_blk * d * 4
+    if taylor == "order1":
+        stats_out += B * Hkv * n_blk * d * d * es
+    return dict(flop_exact=flop_exact, flop_taylor0=flop_t0, flop_taylor1=flop_t1,
+                flop_attn=flop_exact + flop_t0 + flop_t1, flop_dense=dense,
+                stats_bytes=qkv + stats_out, exact_pairs=exact, taylor_pairs=taylor_pairs)
+
+
+def cpu_baseline(wl, q, k, v, heads: int, budget_s: float) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample: the whole path
+    (stats, selection, attention) for the first `heads` query heads (and
+    their KV heads) of batch 0; throughput in dense-equivalent TFLOP/s."""
+    from oracle import pisa_oracle as po
+
+    ratio = wl.Hq // wl.Hkv
+    hkv = max(1, -(-heads // ratio))
+    kn = dict(wl.knobs(), B=1, Hq=heads, Hkv=hkv)
+    P = po.Problem.from_knobs(**kn)
+    qa = q[:1, :heads].double().numpy()
+    ka = k[:1, :hkv].double().numpy()
+    va = v[:1, :hkv].double().numpy()
+    t0 = time.perf_counter()
+    st = po.block_stats(qa, ka, va, P)
+    idx, _ = po.select(qa, st, P)
+    rows_done = 0
+    for h in range(heads):
+        po.attend_tokens(qa, ka, va, st, idx, P, 0, h, np.arange(wl.L))
+        rows_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    dense_pairs = (wl.L * (wl.L + 1) // 2) if wl.causal else wl.L * wl.L
+    flops = 4 * wl.d * dense_pairs * rows_done
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas = cores
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas)),
+            "kind": "oracle",
+            "sample": f"float64 NumPy oracle, whole path (block stats + selection + attention) for "
+                      f"{rows_done} of {wl.B * wl.Hq} query heads of the same workload, "
+                      f"{dt:.1f} s; dense-equivalent FLOPs / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video_dit")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from piecewise_attention_dit_amd import pisa
+    from piecewise_attention_dit_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    knobs = wl.knobs()
+    print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = W.make_inputs(wl)
+    p = pisa.make_params(**knobs)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    st = pisa.alloc_stats(p)
+    idx, cand = pisa.alloc_index(p)
+    out = torch.empty_like(dq)
+    lse = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        pisa.block_stats(p, dq, dk, dv, st)
+        if ev:
+            ev[1].record(stream)
+        pisa.indexer_topk(p, dq, st, idx, cand)
+        if ev:
+            ev[2].record(stream)
+        pisa.sparse_attn_fwd(p, dq, dk, dv, st, idx, out, lse)
+        if ev:
+            ev[3].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    ms_stats, ms_idx, ms_attn = per.mean(axis=0)
+    ms_step = wall * 1e3 / args.steps
+
+    work = algorithmic_work(knobs, idx.cpu().numpy())
+    tflops_eff = work["flop_dense"] / (ms_step * 1e-3) / 1e12
+    attn_achieved = work["flop_attn"] / (ms_attn * 1e-3) / 1e12
+    stats_gbs = work["stats_bytes"] / (ms_stats * 1e-3) / 1e9
+    line = {
+        "metric": "sparse-attn fwd ms & effective TFLOP/s at L=32K; % of bf16 MFMA / HBM roofline",
+        "value": round(tflops_eff, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L, "d": wl.d,
+                   "block": wl.block, "topk": wl.topk, "window": wl.window, "group": wl.group,
+                   "n_cand": wl.n_cand, "causal": wl.causal, "taylor": wl.taylor,
+                   "value_is": "dense-equivalent FLOPs (4 d L^2 B H) / step time"},
+        "roofline": {"bound": "mfma", "kernel": "pisa_sparse_attn_fwd",
+                     "achieved": round(attn_achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernels": {
+            "block_stats": {"ms": round(ms_stats, 4), "GB/s": round(stats_gbs, 1),
+                            "hbm_frac": round(stats_gbs / PEAK_HBM_GBS, 4)},
+            "indexer_topk": {"ms": round(ms_idx, 4)},
+            "sparse_attn_fwd": {"ms": round(ms_attn, 4),
+                                "kept_mfma_frac": round(work["flop_exact"] / (ms_attn * 1e-3) / 1e12
+                                                        / PEAK_BF16_TFLOPS, 4),
+                                "total_mfma_frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
+                                "flop_exact": work["flop_exact"], "flop_taylor": work["flop_taylor0"]
+                                + work["flop_taylor1"]},
+        },
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_heads, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -867,5 +867,5 @@ hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const v
     return hipGetLastError();
   }
   if (dm.d == 64) return dm.bs == 64 ? launch_bf16<64, 64, 8, 1>(a, st) : launch_bf16<64, 128, 4, 2>(a, st);
-  return dm.bs == 64 ? launch_bf16<128, 64, 4, 2>(a, st) : launch_bf16<128, 128, 4, 2>(a, st);
+  return dm.bs == 64 ? launch_bf16<128, 64, 8, 1>(a, st) : launch_bf16<128, 128, 8, 1>(a, st);
 }
