@@ -636,8 +636,10 @@ hipError_t launch(const AttnArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st) {
-  // eight waves of 32 rows (two waves per SIMD): latency hiding across waves
-  // beats the halved LDS traffic of 64-row waves at one wave per SIMD
+  // block rows: one kept list per query block, walked part by part
+  if (a.dm.group == 0) return launch_attn_blocks(a, st);
+  // PIVOT rows (one list per token): the union walk with per-row masks,
+  // eight waves of 32 rows (two waves per SIMD)
   if (a.dm.d == 64) return a.dm.bs == 64 ? launch<64, 64, 8, 1>(a, st) : launch<64, 128, 8, 1>(a, st);
   return a.dm.bs == 64 ? launch<128, 64, 8, 1>(a, st) : launch<128, 128, 8, 1>(a, st);
 }

@@ -1,0 +1,582 @@
+// Stage C, bf16, block-row selection: exact online-softmax attention over
+// each query block's kept key blocks, fused with the per-block Taylor tail
+// for every other candidate block, on gfx950 MFMA.
+//
+// PISA page, section 2: o_t = N_t / D_t; exact terms e^{q k} v over the
+// selected blocks; for a non-selected block j, alpha = e^{q . kbar_j} times
+// (sum of its values + q H_j) in N_t and alpha * n_j in D_t.  Hardware
+// implementation section: one fused online-softmax kernel, selected blocks
+// staged on chip, pooled statistics scanned for the rest.  Sliding Window
+// Attention page (causal window, widened here to whole blocks).
+//
+// Work split (MI355X):
+//   * workgroup = 8 waves x 32 query rows = 256 rows, two waves per SIMD;
+//     the rows form P = 256 / block "parts", each one selection row (one
+//     query block of one head; GQA heads that share a KV head are packed);
+//   * the exact phase runs in steps.  In a step every part takes SK keys of
+//     its own kept list (its own LDS region), so no wave ever waits on a
+//     block it does not use; the causal window range, identical for heads
+//     and overlapping for neighbouring block rows, is walked first with one
+//     shared region;
+//   * a wave computes everything transposed, lane = query (lane % 32):
+//       S^T  = K Q^T           A = K tile (LDS),  B = Q (registers)
+//       O^T += V^T P^T         A = V tile through ds_read_b64_tr_b16
+//     and software-pipelines its steps: in step i it issues the MFMAs of
+//     S_{i+1} and of P_{i-1} V_{i-1} around the exponentials of step i, so
+//     the matrix cores and the VALU work at the same time;
+//   * K and V move global -> LDS by the DMA path (no registers) in two
+//     2-deep rings, one step ahead, one barrier per step;
+//   * the Taylor phase walks the union of the parts' Taylor blocks, 16 per
+//     logits batch (a^T = Kbar Q^T, zero order Sigma^T alpha^T with bf16
+//     hi/lo splits), and per block the first order u = H_j^T Q^T, added as
+//     O^T += (alpha scale) u in fp32; H tiles in a 3-deep ring, two ahead;
+//   * row maxima move only when a logit exceeds them by more than 2^8.
+#include "attn_tiles.h"
+
+using namespace pisa_attn;
+
+namespace {
+
+constexpr int NW = 8;              // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int ROWS = NW * 32;      // query rows per workgroup
+constexpr int kNB = 16;            // Taylor entries per logits batch
+constexpr int kRingH = 3;
+constexpr float kRescale = 8.f;    // lazy max threshold (log2 units)
+constexpr int kMaxK = 64;          // kept-list capacity per part
+
+template <int D, int BS>
+struct Cfg {
+  static constexpr int P = ROWS / BS;                         // parts per workgroup
+  static constexpr int WPP = NW / P;                          // waves per part
+  static constexpr int SK = (BS == 64 && D == 128) ? 32 : 64; // keys per part per step
+  static constexpr int SPB = BS / SK;                         // steps per block
+  static constexpr int NQT = SK / 32;                         // 32-key tiles per step
+  static constexpr int NE = D / 32;                           // 32-feature output tiles
+  static constexpr int SUB = SK * D * 2;                      // one part's K (or V) bytes per step
+  static constexpr int SLOT = P * SUB;
+  static constexpr int CPS = SUB / 1024;                      // DMA kilobytes per sub-tile
+  static constexpr int EX_K = 0, EX_V = 2 * SLOT, EX_END = 4 * SLOT;
+  static constexpr int HT = D * D * 2;
+  static constexpr int HCH = HT / 1024;
+  static constexpr int TY_H = 0;
+  static constexpr int TY_KBH = TY_H + kRingH * HT;
+  static constexpr int TY_KBL = TY_KBH + kNB * D * 2;
+  static constexpr int TY_STH = TY_KBL + kNB * D * 2;
+  static constexpr int TY_STL = TY_STH + D * kNB * 2;
+  static constexpr int TY_AL = TY_STL + D * kNB * 2;          // fp32 [wave][entry][32 rows]
+  static constexpr int TY_NJ = TY_AL + NW * kNB * 32 * 4;
+  static constexpr int TY_END = TY_NJ + kNB * 4;
+  static constexpr int MAIN = EX_END > TY_END ? EX_END : TY_END;
+  static constexpr int LST = MAIN;                            // uint16 [P][kMaxK]
+  static constexpr int KBM = LST + P * kMaxK * 2;             // u32 [P][32] kept bitmaps
+  static constexpr int TYL = KBM + P * 32 * 4;                // uint16 [1024] Taylor union
+  static constexpr int CNT = TYL + 1024 * 2;                  // int [8]
+  static constexpr int TOTAL = CNT + 32;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(CPS % NW == 0 && HCH % NW == 0, "DMA must split evenly over the waves");
+  static_assert(kNB * (D / 8) <= NT, "one table unit per thread");
+};
+
+struct Item {
+  int key0;    // first key of the step's sub-tile
+  int reg;     // LDS region (part) holding it
+  bool mem;    // this wave's rows use it
+  bool full;   // no causal or ragged-tail mask needed
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
+  using C = Cfg<D, BS>;
+  constexpr int P = C::P, WPP = C::WPP, SK = C::SK, SPB = C::SPB, NQT = C::NQT, NE = C::NE;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const PisaDims &dm = a.dm;
+  const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- workgroup -> (b, kv head, head group, tile of TB block rows)
+  const int G = dm.ratio < P ? dm.ratio : P;   // query heads per workgroup
+  const int TB = P / G;                        // block rows per workgroup
+  const int ngrp = dm.ratio / G;
+  const int ntile = (dm.n_blk + TB - 1) / TB;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = logical % ntile;
+  const int rest = logical / ntile;
+  const int grp = rest % ngrp;
+  const int bk = rest / ngrp;
+  const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
+  // ---- wave -> part (head, block row) and 32 of its rows
+  const int part = w / WPP, rg = w % WPP;
+  const int h = hk * dm.ratio + grp * G + part / TB;
+  const int iblk = tile * TB + part % TB;
+  const bool pvalid = iblk < dm.n_blk;
+  const int t = iblk * BS + rg * 32 + lq;
+  const bool valid = t < dm.L;
+  const bool causal = dm.causal != 0;
+  const int taylor = dm.taylor;
+  int own, lo;
+  const int nc = pisa_row_geometry(dm, iblk * BS, &own, &lo);
+
+  uint16_t *lst = reinterpret_cast<uint16_t *>(lds + C::LST);
+  uint32_t *kbm = reinterpret_cast<uint32_t *>(lds + C::KBM);
+  uint16_t *tyl = reinterpret_cast<uint16_t *>(lds + C::TYL);
+  int *cnt = reinterpret_cast<int *>(lds + C::CNT);
+
+  // ---- 1. kept lists and bitmaps per part; union of the Taylor sets
+  for (int i = tid; i < P * 32; i += NT) kbm[i] = 0;
+  __syncthreads();
+  if (rg == 0 && l == 0) {
+    int c = 0;
+    if (pvalid && a.idx && dm.topk > 0) {
+      const int32_t *row = a.idx + ((size_t)(b * dm.Hq + h) * dm.n_rows + iblk) * dm.topk;
+      for (int k = 0; k < dm.topk; ++k) {
+        const int j = row[k];
+        if (j < 0) break;
+        lst[part * kMaxK + c++] = (uint16_t)j;
+        kbm[part * 32 + (j >> 5)] |= 1u << (j & 31);
+      }
+    }
+    cnt[part] = c;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint32_t tb = 0;
+    const int nwords = (dm.n_blk + 31) >> 5;
+    if (taylor && l < nwords) {
+      for (int p = 0; p < P; ++p) {
+        const int ip = tile * TB + p % TB;
+        if (ip >= dm.n_blk) continue;
+        int o2, l2;
+        const int nc2 = pisa_row_geometry(dm, ip * BS, &o2, &l2) - l * 32;
+        const uint32_t rm = nc2 >= 32 ? 0xFFFFFFFFu : (nc2 > 0 ? (1u << nc2) - 1u : 0u);
+        tb |= rm & ~kbm[p * 32 + l];
+      }
+    }
+    const int ct = __popc(tb);
+    const int it = wave_incl_scan(ct);
+    int pt = it - ct;
+    for (uint32_t m = tb; m; m &= m - 1) tyl[pt++] = (uint16_t)(l * 32 + __ffs(m) - 1);
+    if (l == 63) cnt[7] = it;
+  }
+
+  // ---- 2. Q fragments (B operand: query lq, features 16 ks + 8 hl .. + 7)
+  const uint16_t *Qh = static_cast<const uint16_t *>(a.Q) + ((size_t)(b * dm.Hq + h) * dm.L) * D;
+  u32x4_t qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = valid ? *reinterpret_cast<const u32x4_t *>(Qh + (size_t)t * D + ks * 16 + hl * 8)
+                   : u32x4_t{0, 0, 0, 0};
+  __syncthreads();
+  const int cnt_me = __builtin_amdgcn_readfirstlane(cnt[part]);
+  const int n_ty = __builtin_amdgcn_readfirstlane(cnt[7]);
+  int n_t = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) n_t = max(n_t, __builtin_amdgcn_readfirstlane(cnt[p]));
+  n_t *= SPB;
+  // causal window range of the workgroup's block rows (contiguous)
+  int wlo = 0, n_w = 0;
+  if (causal) {
+    const int i0 = tile * TB, i1 = min(tile * TB + TB, dm.n_blk) - 1;
+    int o0, l0;
+    pisa_row_geometry(dm, i0 * BS, &o0, &l0);
+    wlo = l0;
+    n_w = (i1 - l0 + 1) * SPB;
+  }
+  const int n = n_w + n_t;
+
+  f32x16_t oacc[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) oacc[i] = f32x16_t{};
+  float m_run = kNegInf, d_run = 0.f;
+  const float sl2 = a.sl2;
+
+  const size_t kvoff = ((size_t)(b * dm.Hkv + hk) * dm.L) * D;
+  const uint16_t *Kh = static_cast<const uint16_t *>(a.K) + kvoff;
+  const uint16_t *Vh = static_cast<const uint16_t *>(a.V) + kvoff;
+  const int srow = (l & 15) >> 2;
+  const int ecol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+
+  // ---- 3. exact phase
+  if (n > 0) {
+    // This wave's share of a step's K (or V) slot: kilobytes c = w + NW u,
+    // part c / CPS, kilobyte c % CPS of that part's sub-tile.  The per-lane
+    // source offsets (elements from the sub-tile's first key) never change.
+    constexpr int NU = P * C::CPS / NW;   // kilobytes per wave, top-k steps
+    constexpr int NUW = C::CPS / NW;      // window steps (one shared sub-tile)
+    int offk[NU], offv[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int pos = ((w + NW * u) % C::CPS) * 64 + l;
+      const int row = pos / (D / 8), phys = pos % (D / 8);
+      offk[u] = row * D + ((phys ^ kswz<D>(row)) << 3);
+      offv[u] = row * D + ((phys ^ vswz<D>(row)) << 3);
+    }
+    int cnt_s[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) cnt_s[p] = __builtin_amdgcn_readfirstlane(cnt[p]);
+    // first key of part p's sub-tile in step s (window steps are shared;
+    // idle parts load block 0, finite data that their zero weights ignore)
+    auto key0_of = [&](int s, int p) -> int {
+      if (s < n_w) return (wlo + s / SPB) * BS + (s % SPB) * SK;
+      const int s2 = s - n_w, bi = s2 / SPB;
+      const int j = bi < cnt_s[p] ? __builtin_amdgcn_readfirstlane(lst[p * kMaxK + bi]) : 0;
+      return j * BS + (s2 % SPB) * SK;
+    };
+    // K (isv false) or V sub-tiles of step s into the ring slot at byte offset base
+    auto dma_step = [&](int s, bool isv, int base) {
+      const uint16_t *g = isv ? Vh : Kh;
+      const bool win = s < n_w;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (win && u >= NUW) break;
+        const int c = w + NW * u;
+        const int p = c / C::CPS;
+        const int k0 = key0_of(s, p);
+        uint8_t *dst = lds + base + p * C::SUB + (c % C::CPS) * 1024;
+        const int off = isv ? offv[u] : offk[u];
+        if (k0 + SK <= dm.L) {
+          dma16(g + (size_t)k0 * D + off, dst);
+        } else {   // ragged last block: rows past the end repeat the last key
+          const int row = off / D;
+          dma16(g + (size_t)min(k0 + row, dm.L - 1) * D + (off - row * D), dst);
+        }
+      }
+    };
+    auto info = [&](int s) -> Item {
+      Item it;
+      if (s < n_w) {
+        const int j = wlo + s / SPB;
+        it.key0 = j * BS + (s % SPB) * SK;
+        it.reg = 0;
+        it.mem = pvalid && j >= lo && j <= own;
+        it.full = it.key0 + SK <= dm.L && !(causal && j == own);
+      } else {
+        const int s2 = s - n_w, bi = s2 / SPB;
+        it.mem = bi < cnt_me;
+        const int j = it.mem ? __builtin_amdgcn_readfirstlane(lst[part * kMaxK + bi]) : 0;
+        it.key0 = j * BS + (s2 % SPB) * SK;
+        it.reg = part;
+        it.full = it.key0 + SK <= dm.L;
+      }
+      return it;
+    };
+    auto scores = [&](const uint8_t *kt, f32x16_t (&s)[NQT]) {
+#pragma unroll
+      for (int q = 0; q < NQT; ++q) {
+        s[q] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) s[q] = mfma32(frag_a<D>(kt, q * 32 + lq, 2 * ks + hl), qf[ks], s[q]);
+      }
+    };
+
+    // V slot 1 starts as zeros: step 0 multiplies it by an all-zero P
+    for (int i = tid; i < C::SLOT / 16; i += NT)
+      reinterpret_cast<u32x4_t *>(lds + C::EX_V + C::SLOT)[i] = u32x4_t{0, 0, 0, 0};
+    dma_step(0, false, C::EX_K);
+    if (n > 1) dma_step(1, false, C::EX_K + C::SLOT);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    f32x16_t sa[NQT], sb[NQT];
+    u32x4_t pprev[NQT][2];
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) pprev[q][0] = pprev[q][1] = u32x4_t{0, 0, 0, 0};
+    {
+      const Item c0 = info(0);
+      scores(lds + C::EX_K + c0.reg * C::SUB, sa);
+    }
+
+    auto step = [&](int i, f32x16_t (&sc)[NQT], f32x16_t (&sn)[NQT]) {
+      wait_vmcnt<0>();   // K_{i+1} and V_{i-1} have landed (this wave's part)
+      __syncthreads();   // ... for every wave; K slot i%2 and V slot i%2 are free
+      if (i + 2 < n) dma_step(i + 2, false, C::EX_K + (i & 1) * C::SLOT);
+      dma_step(i, true, C::EX_V + (i & 1) * C::SLOT);
+      const Item cur = info(i);
+      const Item nxt = info(i + 1 < n ? i + 1 : i);
+      const Item prv = info(i > 0 ? i - 1 : 0);
+      // causal diagonal / ragged tail: mask in place
+      if (cur.mem && !cur.full) {
+        const int lim = min(causal ? t : dm.L - 1, dm.L - 1) - cur.key0 - 4 * hl;
+#pragma unroll
+        for (int q = 0; q < NQT; ++q)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (q * 32 + 8 * (r >> 2) + (r & 3) > lim) sc[q][r] = kNegInf;
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int q = 0; q < NQT; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[q][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float ms = cur.mem ? mx * sl2 : kNegInf;
+      const bool grow = ms > m_run + kRescale;   // includes the first visible step
+      if (ballot64(grow)) {
+        const float corr = grow ? fast_exp2(m_run - ms) : 1.f;
+        d_run *= corr;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) oacc[et] *= corr;
+#pragma unroll
+        for (int q = 0; q < NQT; ++q)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              pprev[q][hf][k] = pack_bf16x2(bf16lo(pprev[q][hf][k]) * corr, bf16hi(pprev[q][hf][k]) * corr);
+        m_run = grow ? ms : m_run;
+      }
+      const float mneg = cur.mem ? -(m_run == kNegInf ? 0.f : m_run) : kNegInf;
+      // one block: S_{i+1} and P_{i-1} V_{i-1} on the matrix cores, exp of S_i on the VALU
+      const uint8_t *kt = lds + C::EX_K + ((i + 1) & 1) * C::SLOT + nxt.reg * C::SUB;
+      const uint8_t *vt = lds + C::EX_V + ((i + 1) & 1) * C::SLOT + prv.reg * C::SUB;
+      scores(kt, sn);
+#pragma unroll
+      for (int q = 0; q < NQT; ++q)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r1 = q * 32 + 16 * hf + 4 * hl + srow;
+#pragma unroll
+          for (int et = 0; et < NE; ++et)
+            oacc[et] = mfma32(frag_vt<D>(vt, r1, et * 32 + ecol), pprev[q][hf], oacc[et]);
+        }
+      float psum = 0.f;
+#pragma unroll
+      for (int q = 0; q < NQT; ++q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[q][r] = fast_exp2(fmaf(sc[q][r], sl2, mneg));
+        pprev[q][0] = pack8(sc[q], 0);
+        pprev[q][1] = pack8(sc[q], 8);
+        psum = sum_bf16x8(pprev[q][0], psum);
+        psum = sum_bf16x8(pprev[q][1], psum);
+      }
+      psum += __shfl_xor(psum, 32);
+      d_run += psum;
+    };
+
+    for (int i = 0; i < n; i += 2) {
+      step(i, sa, sb);
+      if (i + 1 >= n) break;
+      step(i + 1, sb, sa);
+    }
+    // drain: P_{n-1} V_{n-1}
+    wait_vmcnt<0>();
+    __syncthreads();
+    {
+      const Item last = info(n - 1);
+      const uint8_t *vt = lds + C::EX_V + ((n - 1) & 1) * C::SLOT + last.reg * C::SUB;
+#pragma unroll
+      for (int q = 0; q < NQT; ++q)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r1 = q * 32 + 16 * hf + 4 * hl + srow;
+#pragma unroll
+          for (int et = 0; et < NE; ++et)
+            oacc[et] = mfma32(frag_vt<D>(vt, r1, et * 32 + ecol), pprev[q][hf], oacc[et]);
+        }
+    }
+    __syncthreads();   // the Taylor phase reuses the rings' LDS
+  }
+
+  // ---- 4. Taylor phase: union of the parts' Taylor blocks
+  if (taylor && n_ty > 0) {
+    const size_t soff = (size_t)(b * dm.Hkv + hk) * dm.n_blk;
+    const float *kbar = a.kbar + soff * D;
+    const float *vsum = a.vsum + soff * D;
+    const uint16_t *HTh = static_cast<const uint16_t *>(a.HT) + soff * D * D;
+    uint8_t *kbh = lds + C::TY_KBH, *kbl = lds + C::TY_KBL;
+    uint8_t *sth = lds + C::TY_STH, *stl = lds + C::TY_STL;
+    float *alp = reinterpret_cast<float *>(lds + C::TY_AL) + w * kNB * 32;
+    float *nj = reinterpret_cast<float *>(lds + C::TY_NJ);
+    const uint32_t *kb_me = kbm + part * 32;
+    const bool order1 = taylor == 2;
+    constexpr int PER_H = C::HCH / NW;
+    int offh[PER_H];
+#pragma unroll
+    for (int u = 0; u < PER_H; ++u) {
+      const int pos = (w + NW * u) * 64 + l;
+      const int row = pos / (D / 8), phys = pos % (D / 8);
+      offh[u] = row * D + ((phys ^ kswz<D>(row)) << 3);
+    }
+    auto dma_h = [&](int eg) {
+      const uint16_t *src = HTh + (size_t)__builtin_amdgcn_readfirstlane(tyl[eg]) * D * D;
+      uint8_t *dst = lds + C::TY_H + (eg % kRingH) * C::HT;
+#pragma unroll
+      for (int u = 0; u < PER_H; ++u) dma16(src + offh[u], dst + (w + NW * u) * 1024);
+    };
+    if (order1) {
+      dma_h(0);
+      if (n_ty > 1) dma_h(1);
+    }
+    uint32_t tmask = 0;
+    for (int eg = 0; eg < n_ty; ++eg) {
+      const int e = eg % kNB;
+      if (e == 0) {
+        const int nb = min(kNB, n_ty - eg);
+        __syncthreads();   // the previous batch's tables are consumed
+        if (tid < kNB * (D / 8)) {
+          const int en = tid / (D / 8), ch = tid % (D / 8);
+          u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
+          float sv[8];
+          if (en < nb) {
+            const int j = tyl[eg + en];
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(kbar + (size_t)j * D + ch * 8);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(kbar + (size_t)j * D + ch * 8 + 4);
+            const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(vsum + (size_t)j * D + ch * 8);
+            const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(vsum + (size_t)j * D + ch * 8 + 4);
+            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t pk = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+              hi[i] = pk;
+              lo4[i] = pack_bf16x2(x[2 * i] - bf16lo(pk), x[2 * i + 1] - bf16hi(pk));
+            }
+            sv[0] = v0[0]; sv[1] = v0[1]; sv[2] = v0[2]; sv[3] = v0[3];
+            sv[4] = v1[0]; sv[5] = v1[1]; sv[6] = v1[2]; sv[7] = v1[3];
+            if (ch == 0) nj[en] = (float)min(dm.bs, dm.L - j * dm.bs);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sv[i] = 0.f;
+            if (ch == 0) nj[en] = 0.f;
+          }
+          const int sw = (ch ^ kswz<D>(en)) << 4;
+          *reinterpret_cast<u32x4_t *>(kbh + en * (2 * D) + sw) = hi;
+          *reinterpret_cast<u32x4_t *>(kbl + en * (2 * D) + sw) = lo4;
+          // Sigma^T [feature][16 entries]: entry en at K position perm16(en),
+          // the two 16-byte halves of a row swapped on odd groups of 8 rows
+          const int pos = perm16(en);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = ch * 8 + i;
+            const uint32_t shi = f32_to_bf16(sv[i]);
+            const uint32_t slo = f32_to_bf16(sv[i] - bf16_to_f32(shi));
+            const int off = f * (2 * kNB) + (((pos >> 3) ^ ((f >> 3) & 1)) << 4) + ((pos & 7) << 1);
+            *reinterpret_cast<uint16_t *>(sth + off) = (uint16_t)shi;
+            *reinterpret_cast<uint16_t *>(stl + off) = (uint16_t)slo;
+          }
+        }
+        __syncthreads();
+        tmask = 0;
+        if (pvalid) {
+          for (int en = 0; en < nb; ++en) {
+            const int j = tyl[eg + en];
+            if (j < nc && !((kb_me[j >> 5] >> (j & 31)) & 1u)) tmask |= 1u << en;
+          }
+        }
+        if (tmask) {
+          f32x16_t at = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks) {
+            at = mfma32(frag_a<D>(kbh, lq & 15, 2 * ks + hl), qf[ks], at);
+            at = mfma32(frag_a<D>(kbl, lq & 15, 2 * ks + hl), qf[ks], at);
+          }
+          // entries 0..15 sit in registers 0..7: entry 8 (r / 4) + 4 hl + r % 4
+          float mx = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const int en = 8 * (r >> 2) + 4 * hl + (r & 3);
+            const float x = ((tmask >> en) & 1u) ? at[r] * sl2 : kNegInf;
+            at[r] = x;
+            mx = fmaxf(mx, x);
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const bool grow = mx > m_run + kRescale;
+          if (ballot64(grow)) {
+            const float corr = grow ? fast_exp2(m_run - mx) : 1.f;
+            d_run *= corr;
+#pragma unroll
+            for (int et = 0; et < NE; ++et) oacc[et] *= corr;
+            m_run = grow ? mx : m_run;
+          }
+          const float mref = m_run == kNegInf ? 0.f : m_run;
+          float dpart = 0.f;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const int en = 8 * (r >> 2) + 4 * hl + (r & 3);
+            const float al = fast_exp2(at[r] - mref);
+            at[r] = al;
+            dpart += al * nj[en];
+            if (order1) alp[en * 32 + lq] = al * dm.scale;
+          }
+          dpart += __shfl_xor(dpart, 32);
+          d_run += dpart;
+          u32x4_t ph, pl;
+          pack8_split(at, 0, ph, pl);
+          // zero order: O^T += Sigma^T alpha^T  (hi*hi + lo*hi + hi*lo)
+#pragma unroll
+          for (int et = 0; et < NE; ++et) {
+            const int f = et * 32 + lq;
+            const int off = f * (2 * kNB) + ((hl ^ ((f >> 3) & 1)) << 4);
+            const u32x4_t sh = *reinterpret_cast<const u32x4_t *>(sth + off);
+            const u32x4_t sl = *reinterpret_cast<const u32x4_t *>(stl + off);
+            oacc[et] = mfma32(sh, ph, oacc[et]);
+            oacc[et] = mfma32(sl, ph, oacc[et]);
+            oacc[et] = mfma32(sh, pl, oacc[et]);
+          }
+        }
+      }
+      if (!order1) continue;
+      // first order for entry eg: H ring (3 deep, two ahead)
+      if (eg + 1 < n_ty) wait_vmcnt<PER_H>();
+      else wait_vmcnt<0>();
+      __syncthreads();   // H_eg landed for all waves; slot (eg + 2) % 3 is free
+      if (eg + 2 < n_ty) dma_h(eg + 2);
+      if ((tmask >> e) & 1u) {
+        const uint8_t *hp = lds + C::TY_H + (eg % kRingH) * C::HT;
+        const float al = alp[e * 32 + lq];
+        f32x16_t u[NE];
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+          u[et] = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks) u[et] = mfma32(frag_a<D>(hp, et * 32 + lq, 2 * ks + hl), qf[ks], u[et]);
+        }
+#pragma unroll
+        for (int et = 0; et < NE; ++et)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[et][r] = fmaf(al, u[et][r], oacc[et][r]);
+      }
+    }
+  }
+
+  // ---- 5. epilogue: O = N / D in bf16, lse
+  if (valid) {
+    const float inv = 1.f / d_run;
+    uint16_t *Oh = static_cast<uint16_t *>(a.O) + ((size_t)(b * dm.Hq + h) * dm.L + t) * D;
+#pragma unroll
+    for (int et = 0; et < NE; ++et)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = et * 32 + 8 * g + 4 * hl;
+        u32x2_t o;
+        o[0] = pack_bf16x2(oacc[et][4 * g] * inv, oacc[et][4 * g + 1] * inv);
+        o[1] = pack_bf16x2(oacc[et][4 * g + 2] * inv, oacc[et][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2_t *>(Oh + e) = o;
+      }
+    if (a.lse && hl == 0) a.lse[(size_t)(b * dm.Hq + h) * dm.L + t] = (m_run + log2f(d_run)) * kLn2;
+  }
+}
+
+template <int D, int BS>
+hipError_t launch(const AttnArgs &a, hipStream_t st) {
+  using C = Cfg<D, BS>;
+  const PisaDims &dm = a.dm;
+  const int G = dm.ratio < C::P ? dm.ratio : C::P;
+  const int TB = C::P / G;
+  const unsigned grid = (unsigned)dm.B * dm.Hkv * (dm.ratio / G) * ((dm.n_blk + TB - 1) / TB);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_blocks<D, BS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  attn_blocks<D, BS><<<grid, NT, C::TOTAL, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_blocks(const AttnArgs &a, hipStream_t st) {
+  if (a.dm.d == 64) return a.dm.bs == 64 ? launch<64, 64>(a, st) : launch<64, 128>(a, st);
+  return a.dm.bs == 64 ? launch<128, 64>(a, st) : launch<128, 128>(a, st);
+}

@@ -20,3 +20,4 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st);
+hipError_t launch_attn_blocks(const AttnArgs &a, hipStream_t st);
