@@ -68,15 +68,34 @@ struct Cfg {
   static constexpr int TY_NJ = TY_AL + NW * kNB * 32 * 4;
   static constexpr int TY_END = TY_NJ + kNB * 4;
   static constexpr int MAIN = EX_END > TY_END ? EX_END : TY_END;
-  static constexpr int LST = MAIN;                            // uint16 [P][kMaxK]
-  static constexpr int KBM = LST + P * kMaxK * 2;             // u32 [P][32] kept bitmaps
-  static constexpr int TYL = KBM + P * 32 * 4;                // uint16 [1024] Taylor union
-  static constexpr int CNT = TYL + 1024 * 2;                  // int [8]
-  static constexpr int TOTAL = CNT + 32;
+  static constexpr int LST = MAIN;                            // uint16 [P][kMaxK] kept lists
+  static constexpr int PRV = LST + P * kMaxK * 2;             // uint16 [P][kMaxK] private parts
+  static constexpr int SHL = PRV + P * kMaxK * 2;             // uint16 [kMaxK] shared by all parts
+  static constexpr int KBM = SHL + kMaxK * 2;                 // u32 [P][32] kept bitmaps
+  static constexpr int ITB = KBM + P * 32 * 4;                // u32 [32] intersection bitmap
+  static constexpr int TYL = ITB + 32 * 4;                    // uint16 [1024] Taylor union
+  static constexpr int CNT = TYL + 1024 * 2;                  // int [16]
+  static constexpr int TOTAL = CNT + 64;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
   static_assert(CPS % NW == 0 && HCH % NW == 0, "DMA must split evenly over the waves");
   static_assert(kNB * (D / 8) <= NT, "one table unit per thread");
 };
+
+// Instruction order of a pipelined step, for the scheduler: a few LDS reads
+// up front, then every MFMA followed by one LDS read, TPM exponentials and
+// VPM other VALU instructions of the current step's softmax, so the matrix
+// core and the VALU of a wave stay busy together.
+template <int NM, int ND, int TPM, int VPM>
+PISA_DEV void interleave_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, ND - NM, 0);   // DS reads
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+    __builtin_amdgcn_sched_group_barrier(0x400, TPM, 0);     // transcendental
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);     // other VALU
+  }
+}
 
 struct Item {
   int key0;    // first key of the step's sub-tile
@@ -118,11 +137,16 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
   const int nc = pisa_row_geometry(dm, iblk * BS, &own, &lo);
 
   uint16_t *lst = reinterpret_cast<uint16_t *>(lds + C::LST);
+  uint16_t *prv = reinterpret_cast<uint16_t *>(lds + C::PRV);
+  uint16_t *shl = reinterpret_cast<uint16_t *>(lds + C::SHL);
   uint32_t *kbm = reinterpret_cast<uint32_t *>(lds + C::KBM);
+  uint32_t *itb = reinterpret_cast<uint32_t *>(lds + C::ITB);
   uint16_t *tyl = reinterpret_cast<uint16_t *>(lds + C::TYL);
-  int *cnt = reinterpret_cast<int *>(lds + C::CNT);
+  int *cnt = reinterpret_cast<int *>(lds + C::CNT);   // [p] private counts, [4] shared, [7] Taylor, [8 + p] kept
 
-  // ---- 1. kept lists and bitmaps per part; union of the Taylor sets
+  // ---- 1. kept lists per part; blocks kept by every part (walked once, in
+  // one shared LDS region) and each part's private rest; union of the
+  // parts' Taylor sets
   for (int i = tid; i < P * 32; i += NT) kbm[i] = 0;
   __syncthreads();
   if (rg == 0 && l == 0) {
@@ -136,27 +160,45 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         kbm[part * 32 + (j >> 5)] |= 1u << (j & 31);
       }
     }
-    cnt[part] = c;
+    cnt[8 + part] = c;
   }
   __syncthreads();
   if (w == 0) {
-    uint32_t tb = 0;
     const int nwords = (dm.n_blk + 31) >> 5;
-    if (taylor && l < nwords) {
-      for (int p = 0; p < P; ++p) {
-        const int ip = tile * TB + p % TB;
-        if (ip >= dm.n_blk) continue;
+    uint32_t ib = l < nwords ? 0xFFFFFFFFu : 0u, tb = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int ip = tile * TB + p % TB;
+      if (ip >= dm.n_blk) continue;
+      const uint32_t kw = l < nwords ? kbm[p * 32 + l] : 0u;
+      ib &= kw;
+      if (taylor) {
         int o2, l2;
         const int nc2 = pisa_row_geometry(dm, ip * BS, &o2, &l2) - l * 32;
         const uint32_t rm = nc2 >= 32 ? 0xFFFFFFFFu : (nc2 > 0 ? (1u << nc2) - 1u : 0u);
-        tb |= rm & ~kbm[p * 32 + l];
+        tb |= rm & ~kw;
       }
     }
-    const int ct = __popc(tb);
-    const int it = wave_incl_scan(ct);
-    int pt = it - ct;
+    if (l < 32) itb[l] = ib;
+    const int ci = __popc(ib), ct = __popc(tb);
+    const int ii = wave_incl_scan(ci), it = wave_incl_scan(ct);
+    int pi = ii - ci, pt = it - ct;
+    for (uint32_t m = ib; m; m &= m - 1) shl[pi++] = (uint16_t)(l * 32 + __ffs(m) - 1);
     for (uint32_t m = tb; m; m &= m - 1) tyl[pt++] = (uint16_t)(l * 32 + __ffs(m) - 1);
-    if (l == 63) cnt[7] = it;
+    if (l == 63) {
+      cnt[4] = ii;
+      cnt[7] = it;
+    }
+  }
+  __syncthreads();
+  if (rg == 0 && l == 0) {
+    int c = 0;
+    const int nk = cnt[8 + part];
+    for (int k = 0; k < nk; ++k) {
+      const int j = lst[part * kMaxK + k];
+      if (!((itb[j >> 5] >> (j & 31)) & 1u)) prv[part * kMaxK + c++] = (uint16_t)j;
+    }
+    cnt[part] = c;
   }
 
   // ---- 2. Q fragments (B operand: query lq, features 16 ks + 8 hl .. + 7)
@@ -167,12 +209,13 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     qf[ks] = valid ? *reinterpret_cast<const u32x4_t *>(Qh + (size_t)t * D + ks * 16 + hl * 8)
                    : u32x4_t{0, 0, 0, 0};
   __syncthreads();
-  const int cnt_me = __builtin_amdgcn_readfirstlane(cnt[part]);
+  const int cnt_me = __builtin_amdgcn_readfirstlane(cnt[part]);   // private blocks of this part
   const int n_ty = __builtin_amdgcn_readfirstlane(cnt[7]);
+  const int n_s = __builtin_amdgcn_readfirstlane(cnt[4]) * SPB;      // shared steps
   int n_t = 0;
 #pragma unroll
   for (int p = 0; p < P; ++p) n_t = max(n_t, __builtin_amdgcn_readfirstlane(cnt[p]));
-  n_t *= SPB;
+  n_t *= SPB;                                                         // private steps
   // causal window range of the workgroup's block rows (contiguous)
   int wlo = 0, n_w = 0;
   if (causal) {
@@ -182,7 +225,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     wlo = l0;
     n_w = (i1 - l0 + 1) * SPB;
   }
-  const int n = n_w + n_t;
+  const int n = n_w + n_s + n_t;
+  const int n_one = n_w + n_s;   // steps with one region shared by all parts
 
   f32x16_t oacc[NE];
 #pragma unroll
@@ -198,66 +242,74 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
 
   // ---- 3. exact phase
   if (n > 0) {
-    // This wave's share of a step's K (or V) slot: kilobytes c = w + NW u,
-    // part c / CPS, kilobyte c % CPS of that part's sub-tile.  The per-lane
-    // source offsets (elements from the sub-tile's first key) never change.
-    constexpr int NU = P * C::CPS / NW;   // kilobytes per wave, top-k steps
-    constexpr int NUW = C::CPS / NW;      // window steps (one shared sub-tile)
-    int offk[NU], offv[NU];
+    // This wave's share of a step's K (or V) slot: kilobyte w + NW uu of each
+    // part's sub-tile, uu < UPP.  The per-lane source offsets (bytes from the
+    // sub-tile's first key) never change.
+    constexpr int UPP = C::CPS / NW;      // kilobytes of one sub-tile per wave
+    constexpr int NU = P * UPP;
+    int offk[UPP], offv[UPP];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int pos = ((w + NW * u) % C::CPS) * 64 + l;
+    for (int u = 0; u < UPP; ++u) {
+      const int pos = (w + NW * u) * 64 + l;
       const int row = pos / (D / 8), phys = pos % (D / 8);
-      offk[u] = row * D + ((phys ^ kswz<D>(row)) << 3);
-      offv[u] = row * D + ((phys ^ vswz<D>(row)) << 3);
+      offk[u] = (row * D + ((phys ^ kswz<D>(row)) << 3)) * 2;
+      offv[u] = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
     }
-    int cnt_s[P];
+    // the block lists live in VGPRs, entry e in lane e; a step reads its
+    // entry with v_readlane
+    int cnt_s[P], vprv[P];
 #pragma unroll
-    for (int p = 0; p < P; ++p) cnt_s[p] = __builtin_amdgcn_readfirstlane(cnt[p]);
-    // first key of part p's sub-tile in step s (window steps are shared;
-    // idle parts load block 0, finite data that their zero weights ignore)
-    auto key0_of = [&](int s, int p) -> int {
-      if (s < n_w) return (wlo + s / SPB) * BS + (s % SPB) * SK;
-      const int s2 = s - n_w, bi = s2 / SPB;
-      const int j = bi < cnt_s[p] ? __builtin_amdgcn_readfirstlane(lst[p * kMaxK + bi]) : 0;
-      return j * BS + (s2 % SPB) * SK;
+    for (int p = 0; p < P; ++p) {
+      cnt_s[p] = __builtin_amdgcn_readfirstlane(cnt[p]);
+      vprv[p] = l < cnt_s[p] ? (int)prv[p * kMaxK + l] : 0;
+    }
+    const int vshl = l < n_s / SPB ? (int)shl[l] : 0;
+    int vme = vprv[0];   // this wave's own private list
+#pragma unroll
+    for (int p = 1; p < P; ++p)
+      if (part == p) vme = vprv[p];
+    // first key of the sub-tile of a step with one region: window steps,
+    // then the shared blocks
+    auto key0_one = [&](int s) -> int {
+      const int s1 = s - n_w;
+      const int jw = wlo + s / SPB, js = __builtin_amdgcn_readlane(vshl, (s1 / SPB) & 63);
+      return (s < n_w ? jw * BS + (s % SPB) * SK : js * BS + (s1 % SPB) * SK);
+    };
+    // ... of part p's sub-tile in a private step (idle parts load block 0,
+    // finite data that their zero weights ignore)
+    auto key0_prv = [&](int s, int vlist, int count) -> int {
+      const int s2 = s - n_one, bi = s2 / SPB;
+      const int j = __builtin_amdgcn_readlane(vlist, bi & 63);
+      return (bi < count ? j : 0) * BS + (s2 % SPB) * SK;
     };
     // K (isv false) or V sub-tiles of step s into the ring slot at byte offset base
     auto dma_step = [&](int s, bool isv, int base) {
       const uint16_t *g = isv ? Vh : Kh;
-      const bool win = s < n_w;
+      if (s < n_one) {
+        const int k0 = key0_one(s);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (win && u >= NUW) break;
-        const int c = w + NW * u;
-        const int p = c / C::CPS;
-        const int k0 = key0_of(s, p);
-        uint8_t *dst = lds + base + p * C::SUB + (c % C::CPS) * 1024;
-        const int off = isv ? offv[u] : offk[u];
-        if (k0 + SK <= dm.L) {
-          dma16(g + (size_t)k0 * D + off, dst);
-        } else {   // ragged last block: rows past the end repeat the last key
-          const int row = off / D;
-          dma16(g + (size_t)min(k0 + row, dm.L - 1) * D + (off - row * D), dst);
+        for (int u = 0; u < UPP; ++u)
+          dma16_buf(g + (size_t)k0 * D, max(dm.L - k0, 0) * D * 2, isv ? offv[u] : offk[u],
+                    lds + base + (w + NW * u) * 1024);
+      } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int k0 = key0_prv(s, vprv[p], cnt_s[p]);
+#pragma unroll
+          for (int u = 0; u < UPP; ++u)
+            dma16_buf(g + (size_t)k0 * D, max(dm.L - k0, 0) * D * 2, isv ? offv[u] : offk[u],
+                      lds + base + p * C::SUB + (w + NW * u) * 1024);
         }
       }
     };
     auto info = [&](int s) -> Item {
       Item it;
-      if (s < n_w) {
-        const int j = wlo + s / SPB;
-        it.key0 = j * BS + (s % SPB) * SK;
-        it.reg = 0;
-        it.mem = pvalid && j >= lo && j <= own;
-        it.full = it.key0 + SK <= dm.L && !(causal && j == own);
-      } else {
-        const int s2 = s - n_w, bi = s2 / SPB;
-        it.mem = bi < cnt_me;
-        const int j = it.mem ? __builtin_amdgcn_readfirstlane(lst[part * kMaxK + bi]) : 0;
-        it.key0 = j * BS + (s2 % SPB) * SK;
-        it.reg = part;
-        it.full = it.key0 + SK <= dm.L;
-      }
+      const bool win = s < n_w, one = s < n_one;
+      const int jw = wlo + s / SPB;
+      it.key0 = one ? key0_one(s) : key0_prv(s, vme, cnt_me);
+      it.reg = one ? 0 : part;
+      it.mem = win ? (pvalid && jw >= lo && jw <= own) : (one ? pvalid : (s - n_one) / SPB < cnt_me);
+      it.full = it.key0 + SK <= dm.L && !(win && causal && jw == own);
       return it;
     };
     auto scores = [&](const uint8_t *kt, f32x16_t (&s)[NQT]) {
@@ -286,8 +338,24 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       scores(lds + C::EX_K + c0.reg * C::SUB, sa);
     }
 
+    // softmax weights of the current step against the running max reference
+    auto weights = [&](const f32x16_t (&sc)[NQT], float mneg, u32x4_t (&pc)[NQT][2]) -> float {
+      float psum = 0.f;
+#pragma unroll
+      for (int q = 0; q < NQT; ++q) {
+        f32x16_t e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(sc[q][r], sl2, mneg));
+        pc[q][0] = pack8(e, 0);
+        pc[q][1] = pack8(e, 8);
+        psum = sum_bf16x8(pc[q][0], psum);
+        psum = sum_bf16x8(pc[q][1], psum);
+      }
+      return psum;
+    };
+
     auto step = [&](int i, f32x16_t (&sc)[NQT], f32x16_t (&sn)[NQT]) {
-      wait_vmcnt<0>();   // K_{i+1} and V_{i-1} have landed (this wave's part)
+      wait_vmcnt<0>();   // K_{i+1} and V_{i-1} have landed (this wave's share)
       __syncthreads();   // ... for every wave; K slot i%2 and V slot i%2 are free
       if (i + 2 < n) dma_step(i + 2, false, C::EX_K + (i & 1) * C::SLOT);
       dma_step(i, true, C::EX_V + (i & 1) * C::SLOT);
@@ -303,54 +371,77 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           for (int r = 0; r < 16; ++r)
             if (q * 32 + 8 * (r >> 2) + (r & 3) > lim) sc[q][r] = kNegInf;
       }
-      float mx = kNegInf;
+      const float mold = m_run;
+      const float mneg = cur.mem ? -(mold == kNegInf ? 0.f : mold) : kNegInf;
+      // One block, scheduled by hand: MFMA k of S_{i+1} = K_{i+1} Q^T and of
+      // P_{i-1} V_{i-1}, the LDS reads of the fragment three MFMAs ahead, and
+      // E softmax elements of step i (max, exponential, bf16 pair, row sum),
+      // so the matrix core and the VALU of the wave work side by side.
+      const uint8_t *kt = lds + C::EX_K + ((i + 1) & 1) * C::SLOT + nxt.reg * C::SUB;
+      const uint8_t *vt = lds + C::EX_V + ((i + 1) & 1) * C::SLOT + prv.reg * C::SUB;
+      constexpr int KS = D / 16, NS = NQT * KS, NM = NS + NQT * 2 * NE, E = NQT * 16 / NM;
+      static_assert(E * NM == NQT * 16, "softmax elements must split evenly over the MFMAs");
+      auto frag = [&](int k) -> u32x4_t {
+        if (k < NS) return frag_a<D>(kt, (k / KS) * 32 + lq, 2 * (k % KS) + hl);
+        const int k2 = k - NS, q = k2 / (2 * NE), hf = (k2 / NE) % 2, et = k2 % NE;
+        return frag_vt<D>(vt, q * 32 + 16 * hf + 4 * hl + srow, et * 32 + ecol);
+      };
+      u32x4_t fr[3];
 #pragma unroll
-      for (int q = 0; q < NQT; ++q)
+      for (int k = 0; k < 3; ++k) fr[k] = frag(k);
+      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float mx = kNegInf, psum = 0.f, ehold = 0.f;
+      u32x4_t pc[NQT][2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[q][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int k = 0; k < NM; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (k < NS) {
+          const int q = k / KS, ks = k % KS;
+          sn[q] = mfma32(fr[k % 3], qf[ks], ks == 0 ? f32x16_t{} : sn[q]);
+        } else {
+          const int k2 = k - NS, q = k2 / (2 * NE), hf = (k2 / NE) % 2, et = k2 % NE;
+          oacc[et] = mfma32(fr[k % 3], pprev[q][hf], oacc[et]);
+        }
+        if (k + 3 < NM) fr[k % 3] = frag(k + 3);
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+          const int el = k * E + u, q = el / 16, r = el % 16;
+          const float x = sc[q][r];
+          const float e = fast_exp2(fmaf(x, sl2, mneg));
+          if (el & 1) {
+            mx = fmaxf(fmaxf(mx, sc[q][r - 1]), x);
+            const f32x2_t v2 = {ehold, e};
+            const bf16x2_t b2 = __builtin_convertvector(v2, bf16x2_t);
+            pc[q][r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, b2);
+            psum = __builtin_amdgcn_fdot2_f32_bf16(b2, one2, psum, false);
+          } else {
+            ehold = e;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // keep this computation here (it must not be merged into the rare
+      // recomputation below)
+      asm volatile("" : "+v"(psum), "+v"(mx));
+      // the max moved by more than 2^8 (or the row's first visible step):
+      // rescale and recompute this step's weights
+      mx = pair_max(mx);
       const float ms = cur.mem ? mx * sl2 : kNegInf;
-      const bool grow = ms > m_run + kRescale;   // includes the first visible step
+      const bool grow = ms > mold + kRescale;
       if (ballot64(grow)) {
-        const float corr = grow ? fast_exp2(m_run - ms) : 1.f;
+        const float corr = grow ? fast_exp2(mold - ms) : 1.f;
+        m_run = grow ? ms : mold;
         d_run *= corr;
 #pragma unroll
         for (int et = 0; et < NE; ++et) oacc[et] *= corr;
-#pragma unroll
-        for (int q = 0; q < NQT; ++q)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              pprev[q][hf][k] = pack_bf16x2(bf16lo(pprev[q][hf][k]) * corr, bf16hi(pprev[q][hf][k]) * corr);
-        m_run = grow ? ms : m_run;
+        psum = weights(sc, cur.mem ? -(m_run == kNegInf ? 0.f : m_run) : kNegInf, pc);
       }
-      const float mneg = cur.mem ? -(m_run == kNegInf ? 0.f : m_run) : kNegInf;
-      // one block: S_{i+1} and P_{i-1} V_{i-1} on the matrix cores, exp of S_i on the VALU
-      const uint8_t *kt = lds + C::EX_K + ((i + 1) & 1) * C::SLOT + nxt.reg * C::SUB;
-      const uint8_t *vt = lds + C::EX_V + ((i + 1) & 1) * C::SLOT + prv.reg * C::SUB;
-      scores(kt, sn);
-#pragma unroll
-      for (int q = 0; q < NQT; ++q)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int r1 = q * 32 + 16 * hf + 4 * hl + srow;
-#pragma unroll
-          for (int et = 0; et < NE; ++et)
-            oacc[et] = mfma32(frag_vt<D>(vt, r1, et * 32 + ecol), pprev[q][hf], oacc[et]);
-        }
-      float psum = 0.f;
+      d_run += pair_sum(psum);
 #pragma unroll
       for (int q = 0; q < NQT; ++q) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[q][r] = fast_exp2(fmaf(sc[q][r], sl2, mneg));
-        pprev[q][0] = pack8(sc[q], 0);
-        pprev[q][1] = pack8(sc[q], 8);
-        psum = sum_bf16x8(pprev[q][0], psum);
-        psum = sum_bf16x8(pprev[q][1], psum);
+        pprev[q][0] = pc[q][0];
+        pprev[q][1] = pc[q][1];
       }
-      psum += __shfl_xor(psum, 32);
-      d_run += psum;
     };
 
     for (int i = 0; i < n; i += 2) {
@@ -395,13 +486,13 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     for (int u = 0; u < PER_H; ++u) {
       const int pos = (w + NW * u) * 64 + l;
       const int row = pos / (D / 8), phys = pos % (D / 8);
-      offh[u] = row * D + ((phys ^ kswz<D>(row)) << 3);
+      offh[u] = (row * D + ((phys ^ kswz<D>(row)) << 3)) * 2;
     }
     auto dma_h = [&](int eg) {
       const uint16_t *src = HTh + (size_t)__builtin_amdgcn_readfirstlane(tyl[eg]) * D * D;
       uint8_t *dst = lds + C::TY_H + (eg % kRingH) * C::HT;
 #pragma unroll
-      for (int u = 0; u < PER_H; ++u) dma16(src + offh[u], dst + (w + NW * u) * 1024);
+      for (int u = 0; u < PER_H; ++u) dma16_buf(src, D * D * 2, offh[u], dst + (w + NW * u) * 1024);
     };
     if (order1) {
       dma_h(0);
@@ -478,7 +569,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
             at[r] = x;
             mx = fmaxf(mx, x);
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          mx = pair_max(mx);
           const bool grow = mx > m_run + kRescale;
           if (ballot64(grow)) {
             const float corr = grow ? fast_exp2(m_run - mx) : 1.f;
@@ -497,7 +588,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
             dpart += al * nj[en];
             if (order1) alp[en * 32 + lq] = al * dm.scale;
           }
-          dpart += __shfl_xor(dpart, 32);
+          dpart = pair_sum(dpart);
           d_run += dpart;
           u32x4_t ph, pl;
           pack8_split(at, 0, ph, pl);

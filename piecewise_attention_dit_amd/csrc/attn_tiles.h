@@ -34,6 +34,16 @@ PISA_DEV void dma16(const void *src, uint8_t *lds_chunk) {
   __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)lds_chunk, 16, 0, 0);
 }
 
+// Sixteen bytes per lane global -> LDS through a raw buffer descriptor that
+// starts at `base` and holds `bytes` bytes: lanes whose byte offset voff is
+// at or past the end read zeros (the descriptor's range check), so a tile
+// that runs past the last key needs no clamping.  LDS destination as dma16.
+PISA_DEV void dma16_buf(const void *base, int bytes, int voff, uint8_t *lds_chunk) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes,
+                                                                     0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds_chunk, 16, voff, 0, 0, 0);
+}
+
 template <int D>
 PISA_DEV int kswz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
@@ -113,6 +123,18 @@ PISA_DEV float sum_bf16x8(const u32x4_t &p, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
   }
   return acc;
+}
+
+// x combined with the value of lane l ^ 32 (v_permlane32_swap_b32 swaps
+// the upper half of one register with the lower half of another; with both
+// operands x, the two results hold x and its partner on every lane)
+PISA_DEV float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+PISA_DEV float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace pisa_attn
