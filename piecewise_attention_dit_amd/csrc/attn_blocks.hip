@@ -77,7 +77,7 @@ struct Cfg {
   static constexpr int CNT = TYL + 1024 * 2;                  // int [16]
   static constexpr int TOTAL = CNT + 64;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  static_assert(CPS % NW == 0 && HCH % NW == 0, "DMA must split evenly over the waves");
+  static_assert(CPS % (NW / 2) == 0 && HCH % NW == 0, "DMA must split evenly over the waves");
   static_assert(kNB * (D / 8) <= NT, "one table unit per thread");
 };
 
@@ -242,15 +242,18 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
 
   // ---- 3. exact phase
   if (n > 0) {
-    // This wave's share of a step's K (or V) slot: kilobyte w + NW uu of each
-    // part's sub-tile, uu < UPP.  The per-lane source offsets (bytes from the
-    // sub-tile's first key) never change.
-    constexpr int UPP = C::CPS / NW;      // kilobytes of one sub-tile per wave
-    constexpr int NU = P * UPP;
+    // The DMA of a step is issued by waves 0..NW/2-1 only (kilobyte
+    // w + NDW uu of each part's sub-tile, uu < UPP): while they drain it
+    // through the CU's load path, the other wave on each SIMD already runs
+    // its MFMA block, and the two swap roles within the step.  The per-lane
+    // source offsets (bytes from the sub-tile's first key) never change.
+    constexpr int NDW = NW / 2;           // DMA-issuing waves
+    constexpr int UPP = C::CPS / NDW;     // kilobytes of one sub-tile per issuing wave
+    const bool dma_wave = w < NDW;
     int offk[UPP], offv[UPP];
 #pragma unroll
     for (int u = 0; u < UPP; ++u) {
-      const int pos = (w + NW * u) * 64 + l;
+      const int pos = ((w % NDW) + NDW * u) * 64 + l;
       const int row = pos / (D / 8), phys = pos % (D / 8);
       offk[u] = (row * D + ((phys ^ kswz<D>(row)) << 3)) * 2;
       offv[u] = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
@@ -284,13 +287,14 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     };
     // K (isv false) or V sub-tiles of step s into the ring slot at byte offset base
     auto dma_step = [&](int s, bool isv, int base) {
+      if (!dma_wave) return;
       const uint16_t *g = isv ? Vh : Kh;
       if (s < n_one) {
         const int k0 = key0_one(s);
 #pragma unroll
         for (int u = 0; u < UPP; ++u)
           dma16_buf(g + (size_t)k0 * D, max(dm.L - k0, 0) * D * 2, isv ? offv[u] : offk[u],
-                    lds + base + (w + NW * u) * 1024);
+                    lds + base + (w + NDW * u) * 1024);
       } else {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
 #pragma unroll
           for (int u = 0; u < UPP; ++u)
             dma16_buf(g + (size_t)k0 * D, max(dm.L - k0, 0) * D * 2, isv ? offv[u] : offk[u],
-                      lds + base + p * C::SUB + (w + NW * u) * 1024);
+                      lds + base + p * C::SUB + (w + NDW * u) * 1024);
         }
       }
     };
