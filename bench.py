@@ -10,6 +10,7 @@ blocks per query block, first-order Taylor for the rest, non-causal.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,6 +23,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# source of the attention kernel that runs for block rows (True) / PIVOT rows
+ATTN_SRC = {True: os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn_blocks.hip"),
+            False: os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn.hip")}
 
 
 def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
@@ -79,42 +83,60 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
                 stats_bytes=qkv + stats_out, exact_pairs=exact, taylor_pairs=taylor_pairs)
 
 
-def cpu_baseline(wl, q, k, v, heads: int, budget_s: float) -> dict:
-    """The float64 oracle, as it stands, on a bounded sample: the whole path
-    (stats, selection, attention) for the first `heads` query heads (and
-    their KV heads) of batch 0; throughput in dense-equivalent TFLOP/s."""
+def cpu_baseline(wl, q, k, v, budget_s: float) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: block statistics and selection for query head 0 of batch 0
+    (and its KV head), then the attention of that head's query blocks in
+    order until the time budget is spent.  The whole-head time is that
+    measured time with the attention part scaled to all L rows; the value is
+    the head's dense-equivalent FLOPs over it (the metric's unit)."""
     from oracle import pisa_oracle as po
 
-    ratio = wl.Hq // wl.Hkv
-    hkv = max(1, -(-heads // ratio))
-    kn = dict(wl.knobs(), B=1, Hq=heads, Hkv=hkv)
+    kn = dict(wl.knobs(), B=1, Hq=1, Hkv=1)
     P = po.Problem.from_knobs(**kn)
-    qa = q[:1, :heads].double().numpy()
-    ka = k[:1, :hkv].double().numpy()
-    va = v[:1, :hkv].double().numpy()
+    qa, ka, va = (x[:1, :1].double().numpy() for x in (q, k, v))
     t0 = time.perf_counter()
     st = po.block_stats(qa, ka, va, P)
     idx, _ = po.select(qa, st, P)
-    rows_done = 0
-    for h in range(heads):
-        po.attend_tokens(qa, ka, va, st, idx, P, 0, h, np.arange(wl.L))
-        rows_done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    rows = 0
+    step = wl.block if wl.group == 0 else 64
+    while rows < wl.L and time.perf_counter() - t1 < budget_s:
+        toks = np.arange(rows, min(wl.L, rows + step))
+        po.attend_tokens(qa, ka, va, st, idx, P, 0, 0, toks)
+        rows += len(toks)
+    t2 = time.perf_counter()
+    head_time = (t1 - t0) + (t2 - t1) * wl.L / rows
     dense_pairs = (wl.L * (wl.L + 1) // 2) if wl.causal else wl.L * wl.L
-    flops = 4 * wl.d * dense_pairs * rows_done
-    cores = len(os.sched_getaffinity(0))
+    flops = 4 * wl.d * dense_pairs
     try:
         from threadpoolctl import threadpool_info
-        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        blas = cores
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas)),
+        threads = len(os.sched_getaffinity(0))
+    return {"value": round(flops / head_time / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"float64 NumPy oracle, whole path (block stats + selection + attention) for "
-                      f"{rows_done} of {wl.B * wl.Hq} query heads of the same workload, "
-                      f"{dt:.1f} s; dense-equivalent FLOPs / time"}
+            "sample": f"float64 NumPy oracle on query head 0 of batch 0: block stats + selection "
+                      f"({t1 - t0:.1f} s), then attention of its first {rows} of {wl.L} rows "
+                      f"({t2 - t1:.1f} s), scaled to the whole head; dense-equivalent FLOPs of one head "
+                      f"over the scaled time"}
+
+
+def hbm_traffic(kernel_src: str, launches_per_step: int = 1):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration factor), or None if that summary was taken on other source."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(kernel_src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -123,10 +145,22 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_dit")
-    ap.add_argument("--cpu-heads", type=int, default=1)
-    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run three plain device copies of MIB MiB (reads and writes MIB MiB "
+                         "each), to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -201,7 +235,8 @@ def main():
                    "value_is": "dense-equivalent FLOPs (4 d L^2 B H) / step time"},
         "roofline": {"bound": "mfma", "kernel": "pisa_sparse_attn_fwd",
                      "achieved": round(attn_achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": hbm_traffic(ATTN_SRC.get(wl.group == 0))},
         "kernels": {
             "block_stats": {"ms": round(ms_stats, 4), "GB/s": round(stats_gbs, 1),
                             "hbm_frac": round(stats_gbs / PEAK_HBM_GBS, 4)},
@@ -216,7 +251,7 @@ def main():
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_heads, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 
