@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12   # fp32 FMA on the VALU, not packed: 78.6
 # source of the attention kernel that runs for block rows (True) / PIVOT rows
 ATTN_SRC = {True: os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn_blocks.hip"),
             False: os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn.hip")}
@@ -78,9 +79,10 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
         stats_out += 2 * B * Hkv * n_blk * d * 4
     if taylor == "order1":
         stats_out += B * Hkv * n_blk * d * d * es
-    return dict(flop_exact=flop_exact, flop_taylor0=flop_t0, flop_taylor1=flop_t1,
-                flop_attn=flop_exact + flop_t0 + flop_t1, flop_dense=dense,
-                stats_bytes=qkv + stats_out, exact_pairs=exact, taylor_pairs=taylor_pairs)
+    return {k: int(v) for k, v in dict(flop_exact=flop_exact, flop_taylor0=flop_t0, flop_taylor1=flop_t1,
+                                        flop_attn=flop_exact + flop_t0 + flop_t1, flop_dense=dense,
+                                        stats_bytes=qkv + stats_out, exact_pairs=exact,
+                                        taylor_pairs=taylor_pairs).items()}
 
 
 def cpu_baseline(wl, q, k, v, budget_s: float) -> dict:
@@ -122,10 +124,11 @@ def cpu_baseline(wl, q, k, v, budget_s: float) -> dict:
                       f"over the scaled time"}
 
 
-def hbm_traffic(kernel_src: str, launches_per_step: int = 1):
+def hbm_traffic(kernel_src: str, workload: str):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
-    calibration factor), or None if that summary was taken on other source."""
+    calibration factor), or None if that summary was taken on other source
+    or another workload."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
     try:
         with open(path) as f:
@@ -134,7 +137,7 @@ def hbm_traffic(kernel_src: str, launches_per_step: int = 1):
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -213,6 +216,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     work = algorithmic_work(knobs, idx.cpu().numpy())
+    # bf16 runs on the matrix cores; the fp32 path is plain fp32 FMA on the
+    # VALU (no packed fp32): 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz
+    peak_kind, peak = ("mfma", PEAK_BF16_TFLOPS) if wl.dtype == "bf16" else ("alu", PEAK_F32_VALU_TFLOPS)
     tflops_eff = work["flop_dense"] / (ms_step * 1e-3) / 1e12
     attn_achieved = work["flop_attn"] / (ms_attn * 1e-3) / 1e12
     stats_gbs = work["stats_bytes"] / (ms_stats * 1e-3) / 1e9
@@ -233,18 +239,18 @@ def main():
                    "block": wl.block, "topk": wl.topk, "window": wl.window, "group": wl.group,
                    "n_cand": wl.n_cand, "causal": wl.causal, "taylor": wl.taylor,
                    "value_is": "dense-equivalent FLOPs (4 d L^2 B H) / step time"},
-        "roofline": {"bound": "mfma", "kernel": "pisa_sparse_attn_fwd",
-                     "achieved": round(attn_achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": hbm_traffic(ATTN_SRC.get(wl.group == 0))},
+        "roofline": {"bound": peak_kind, "kernel": "pisa_sparse_attn_fwd",
+                     "achieved": round(attn_achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attn_achieved / peak, 4),
+                     "traffic": hbm_traffic(ATTN_SRC[wl.group == 0], wl.name) if wl.dtype == "bf16" else None},
         "kernels": {
             "block_stats": {"ms": round(ms_stats, 4), "GB/s": round(stats_gbs, 1),
                             "hbm_frac": round(stats_gbs / PEAK_HBM_GBS, 4)},
             "indexer_topk": {"ms": round(ms_idx, 4)},
             "sparse_attn_fwd": {"ms": round(ms_attn, 4),
                                 "kept_mfma_frac": round(work["flop_exact"] / (ms_attn * 1e-3) / 1e12
-                                                        / PEAK_BF16_TFLOPS, 4),
-                                "total_mfma_frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
+                                                        / peak, 4),
+                                "total_mfma_frac": round(attn_achieved / peak, 4),
                                 "flop_exact": work["flop_exact"], "flop_taylor": work["flop_taylor0"]
                                 + work["flop_taylor1"]},
         },
