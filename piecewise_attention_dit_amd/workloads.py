@@ -231,7 +231,9 @@ def make_inputs(wl: Workload, seed: int | None = None):
                     noise = rng.standard_normal(size=(L, d))
                     eta = rng.standard_normal(size=(L, d))
                     eta[1:] *= c
-                    drift = lfilter([1.0], [1.0, -rho], eta, axis=0)
+                    # the recurrence runs along tokens; filtering the
+                    # transposed copy is the same arithmetic, contiguous
+                    drift = lfilter([1.0], [1.0, -rho], np.ascontiguousarray(eta.T), axis=-1).T
                     t[b, h] = _to_dtype(noise + drift, wl.dtype)
             outs.append(t)
         return tuple(outs)
