@@ -66,7 +66,8 @@ struct Cfg {
   static constexpr int TY_STL = TY_STH + D * kNB * 2;
   static constexpr int TY_AL = TY_STL + D * kNB * 2;          // fp32 [wave][entry][32 rows]
   static constexpr int TY_NJ = TY_AL + NW * kNB * 32 * 4;
-  static constexpr int TY_END = TY_NJ + kNB * 4;
+  static constexpr int TY_STG = TY_NJ + kNB * 4;              // fp32 [2][kNB][D]: next batch's kbar, vsum rows
+  static constexpr int TY_END = TY_STG + 2 * kNB * D * 4;
   static constexpr int MAIN = EX_END > TY_END ? EX_END : TY_END;
   static constexpr int LST = MAIN;                            // uint16 [P][kMaxK] kept lists
   static constexpr int PRV = LST + P * kMaxK * 2;             // uint16 [P][kMaxK] private parts
@@ -77,7 +78,9 @@ struct Cfg {
   static constexpr int CNT = TYL + 1024 * 2;                  // int [16]
   static constexpr int TOTAL = CNT + 64;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  static_assert(CPS % (NW / 2) == 0 && HCH % NW == 0, "DMA must split evenly over the waves");
+  static constexpr int STGCH = 2 * kNB * D * 4 / 1024;          // staging kilobytes per batch
+  static_assert(CPS % (NW / 2) == 0 && HCH % (NW / 2) == 0 && STGCH % (NW / 2) == 0,
+                "DMA must split evenly over the issuing waves");
   static_assert(kNB * (D / 8) <= NT, "one table unit per thread");
 };
 
@@ -484,40 +487,71 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     float *nj = reinterpret_cast<float *>(lds + C::TY_NJ);
     const uint32_t *kb_me = kbm + part * 32;
     const bool order1 = taylor == 2;
-    constexpr int PER_H = C::HCH / NW;
-    int offh[PER_H];
+    // Loads of the Taylor phase are issued by waves 0..NDW-1 (as in the exact
+    // phase): H_j tiles (PH kilobytes per issuing wave) and, half a batch
+    // ahead, the next batch's kbar and vsum rows into an LDS staging area.
+    constexpr int NDW = NW / 2, PH = C::HCH / NDW, PS = C::STGCH / NDW;
+    const bool issuer = w < NDW;
+    int offh[PH];
 #pragma unroll
-    for (int u = 0; u < PER_H; ++u) {
-      const int pos = (w + NW * u) * 64 + l;
+    for (int u = 0; u < PH; ++u) {
+      const int pos = (w % NDW + NDW * u) * 64 + l;
       const int row = pos / (D / 8), phys = pos % (D / 8);
       offh[u] = (row * D + ((phys ^ kswz<D>(row)) << 3)) * 2;
     }
     auto dma_h = [&](int eg) {
+      if (!issuer) return;
       const uint16_t *src = HTh + (size_t)__builtin_amdgcn_readfirstlane(tyl[eg]) * D * D;
       uint8_t *dst = lds + C::TY_H + (eg % kRingH) * C::HT;
 #pragma unroll
-      for (int u = 0; u < PER_H; ++u) dma16_buf(src, D * D * 2, offh[u], dst + (w + NW * u) * 1024);
+      for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], dst + (w + NDW * u) * 1024);
     };
+    // staging kilobyte c holds rows c * RPC .. of [kbar entries | vsum entries]
+    constexpr int RPC = 1024 / (D * 4), LPR = 64 / RPC;   // rows per kilobyte, lanes per row
+    const int tbl_bytes = dm.n_blk * D * 4;
+    auto stage = [&](int b0) {
+      if (!issuer) return;
+      const int nb = min(kNB, n_ty - b0);
+#pragma unroll
+      for (int u = 0; u < PS; ++u) {
+        const int c = w + NDW * u;
+        const int row = c * RPC + l / LPR;             // 0 .. 2 kNB - 1
+        const int en = row % kNB;
+        const int j = tyl[b0 + min(en, nb - 1)];
+        const int voff = en < nb ? j * D * 4 + (l % LPR) * 16 : tbl_bytes;   // past the end: zeros
+        dma16_buf(row < kNB ? (const void *)kbar : (const void *)vsum, tbl_bytes, voff,
+                  lds + C::TY_STG + c * 1024);
+      }
+    };
+    stage(0);
     if (order1) {
       dma_h(0);
       if (n_ty > 1) dma_h(1);
     }
+    const float *stg = reinterpret_cast<const float *>(lds + C::TY_STG);
     uint32_t tmask = 0;
     for (int eg = 0; eg < n_ty; ++eg) {
       const int e = eg % kNB;
       if (e == 0) {
         const int nb = min(kNB, n_ty - eg);
-        __syncthreads();   // the previous batch's tables are consumed
+        // this batch's staged rows have landed (H waits of the previous
+        // steps cover them in order; the first batch waits here)
+        if (!order1) wait_vmcnt<0>();
+        else if (eg == 0) {
+          if (n_ty > 1) wait_vmcnt<2 * PH>();
+          else wait_vmcnt<PH>();
+        }
+        __syncthreads();   // the previous batch's tables are consumed; staging landed
         if (tid < kNB * (D / 8)) {
           const int en = tid / (D / 8), ch = tid % (D / 8);
           u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
           float sv[8];
           if (en < nb) {
             const int j = tyl[eg + en];
-            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(kbar + (size_t)j * D + ch * 8);
-            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(kbar + (size_t)j * D + ch * 8 + 4);
-            const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(vsum + (size_t)j * D + ch * 8);
-            const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(vsum + (size_t)j * D + ch * 8 + 4);
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8 + 4);
+            const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8);
+            const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8 + 4);
             const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -550,12 +584,13 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           }
         }
         __syncthreads();
-        tmask = 0;
-        if (pvalid) {
-          for (int en = 0; en < nb; ++en) {
-            const int j = tyl[eg + en];
-            if (j < nc && !((kb_me[j >> 5] >> (j & 31)) & 1u)) tmask |= 1u << en;
+        {   // lane en < nb decides entry en for this wave's part
+          bool mine = false;
+          if (pvalid && l < nb) {
+            const int j = tyl[eg + l];
+            mine = j < nc && !((kb_me[j >> 5] >> (j & 31)) & 1u);
           }
+          tmask = (uint32_t)ballot64(mine);
         }
         if (tmask) {
           f32x16_t at = f32x16_t{};
@@ -609,26 +644,46 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           }
         }
       }
+      // the next batch's kbar / vsum rows, half a batch ahead (this batch's
+      // tables were built before the batch-start barrier)
+      if (e == kNB / 2 && eg - e + kNB < n_ty) stage(eg - e + kNB);
       if (!order1) continue;
       // first order for entry eg: H ring (3 deep, two ahead)
-      if (eg + 1 < n_ty) wait_vmcnt<PER_H>();
+      if (eg + 1 < n_ty) wait_vmcnt<PH>();
       else wait_vmcnt<0>();
       __syncthreads();   // H_eg landed for all waves; slot (eg + 2) % 3 is free
       if (eg + 2 < n_ty) dma_h(eg + 2);
       if ((tmask >> e) & 1u) {
+        // u = H_j^T Q^T tile by tile (MFMA k: output tile k / KS, K-step
+        // k % KS), scheduled by hand: the LDS read of the fragment four MFMAs
+        // ahead, and chunk c of O += (alpha scale) u, 16 / KS values of tile
+        // c / KS, two MFMAs after that tile's last MFMA.
         const uint8_t *hp = lds + C::TY_H + (eg % kRingH) * C::HT;
         const float al = alp[e * 32 + lq];
+        constexpr int KS = D / 16, NMT = NE * KS, FPC = 16 / KS;
+        auto hfrag = [&](int k) { return frag_a<D>(hp, (k / KS) * 32 + lq, 2 * (k % KS) + hl); };
+        auto fchunk = [&](const f32x16_t (&uu)[NE], int c) {
+#pragma unroll
+          for (int i = 0; i < FPC; ++i) {
+            const int et = c / KS, r = (c % KS) * FPC + i;
+            oacc[et][r] = fmaf(al, uu[et][r], oacc[et][r]);
+          }
+        };
+        u32x4_t fr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fr[k] = hfrag(k);
         f32x16_t u[NE];
 #pragma unroll
-        for (int et = 0; et < NE; ++et) {
-          u[et] = f32x16_t{};
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) u[et] = mfma32(frag_a<D>(hp, et * 32 + lq, 2 * ks + hl), qf[ks], u[et]);
+        for (int k = 0; k < NMT; ++k) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int et = k / KS, ks = k % KS;
+          u[et] = mfma32(fr[k % 4], qf[ks], ks == 0 ? f32x16_t{} : u[et]);
+          if (k + 4 < NMT) fr[k % 4] = hfrag(k + 4);
+          if (k >= KS + 1) fchunk(u, k - KS - 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int et = 0; et < NE; ++et)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[et][r] = fmaf(al, u[et][r], oacc[et][r]);
+        for (int c = NMT - KS - 1; c < NMT; ++c) fchunk(u, c);
       }
     }
   }
