@@ -132,6 +132,22 @@ PISA_DEV int wave_incl_scan(int v) {
 }
 PISA_DEV uint64_t ballot64(bool p) { return __ballot(p); }
 
+// x plus the value of lane l ^ 32 (v_permlane32_swap_b32 swaps the upper
+// half of one register with the lower half of another: with both operands x
+// the two results hold x and its partner on every lane)
+PISA_DEV float pair_sum_f(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Make this wave's LDS writes (and LDS atomics) visible to its own later LDS
+// reads, without a workgroup barrier: a memory fence plus a code-motion
+// barrier for the wave.
+PISA_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------- MFMA
 
 // Operands travel as packed u32x4 (8 bf16 in 4 registers) and are

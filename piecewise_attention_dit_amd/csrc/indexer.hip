@@ -174,12 +174,12 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int nc
   uint64_t tau = 0;
   for (;;) {
     for (int b = l; b < 256; b += 64) sh.hist[b] = 0;
-    __syncthreads();
+    wave_lds_sync();
     const uint64_t hi_mask = (shift + 8 >= 64) ? 0ull : ~((1ull << (shift + 8)) - 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       if (valid[s] && (key[s] & hi_mask) == prefix) atomicAdd(&sh.hist[(key[s] >> shift) & 255u], 1u);
-    __syncthreads();
+    wave_lds_sync();
     int h[4];
     int cnt = 0;
 #pragma unroll
@@ -213,7 +213,7 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int nc
     bin = __shfl(bin, owner);
     above = __shfl(above, owner);
     hb = __shfl(hb, owner);
-    __syncthreads();
+    wave_lds_sync();
     need -= above;
     prefix |= (uint64_t)bin << shift;
     if (hb == need || shift == 0) {
@@ -375,6 +375,458 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// PIVOT rows on the matrix cores (bf16, d 64 or 128).
+//
+// A workgroup of 8 waves takes up to 32 proxies that share a KV head and a
+// query block (the query heads of the KV head times the groups of the
+// block), so they share the candidate blocks up to their causal limit:
+//   1. proxy scores S[p][j] = qsel_p . ksel_j for all candidates at once on
+//      MFMA 32x32x16 (ksel rows as A straight from memory, the 32 proxies
+//      as B), with |ksel_j|^2 from the same loads;
+//   2. each proxy's top-C from its row of S: radix select on unique keys,
+//      certified by the rigorous bound D 2^-22 |p| |k| of an fp32 sum of the
+//      exact bf16 products.  Undecided candidates are re-scored in float64 by
+//      the whole wave (exact products, a float64 tree sum with its bound)
+//      and the row is selected and certified again;
+//   3. each member's top-k of its proxy's list: MFMA of the gathered list
+//      rows against the group's member queries, then the same select.
+// Rows still undecided after the float64 re-score (exact ties of different
+// vectors) are left to wave 0, which re-runs them with select_row's exact
+// path once the other waves are done.
+
+constexpr int kPX = 32;        // proxies per workgroup
+constexpr int kPCap = 128;     // proxy list capacity of this path
+constexpr int kPNc = 1024;     // candidate capacity
+constexpr int kPW = 8;         // waves
+constexpr int kPG = 16;        // group size capacity (members per proxy)
+
+struct PivotLayout {
+  static constexpr int SLD = kPNc + 4;                 // floats per proxy row of S (padded)
+  static constexpr int MLD = kPCap + 4;                // floats per member row of the member scores
+  static constexpr int S = 0;                          // fp32 [kPX][SLD]; then member scores
+                                                       // [kPW][kPG][MLD]; then select_row's Shared
+  static constexpr int KN = S + kPX * SLD * 4;         // fp32 [kPNc] |ksel_j|^2
+  static constexpr int PN = KN + kPNc * 4;             // fp32 [kPX] |qsel_p|^2
+  static constexpr int PV = PN + kPX * 4;              // fp32 [kPW][128] row vector under re-score
+  static constexpr int LIST = PV + kPW * 128 * 4;      // uint16 [kPX][kPCap] proxy lists, ascending
+  static constexpr int HIST = LIST + kPX * kPCap * 2;  // u32 [kPW][256] radix histograms
+  static constexpr int DEFN = HIST + kPW * 256 * 4;    // int [4]: deferred proxies, deferred members
+  static constexpr int DEFP = DEFN + 16;               // int [kPX]
+  static constexpr int DEFM = DEFP + kPX * 4;          // int [kPX * kPG] (token * 64 + proxy)
+  static constexpr int TOTAL = DEFM + kPX * kPG * 4;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(kPW * kPG * MLD * 4 <= kPX * SLD * 4, "member scores fit in S");
+  static_assert((int)sizeof(Shared) <= kPX * SLD * 4, "select_row's Shared fits in S");
+};
+
+// float64 score of row vector p (fp32 copy in LDS) against ksel row kr, by
+// the whole wave: exact products, a float64 tree sum; *bound receives a
+// rigorous bound on its error (depth 8 tree, doubled).
+template <int D>
+PISA_DEV double rescore64(const float *p, const uint16_t *kr, double *bound) {
+  const int l = lane_id();
+  double s = 0.0, a = 0.0;
+  for (int c = l; c < D; c += 64) {
+    const double x = (double)p[c] * (double)bf16_to_f32(kr[c]);
+    s += x;
+    a += fabs(x);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    s += __shfl_xor(s, o);
+    a += __shfl_xor(a, o);
+  }
+  *bound = 16.0 * 0x1p-53 * a + 0x1p-1000;
+  return s;
+}
+
+// Select the n_take best of the slot candidates (scores sc, bounds dl, ids
+// cj; slot s of lane l is candidate s * 64 + l) into sel.  Returns false if
+// the selection could not be certified even after re-scoring the undecided
+// candidates in float64 (the caller then defers the row).  p: fp32 copy of
+// the row vector in LDS; kbase: ksel rows of the KV head.
+template <int D, int NS>
+PISA_DEV bool select_scored(uint32_t *hist, double (&sc)[NS], double (&dl)[NS], const int (&cj)[NS],
+                            const bool (&valid)[NS], int n_take, bool (&sel)[NS], const float *p,
+                            const uint16_t *kbase, int32_t *diag) {
+  const int l = lane_id();
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    uint64_t key[NS];
+    uint64_t kmax = 0, kmin = ~0ull;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      key[s] = valid[s] ? (((uint64_t)ord32((float)sc[s]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)cj[s])) : 0ull;
+      if (valid[s]) {
+        kmax = key[s] > kmax ? key[s] : kmax;
+        kmin = key[s] < kmin ? key[s] : kmin;
+      }
+    }
+    kmax = wave_max_u64(kmax);
+    kmin = wave_min_u64(kmin);
+    const uint64_t diff = kmax ^ kmin;
+    int shift = diff ? ((63 - __clzll(diff)) & ~7) : 0;
+    uint64_t prefix = (shift + 8 >= 64) ? 0ull : (kmax >> (shift + 8)) << (shift + 8);
+    int need = n_take;
+    uint64_t tau = 0;
+    for (;;) {
+      for (int bb = l; bb < 256; bb += 64) hist[bb] = 0;
+      wave_lds_sync();
+      const uint64_t hi_mask = (shift + 8 >= 64) ? 0ull : ~((1ull << (shift + 8)) - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if (valid[s] && (key[s] & hi_mask) == prefix) atomicAdd(&hist[(key[s] >> shift) & 255u], 1u);
+      wave_lds_sync();
+      int h[4];
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = (int)hist[255 - 4 * l - q];
+        cnt += h[q];
+      }
+      const int incl = wave_incl_scan(cnt);
+      const int excl = incl - cnt;
+      const bool mine = excl < need && need <= incl;
+      const uint64_t bal = ballot64(mine);
+      if (!bal) {   // unreachable for consistent counts; keeps the loop finite
+        tau = prefix;
+        break;
+      }
+      const int owner = __ffsll((unsigned long long)bal) - 1;
+      int bin = 0, above = 0, hb = 0;
+      if (mine) {
+        int run = excl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (run + h[q] >= need) {
+            bin = 255 - 4 * l - q;
+            above = run;
+            hb = h[q];
+            break;
+          }
+          run += h[q];
+        }
+      }
+      bin = __shfl(bin, owner);
+      above = __shfl(above, owner);
+      hb = __shfl(hb, owner);
+      wave_lds_sync();
+      need -= above;
+      prefix |= (uint64_t)bin << shift;
+      if (hb == need || shift == 0) {
+        tau = prefix;
+        break;
+      }
+      shift -= 8;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sel[s] = valid[s] && key[s] >= tau;
+    double t_in = __builtin_huge_val(), t_out = -__builtin_huge_val();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (!valid[s]) continue;
+      if (sel[s]) t_in = fmin(t_in, sc[s] - dl[s]);
+      else t_out = fmax(t_out, sc[s] + dl[s]);
+    }
+    t_in = wave_min_f64(t_in);
+    t_out = wave_max_f64(t_out);
+    if (t_in > t_out) return true;
+    if (attempt == 1) break;
+    // re-score the undecided candidates in float64 and select again
+    if (diag && l == 0) atomicAdd(&diag[1], 1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bool amb = valid[s] && (sel[s] ? (sc[s] - dl[s] <= t_out) : (sc[s] + dl[s] >= t_in));
+      uint64_t m = ballot64(amb);
+      while (m) {
+        const int lb = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const int j = __shfl(cj[s], lb);
+        double bnd;
+        const double v = rescore64<D>(p, kbase + (size_t)j * D, &bnd);
+        if (l == lb) {
+          sc[s] = v;
+          dl[s] = bnd;
+        }
+      }
+    }
+  }
+  return false;
+}
+
+// ids of the selected slots, ascending, to LDS (uint16) and optionally to
+// global memory (int32, -1 padded to len)
+template <int NS>
+PISA_DEV void write_sorted_lds(const bool (&sel)[NS], const int (&cj)[NS], uint16_t *lout, int32_t *gout,
+                               int len) {
+  const int l = lane_id();
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint64_t m = ballot64(sel[s]);
+    if (sel[s]) {
+      const int pos = base + __popcll(m & ((1ull << l) - 1));
+      if (lout) lout[pos] = (uint16_t)cj[s];
+      if (gout) gout[pos] = cj[s];
+    }
+    base += __popcll(m);
+  }
+  if (gout)
+    for (int pos = base + l; pos < len; pos += 64) gout[pos] = -1;
+}
+
+template <int D>
+PISA_DEV void load_vec_f32(float *dst, const uint16_t *src) {
+  for (int c = lane_id(); c < D; c += 64) dst[c] = bf16_to_f32(src[c]);
+  wave_lds_sync();
+}
+
+// select_row's inputs for one row vector, loaded by one wave
+template <int D>
+PISA_DEV void load_p_wave(Shared &sh, const uint16_t *src) {
+  for (int c = lane_id(); c < D; c += 64) {
+    const float v = bf16_to_f32(src[c]);
+    sh.pf[c] = v;
+    sh.p[c] = (double)v;
+  }
+  wave_lds_sync();
+}
+
+template <int D>
+__global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, const uint16_t *__restrict__ Q,
+                                                                 const uint16_t *__restrict__ qsel,
+                                                                 const uint16_t *__restrict__ ksel,
+                                                                 int32_t *__restrict__ idx,
+                                                                 int32_t *__restrict__ cand, int32_t *diag) {
+  using LY = PivotLayout;
+  constexpr int KS = D / 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = dm.group;
+  const int gpb = dm.bs / g;                  // groups per block
+  const int npb = dm.ratio * gpb;             // proxies per (KV head, block)
+  const int nchunk = (npb + kPX - 1) / kPX;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int cq = logical % nchunk;
+  const int rest = logical / nchunk;
+  const int iblk = rest % dm.n_blk;
+  const int bk = rest / dm.n_blk;
+  const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
+  const uint16_t *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
+  float *S = reinterpret_cast<float *>(lds + LY::S);
+  float *KN = reinterpret_cast<float *>(lds + LY::KN);
+  float *PN = reinterpret_cast<float *>(lds + LY::PN);
+  float *PVw = reinterpret_cast<float *>(lds + LY::PV) + w * 128;
+  uint16_t *LIST = reinterpret_cast<uint16_t *>(lds + LY::LIST);
+  uint32_t *histw = reinterpret_cast<uint32_t *>(lds + LY::HIST) + w * 256;
+  int *defn = reinterpret_cast<int *>(lds + LY::DEFN);
+  int *defp = reinterpret_cast<int *>(lds + LY::DEFP);
+  int *defm = reinterpret_cast<int *>(lds + LY::DEFM);
+  Shared &sh = *reinterpret_cast<Shared *>(lds + LY::S);
+
+  // proxy pp of this workgroup -> (query head, group), candidate count
+  auto proxy = [&](int pl, int &h, int &gm, int &nc) -> bool {
+    const int pp = cq * kPX + pl;
+    h = hk * dm.ratio + pp / gpb;
+    gm = iblk * gpb + pp % gpb;
+    int own, lo;
+    nc = pisa_row_geometry(dm, gm * g, &own, &lo);
+    return pp < npb && gm * g < dm.L;
+  };
+  int ph, pgm, pnc;
+  const bool pval = proxy(lq, ph, pgm, pnc);
+  const int ncmax = __builtin_amdgcn_readfirstlane(wave_max_f32(pval ? (float)pnc : 0.f));
+  if (tid < 4) defn[tid] = 0;
+
+  // ---- 1. proxy scores, |k|^2 and |p|^2
+  u32x4_t pf[KS];
+  float p2 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    pf[ks] = pval ? *reinterpret_cast<const u32x4_t *>(qsel + ((size_t)(b * dm.Hq + ph) * dm.n_sel + pgm) * D +
+                                                       16 * ks + 8 * hl)
+                  : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p2 += bf16lo(pf[ks][i]) * bf16lo(pf[ks][i]) + bf16hi(pf[ks][i]) * bf16hi(pf[ks][i]);
+  }
+  p2 = pair_sum_f(p2);
+  if (w == 0 && hl == 0) PN[lq] = p2;
+  const int ntile = (ncmax + 31) / 32;
+  for (int t = w; t < ntile; t += kPW) {
+    const int j = t * 32 + lq;
+    const int jr = j < dm.n_blk ? j : dm.n_blk - 1;
+    u32x4_t ka[KS];
+    float k2 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ka[ks] = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)jr * D + 16 * ks + 8 * hl);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k2 += bf16lo(ka[ks][i]) * bf16lo(ka[ks][i]) + bf16hi(ka[ks][i]) * bf16hi(ka[ks][i]);
+    }
+    k2 = pair_sum_f(k2);
+    if (hl == 0 && j < kPNc) KN[j] = k2;
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], pf[ks], acc);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int j0 = t * 32 + 8 * g4 + 4 * hl;
+      if (j0 < kPNc)
+        *reinterpret_cast<f32x4_t *>(S + lq * LY::SLD + j0) =
+            f32x4_t{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+    }
+  }
+  __syncthreads();
+
+  constexpr double kG32 = D * 0x1p-22;   // fp32 accumulation bound factor (doubled)
+  // ---- 2. proxy top-C
+  for (int pl = w; pl < kPX; pl += kPW) {
+    int h, gm, nc;
+    if (!proxy(pl, h, gm, nc)) continue;
+    const int C = min(dm.n_cand, nc);
+    int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
+    uint16_t *lout = LIST + pl * kPCap;
+    if (diag && l == 0) atomicAdd(&diag[0], 1);
+    if (C >= nc) {   // every candidate
+      for (int c = l; c < nc; c += 64) lout[c] = (uint16_t)c;
+      if (gout)
+        for (int c = l; c < dm.n_cand; c += 64) gout[c] = c < nc ? c : -1;
+      continue;
+    }
+    load_vec_f32<D>(PVw, qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D);
+    const float pn = PN[pl];
+    double sc[kMaxSlots], dl[kMaxSlots];
+    int cj[kMaxSlots];
+    bool valid[kMaxSlots], sel[kMaxSlots];
+#pragma unroll
+    for (int s = 0; s < kMaxSlots; ++s) {
+      const int c = s * 64 + l;
+      valid[s] = c < nc;
+      cj[s] = c;
+      sc[s] = valid[s] ? (double)S[pl * LY::SLD + c] : 0.0;
+      dl[s] = valid[s] ? kG32 * sqrt((double)pn * (double)KN[c]) + 0x1p-1000 : 0.0;
+    }
+    if (select_scored<D, kMaxSlots>(histw, sc, dl, cj, valid, C, sel, PVw, kbase, diag))
+      write_sorted_lds<kMaxSlots>(sel, cj, lout, gout, dm.n_cand);
+    else if (l == 0)
+      defp[atomicAdd(&defn[0], 1)] = pl;
+  }
+  __syncthreads();
+  if (w == 0) {   // undecided proxies: select_row's exact path
+    const int nd = defn[0];
+    for (int q = 0; q < nd; ++q) {
+      const int pl = defp[q];
+      int h, gm, nc;
+      proxy(pl, h, gm, nc);
+      const int C = min(dm.n_cand, nc);
+      load_p_wave<D>(sh, qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D);
+      bool sel[kMaxSlots];
+      int cj[kMaxSlots];
+      select_row<uint16_t, D, kMaxSlots>(sh, kbase, nullptr, nc, C, sel, cj, diag);
+      int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
+      write_sorted_lds<kMaxSlots>(sel, cj, LIST + pl * kPCap, gout, dm.n_cand);
+      if (diag && l == 0) atomicAdd(&diag[2], 1);
+    }
+  }
+  __syncthreads();
+  if (dm.topk == 0) return;
+
+  // ---- 3. members: top-k of the proxy's list
+  float *Mw = S + w * kPG * LY::MLD;
+  for (int pl = w; pl < kPX; pl += kPW) {
+    int h, gm, nc;
+    if (!proxy(pl, h, gm, nc)) continue;
+    const int C = min(dm.n_cand, nc);
+    const int n_take = min(dm.topk, C);
+    const uint16_t *list = LIST + pl * kPCap;
+    const int t0 = gm * g, t1 = min(dm.L, t0 + g);
+    const size_t qrow0 = (size_t)(b * dm.Hq + h) * dm.L;
+    if (n_take >= C) {   // the whole list
+      for (int t = t0; t < t1; ++t) {
+        int32_t *out = idx + (qrow0 + t) * dm.topk;
+        for (int c = l; c < dm.topk; c += 64) out[c] = c < C ? (int32_t)list[c] : -1;
+        if (diag && l == 0) atomicAdd(&diag[0], 1);
+      }
+      continue;
+    }
+    // member queries as B (lane lq = member), scores of the list rows as A
+    const bool mval = lq < t1 - t0;
+    u32x4_t mq[KS];
+    float q2 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      mq[ks] = mval ? *reinterpret_cast<const u32x4_t *>(Q + (qrow0 + t0 + lq) * D + 16 * ks + 8 * hl)
+                    : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q2 += bf16lo(mq[ks][i]) * bf16lo(mq[ks][i]) + bf16hi(mq[ks][i]) * bf16hi(mq[ks][i]);
+    }
+    q2 = pair_sum_f(q2);
+    const int nct = (C + 31) / 32;
+    for (int ct = 0; ct < nct; ++ct) {
+      const int pos = ct * 32 + lq;
+      const int j = list[pos < C ? pos : 0];
+      u32x4_t ka[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)j * D + 16 * ks + 8 * hl);
+      f32x16_t acc = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], mq[ks], acc);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int p0 = ct * 32 + 8 * g4 + 4 * hl;
+        if (mval)
+          *reinterpret_cast<f32x4_t *>(Mw + lq * LY::MLD + p0) =
+              f32x4_t{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+      }
+    }
+    wave_lds_sync();
+    for (int m = 0; m < t1 - t0; ++m) {
+      const int t = t0 + m;
+      const float qn = __shfl(q2, m);
+      if (diag && l == 0) atomicAdd(&diag[0], 1);
+      load_vec_f32<D>(PVw, Q + (qrow0 + t) * D);
+      constexpr int NS = kPCap / 64;
+      double sc[NS], dl[NS];
+      int cj[NS];
+      bool valid[NS], sel[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int pos = s * 64 + l;
+        valid[s] = pos < C;
+        cj[s] = valid[s] ? (int)list[pos] : 0;
+        sc[s] = valid[s] ? (double)Mw[m * LY::MLD + pos] : 0.0;
+        dl[s] = valid[s] ? kG32 * sqrt((double)qn * (double)KN[cj[s]]) + 0x1p-1000 : 0.0;
+      }
+      if (select_scored<D, NS>(histw, sc, dl, cj, valid, n_take, sel, PVw, kbase, diag))
+        write_sorted_lds<NS>(sel, cj, nullptr, idx + (qrow0 + t) * dm.topk, dm.topk);
+      else if (l == 0)
+        defm[atomicAdd(&defn[1], 1)] = t * 64 + pl;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {   // undecided members: select_row's exact path over the proxy's list
+    const int nd = defn[1];
+    for (int q = 0; q < nd; ++q) {
+      const int t = defm[q] >> 6, pl = defm[q] & 63;
+      int h, gm, nc;
+      proxy(pl, h, gm, nc);
+      const int C = min(dm.n_cand, nc);
+      const int n_take = min(dm.topk, C);
+      for (int c = l; c < C; c += 64) sh.clist[c] = LIST[pl * kPCap + c];
+      load_p_wave<D>(sh, Q + ((size_t)(b * dm.Hq + h) * dm.L + t) * D);
+      bool sel[kPCap / 64];
+      int cj[kPCap / 64];
+      select_row<uint16_t, D, kPCap / 64>(sh, kbase, sh.clist, C, n_take, sel, cj, diag);
+      write_sorted_lds<kPCap / 64>(sel, cj, nullptr, idx + ((size_t)(b * dm.Hq + h) * dm.L + t) * dm.topk,
+                                   dm.topk);
+      if (diag && l == 0) atomicAdd(&diag[2], 1);
+      wave_lds_sync();
+    }
+  }
+}
+
 __global__ void zero_diag(int32_t *d) {
   if (threadIdx.x < 16) d[threadIdx.x] = 0;
 }
@@ -383,6 +835,25 @@ template <typename T, int D>
 hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, int32_t *idx,
                     int32_t *cand, int32_t *diag, hipStream_t st) {
   if (diag) zero_diag<<<1, 64, 0, st>>>(diag);
+  if constexpr (sizeof(T) == 2) {
+    if (dm.group >= 1 && dm.n_cand <= kPCap && dm.group <= kPG) {
+      using LY = PivotLayout;
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&indexer_pivot_mfma<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::TOTAL);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      const int npb = dm.ratio * (dm.bs / dm.group);
+      const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk * ((npb + kPX - 1) / kPX);
+      indexer_pivot_mfma<D><<<grid, kPW * 64, LY::TOTAL, st>>>(dm, static_cast<const uint16_t *>(Q),
+                                                               static_cast<const uint16_t *>(qsel),
+                                                               static_cast<const uint16_t *>(ksel), idx, cand,
+                                                               diag);
+      return hipGetLastError();
+    }
+  }
   if (dm.group >= 1) {
     const unsigned grid = (unsigned)dm.B * dm.Hq * dm.n_sel;
     indexer_pivot<T, D><<<grid, 64, 0, st>>>(dm, static_cast<const T *>(Q), static_cast<const T *>(qsel),
