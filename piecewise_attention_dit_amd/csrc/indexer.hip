@@ -378,47 +378,196 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
 // ---------------------------------------------------------------------------
 // PIVOT rows on the matrix cores (bf16, d 64 or 128).
 //
-// A workgroup of 8 waves takes up to 32 proxies that share a KV head and a
+// A workgroup of 16 waves takes up to 32 proxies that share a KV head and a
 // query block (the query heads of the KV head times the groups of the
 // block), so they share the candidate blocks up to their causal limit:
 //   1. proxy scores S[p][j] = qsel_p . ksel_j for all candidates at once on
 //      MFMA 32x32x16 (ksel rows as A straight from memory, the 32 proxies
-//      as B), with |ksel_j|^2 from the same loads;
-//   2. each proxy's top-C from its row of S: radix select on unique keys,
-//      certified by the rigorous bound D 2^-22 |p| |k| of an fp32 sum of the
-//      exact bf16 products.  Undecided candidates are re-scored in float64 by
-//      the whole wave (exact products, a float64 tree sum with its bound)
-//      and the row is selected and certified again;
+//      as B), with |ksel_j| from the same loads;
+//   2. each proxy's top-C from its row of S;
 //   3. each member's top-k of its proxy's list: MFMA of the gathered list
-//      rows against the group's member queries, then the same select.
-// Rows still undecided after the float64 re-score (exact ties of different
-// vectors) are left to wave 0, which re-runs them with select_row's exact
-// path once the other waves are done.
+//      rows against up to 8 member queries, then the same selection.
+// Selection of one row by one wave, in three tiers:
+//   fast    keys ord(fp32 score); the n-th largest key found by bisection
+//           over its 32 bits, each step one compare per slot and a ballot
+//           count; the set is accepted when it is certified: every kept
+//           lower bound s - e exceeds every dropped upper bound s + e, with
+//           e = D 2^-22 |p| |k| + 2^-110 (see pivot_bound below);
+//   re-score  (rare, a function of its own) candidates whose intervals
+//           straddle the threshold get float64 scores with a float64 bound,
+//           the row is selected again on float64 keys and certified;
+//   exact   rows still undecided (exact ties of different vectors) are left to
+//           wave 0, which re-runs them with select_row's exact path once the
+//           other waves are done.
 
 constexpr int kPX = 32;        // proxies per workgroup
 constexpr int kPCap = 128;     // proxy list capacity of this path
 constexpr int kPNc = 1024;     // candidate capacity
-constexpr int kPW = 8;         // waves
+constexpr int kPW = 16;        // waves
 constexpr int kPG = 16;        // group size capacity (members per proxy)
+constexpr int kPM = 8;         // members scored per MFMA pass
+
+// Rounding bound of an fp32 score computed by MFMA from bf16 operands.  The
+// products are exact in fp32; a sum of D of them in fp32 (any order, round
+// to nearest or toward zero) is off by at most 2 D 2^-24 sum|p_i k_i| <=
+// D 2^-23 |p| |k|.  The factor used, D 2^-22, is twice that, which also
+// covers the rounding of the norms (fp32 sums of squares, square roots), of
+// the bound's own products and of the subtraction s - e / addition s + e in
+// the certification (each a few units of 2^-24 |p| |k|).  The norms are
+// taken of |x|^2 + 2^-118, so squares that underflow cannot make them too
+// small, and the absolute term 2^-110 covers products and partial sums
+// flushed to zero (at most 2 D 2^-126).
+constexpr float kAbsBound = 0x1p-110f;
+constexpr float kSqFloor = 0x1p-118f;
+template <int D>
+constexpr float pivot_bound() { return (float)D * 0x1p-22f; }
 
 struct PivotLayout {
   static constexpr int SLD = kPNc + 4;                 // floats per proxy row of S (padded)
   static constexpr int MLD = kPCap + 4;                // floats per member row of the member scores
   static constexpr int S = 0;                          // fp32 [kPX][SLD]; then member scores
-                                                       // [kPW][kPG][MLD]; then select_row's Shared
-  static constexpr int KN = S + kPX * SLD * 4;         // fp32 [kPNc] |ksel_j|^2
-  static constexpr int PN = KN + kPNc * 4;             // fp32 [kPX] |qsel_p|^2
-  static constexpr int PV = PN + kPX * 4;              // fp32 [kPW][128] row vector under re-score
+                                                       // [kPW][kPM][MLD]; then select_row's Shared
+  static constexpr int SKN = S + kPX * SLD * 4;        // fp32 [kPNc] |ksel_j|
+  static constexpr int SPN = SKN + kPNc * 4;           // fp32 [kPX] |qsel_p|
+  static constexpr int PV = SPN + kPX * 4;             // fp32 [kPW][128] row vector under re-score
   static constexpr int LIST = PV + kPW * 128 * 4;      // uint16 [kPX][kPCap] proxy lists, ascending
-  static constexpr int HIST = LIST + kPX * kPCap * 2;  // u32 [kPW][256] radix histograms
-  static constexpr int DEFN = HIST + kPW * 256 * 4;    // int [4]: deferred proxies, deferred members
+  static constexpr int DEFN = LIST + kPX * kPCap * 2;  // int [4]: deferred proxies, deferred members
   static constexpr int DEFP = DEFN + 16;               // int [kPX]
   static constexpr int DEFM = DEFP + kPX * 4;          // int [kPX * kPG] (token * 64 + proxy)
   static constexpr int TOTAL = DEFM + kPX * kPG * 4;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  static_assert(kPW * kPG * MLD * 4 <= kPX * SLD * 4, "member scores fit in S");
+  static_assert(kPW * kPM * MLD * 4 <= kPX * SLD * 4, "member scores fit in S");
   static_assert((int)sizeof(Shared) <= kPX * SLD * 4, "select_row's Shared fits in S");
 };
+
+// ---- wave reductions on the cross-lane data path (DPP and permlane swaps)
+template <int Ctrl>
+PISA_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+// maximum over the wave, the same in every lane
+PISA_DEV float wave_max_xl(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Largest threshold t with at least `need` keys >= t (keys of invalid slots
+// are 0 and never counted: every probe is >= 1).  Returns true when exactly
+// `need` keys are >= t, i.e. the top set is unique at 32 bits.  Slots
+// s >= nsl (uniform) hold no candidate.
+template <int NS>
+PISA_DEV bool bisect32(const uint32_t (&key)[NS], int nsl, int need, uint32_t &t) {
+  uint32_t lo = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = lo | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s < nsl) cnt += __builtin_popcountll(ballot64(key[s] >= c));
+    if (cnt >= need) {
+      lo = c;
+      if (cnt == need) {
+        t = lo;
+        return true;
+      }
+    }
+  }
+  t = lo;
+  return false;
+}
+
+// Fast tier: select the `need` best of fp32 scores sc (bounds dl) and certify.
+template <int NS>
+PISA_DEV bool fast_select(const float (&sc)[NS], const float (&dl)[NS], const bool (&valid)[NS], int nsl,
+                          int need, bool (&sel)[NS]) {
+  uint32_t key[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) key[s] = valid[s] ? ord32(sc[s]) : 0u;
+  uint32_t t;
+  if (!bisect32<NS>(key, nsl, need, t)) return false;
+  float t_out = -__builtin_huge_valf();
+  bool bad = false;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s >= nsl) {
+      sel[s] = false;
+      continue;
+    }
+    sel[s] = key[s] >= t;
+    const float hi = sc[s] + dl[s], lo = sc[s] - dl[s];
+    if (valid[s]) {
+      if (!sel[s]) t_out = fmaxf(t_out, hi);
+      bad |= !(__builtin_isfinite(hi) && __builtin_isfinite(lo));
+    }
+  }
+  t_out = wave_max_xl(t_out);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nsl) bad |= sel[s] && !(sc[s] - dl[s] > t_out);
+  return ballot64(bad) == 0;
+}
+
+PISA_DEV uint64_t ord64(double d) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Provisional top `need` of float64 scores: bisection over the 64 key bits,
+// keys equal at the threshold taken in slot order (= ascending block id).
+template <int NS>
+PISA_DEV void provisional64(const double (&sc)[NS], const bool (&valid)[NS], int need, bool (&sel)[NS]) {
+  const int l = lane_id();
+  uint64_t t = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t c = t | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) cnt += __builtin_popcountll(ballot64(valid[s] && ord64(sc[s]) >= c));
+    if (cnt >= need) {
+      t = c;
+      if (cnt == need) break;
+    }
+  }
+  int above = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) above += __builtin_popcountll(ballot64(valid[s] && ord64(sc[s]) > t));
+  const int rem = need - above;
+  const uint64_t lt = (1ull << l) - 1;
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint64_t k = valid[s] ? ord64(sc[s]) : 0ull;
+    const uint64_t tie = ballot64(valid[s] && k == t);
+    sel[s] = valid[s] && (k > t || (k == t && base + __builtin_popcountll(tie & lt) < rem));
+    base += __builtin_popcountll(tie);
+  }
+}
+
+// Lowest kept lower bound and highest dropped upper bound (float64); false
+// if any bound is not finite.
+template <int NS>
+PISA_DEV bool bounds64(const double (&sc)[NS], const double (&dl)[NS], const bool (&valid)[NS],
+                       const bool (&sel)[NS], double &t_in, double &t_out) {
+  double a = __builtin_huge_val(), b = -__builtin_huge_val();
+  bool bad = false;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (!valid[s]) continue;
+    const double lo = sc[s] - dl[s], hi = sc[s] + dl[s];
+    bad |= !(__builtin_isfinite(lo) && __builtin_isfinite(hi));
+    if (sel[s]) a = fmin(a, lo);
+    else b = fmax(b, hi);
+  }
+  t_in = wave_min_f64(a);
+  t_out = wave_max_f64(b);
+  return ballot64(bad) == 0;
+}
 
 // float64 score of row vector p (fp32 copy in LDS) against ksel row kr, by
 // the whole wave: exact products, a float64 tree sum; *bound receives a
@@ -439,119 +588,6 @@ PISA_DEV double rescore64(const float *p, const uint16_t *kr, double *bound) {
   }
   *bound = 16.0 * 0x1p-53 * a + 0x1p-1000;
   return s;
-}
-
-// Select the n_take best of the slot candidates (scores sc, bounds dl, ids
-// cj; slot s of lane l is candidate s * 64 + l) into sel.  Returns false if
-// the selection could not be certified even after re-scoring the undecided
-// candidates in float64 (the caller then defers the row).  p: fp32 copy of
-// the row vector in LDS; kbase: ksel rows of the KV head.
-template <int D, int NS>
-PISA_DEV bool select_scored(uint32_t *hist, double (&sc)[NS], double (&dl)[NS], const int (&cj)[NS],
-                            const bool (&valid)[NS], int n_take, bool (&sel)[NS], const float *p,
-                            const uint16_t *kbase, int32_t *diag) {
-  const int l = lane_id();
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    uint64_t key[NS];
-    uint64_t kmax = 0, kmin = ~0ull;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      key[s] = valid[s] ? (((uint64_t)ord32((float)sc[s]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)cj[s])) : 0ull;
-      if (valid[s]) {
-        kmax = key[s] > kmax ? key[s] : kmax;
-        kmin = key[s] < kmin ? key[s] : kmin;
-      }
-    }
-    kmax = wave_max_u64(kmax);
-    kmin = wave_min_u64(kmin);
-    const uint64_t diff = kmax ^ kmin;
-    int shift = diff ? ((63 - __clzll(diff)) & ~7) : 0;
-    uint64_t prefix = (shift + 8 >= 64) ? 0ull : (kmax >> (shift + 8)) << (shift + 8);
-    int need = n_take;
-    uint64_t tau = 0;
-    for (;;) {
-      for (int bb = l; bb < 256; bb += 64) hist[bb] = 0;
-      wave_lds_sync();
-      const uint64_t hi_mask = (shift + 8 >= 64) ? 0ull : ~((1ull << (shift + 8)) - 1);
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        if (valid[s] && (key[s] & hi_mask) == prefix) atomicAdd(&hist[(key[s] >> shift) & 255u], 1u);
-      wave_lds_sync();
-      int h[4];
-      int cnt = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        h[q] = (int)hist[255 - 4 * l - q];
-        cnt += h[q];
-      }
-      const int incl = wave_incl_scan(cnt);
-      const int excl = incl - cnt;
-      const bool mine = excl < need && need <= incl;
-      const uint64_t bal = ballot64(mine);
-      if (!bal) {   // unreachable for consistent counts; keeps the loop finite
-        tau = prefix;
-        break;
-      }
-      const int owner = __ffsll((unsigned long long)bal) - 1;
-      int bin = 0, above = 0, hb = 0;
-      if (mine) {
-        int run = excl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (run + h[q] >= need) {
-            bin = 255 - 4 * l - q;
-            above = run;
-            hb = h[q];
-            break;
-          }
-          run += h[q];
-        }
-      }
-      bin = __shfl(bin, owner);
-      above = __shfl(above, owner);
-      hb = __shfl(hb, owner);
-      wave_lds_sync();
-      need -= above;
-      prefix |= (uint64_t)bin << shift;
-      if (hb == need || shift == 0) {
-        tau = prefix;
-        break;
-      }
-      shift -= 8;
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) sel[s] = valid[s] && key[s] >= tau;
-    double t_in = __builtin_huge_val(), t_out = -__builtin_huge_val();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (!valid[s]) continue;
-      if (sel[s]) t_in = fmin(t_in, sc[s] - dl[s]);
-      else t_out = fmax(t_out, sc[s] + dl[s]);
-    }
-    t_in = wave_min_f64(t_in);
-    t_out = wave_max_f64(t_out);
-    if (t_in > t_out) return true;
-    if (attempt == 1) break;
-    // re-score the undecided candidates in float64 and select again
-    if (diag && l == 0) atomicAdd(&diag[1], 1);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bool amb = valid[s] && (sel[s] ? (sc[s] - dl[s] <= t_out) : (sc[s] + dl[s] >= t_in));
-      uint64_t m = ballot64(amb);
-      while (m) {
-        const int lb = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const int j = __shfl(cj[s], lb);
-        double bnd;
-        const double v = rescore64<D>(p, kbase + (size_t)j * D, &bnd);
-        if (l == lb) {
-          sc[s] = v;
-          dl[s] = bnd;
-        }
-      }
-    }
-  }
-  return false;
 }
 
 // ids of the selected slots, ascending, to LDS (uint16) and optionally to
@@ -581,14 +617,78 @@ PISA_DEV void load_vec_f32(float *dst, const uint16_t *src) {
   wave_lds_sync();
 }
 
-// select_row's inputs for one row vector, loaded by one wave
-template <int D>
-PISA_DEV void load_p_wave(Shared &sh, const uint16_t *src) {
-  for (int c = lane_id(); c < D; c += 64) {
-    const float v = bf16_to_f32(src[c]);
+// Re-score tier for one row whose fast selection was not certified.  srow:
+// fp32 scores by list position; list: block ids by position (nullptr: the
+// position is the id); nc positions; bounds cb |k_j| + 2^-110 as in the fast
+// tier; vec: the row's own vector (bf16, global), staged to pv.  On success
+// writes the row like write_sorted_lds and returns true.
+template <int D, int NS>
+__device__ __attribute__((noinline)) bool rescore_select(const float *srow, const uint16_t *list, int nc,
+                                                         int n_take, float cb, const float *skn,
+                                                         const uint16_t *vec, float *pv, const uint16_t *kbase,
+                                                         uint16_t *lout, int32_t *gout, int len, int32_t *diag) {
+  const int l = lane_id();
+  if (diag && l == 0) atomicAdd(&diag[1], 1);
+  double sc[NS], dl[NS];
+  int cj[NS];
+  bool valid[NS], sel[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int pos = s * 64 + l;
+    valid[s] = pos < nc;
+    cj[s] = valid[s] ? (list ? (int)list[pos] : pos) : 0;
+    sc[s] = valid[s] ? (double)srow[pos] : 0.0;
+    dl[s] = valid[s] ? (double)fmaf(cb, skn[cj[s]], kAbsBound) : 0.0;
+  }
+  load_vec_f32<D>(pv, vec);
+  provisional64<NS>(sc, valid, n_take, sel);
+  double t_in, t_out;
+  bounds64<NS>(sc, dl, valid, sel, t_in, t_out);
+  // undecided: kept ones not above every dropped bound and vice versa (a
+  // non-finite bound counts as undecided)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const double lo = sc[s] - dl[s], hi = sc[s] + dl[s];
+    const bool amb = valid[s] && (sel[s] ? !(lo > t_out) : !(hi < t_in));
+    uint64_t m = ballot64(amb);
+    while (m) {
+      const int lb = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int j = __builtin_amdgcn_readlane(cj[s], lb);
+      double bnd;
+      const double v = rescore64<D>(pv, kbase + (size_t)j * D, &bnd);
+      if (l == lb) {
+        sc[s] = v;
+        dl[s] = bnd;
+      }
+    }
+  }
+  provisional64<NS>(sc, valid, n_take, sel);
+  if (!bounds64<NS>(sc, dl, valid, sel, t_in, t_out) || !(t_in > t_out)) return false;
+  write_sorted_lds<NS>(sel, cj, lout, gout, len);
+  return true;
+}
+
+// Exact tier for one row: select_row over the candidates (list: block ids in
+// LDS, or nullptr for 0..nc-1), written like write_sorted_lds.
+template <int D, int NS>
+__device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_t *kbase, const uint16_t *list,
+                                                       int nc, int n_take, const uint16_t *vec, uint16_t *lout,
+                                                       int32_t *gout, int len, int32_t *diag) {
+  const int l = lane_id();
+  if (list)
+    for (int c = l; c < nc; c += 64) sh.clist[c] = list[c];
+  for (int c = l; c < D; c += 64) {
+    const float v = bf16_to_f32(vec[c]);
     sh.pf[c] = v;
     sh.p[c] = (double)v;
   }
+  wave_lds_sync();
+  bool sel[NS];
+  int cj[NS];
+  select_row<uint16_t, D, NS>(sh, kbase, list ? sh.clist : nullptr, nc, n_take, sel, cj, diag);
+  write_sorted_lds<NS>(sel, cj, lout, gout, len);
+  if (diag && l == 0) atomicAdd(&diag[2], 1);
   wave_lds_sync();
 }
 
@@ -600,6 +700,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
                                                                  int32_t *__restrict__ cand, int32_t *diag) {
   using LY = PivotLayout;
   constexpr int KS = D / 16;
+  constexpr float kG = pivot_bound<D>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -615,11 +716,10 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
   const uint16_t *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
   float *S = reinterpret_cast<float *>(lds + LY::S);
-  float *KN = reinterpret_cast<float *>(lds + LY::KN);
-  float *PN = reinterpret_cast<float *>(lds + LY::PN);
+  float *SKN = reinterpret_cast<float *>(lds + LY::SKN);
+  float *SPN = reinterpret_cast<float *>(lds + LY::SPN);
   float *PVw = reinterpret_cast<float *>(lds + LY::PV) + w * 128;
   uint16_t *LIST = reinterpret_cast<uint16_t *>(lds + LY::LIST);
-  uint32_t *histw = reinterpret_cast<uint32_t *>(lds + LY::HIST) + w * 256;
   int *defn = reinterpret_cast<int *>(lds + LY::DEFN);
   int *defp = reinterpret_cast<int *>(lds + LY::DEFP);
   int *defm = reinterpret_cast<int *>(lds + LY::DEFM);
@@ -639,7 +739,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   const int ncmax = __builtin_amdgcn_readfirstlane(wave_max_f32(pval ? (float)pnc : 0.f));
   if (tid < 4) defn[tid] = 0;
 
-  // ---- 1. proxy scores, |k|^2 and |p|^2
+  // ---- 1. proxy scores, |k| and |p|
   u32x4_t pf[KS];
   float p2 = 0.f;
 #pragma unroll
@@ -651,7 +751,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
     for (int i = 0; i < 4; ++i) p2 += bf16lo(pf[ks][i]) * bf16lo(pf[ks][i]) + bf16hi(pf[ks][i]) * bf16hi(pf[ks][i]);
   }
   p2 = pair_sum_f(p2);
-  if (w == 0 && hl == 0) PN[lq] = p2;
+  if (w == 0 && hl == 0) SPN[lq] = sqrtf(p2 + kSqFloor);
   const int ntile = (ncmax + 31) / 32;
   for (int t = w; t < ntile; t += kPW) {
     const int j = t * 32 + lq;
@@ -665,7 +765,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       for (int i = 0; i < 4; ++i) k2 += bf16lo(ka[ks][i]) * bf16lo(ka[ks][i]) + bf16hi(ka[ks][i]) * bf16hi(ka[ks][i]);
     }
     k2 = pair_sum_f(k2);
-    if (hl == 0 && j < kPNc) KN[j] = k2;
+    if (hl == 0 && j < kPNc) SKN[j] = sqrtf(k2 + kSqFloor);
     f32x16_t acc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], pf[ks], acc);
@@ -679,61 +779,68 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   }
   __syncthreads();
 
-  constexpr double kG32 = D * 0x1p-22;   // fp32 accumulation bound factor (doubled)
   // ---- 2. proxy top-C
-  for (int pl = w; pl < kPX; pl += kPW) {
-    int h, gm, nc;
-    if (!proxy(pl, h, gm, nc)) continue;
-    const int C = min(dm.n_cand, nc);
-    int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
-    uint16_t *lout = LIST + pl * kPCap;
-    if (diag && l == 0) atomicAdd(&diag[0], 1);
-    if (C >= nc) {   // every candidate
-      for (int c = l; c < nc; c += 64) lout[c] = (uint16_t)c;
-      if (gout)
-        for (int c = l; c < dm.n_cand; c += 64) gout[c] = c < nc ? c : -1;
-      continue;
-    }
-    load_vec_f32<D>(PVw, qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D);
-    const float pn = PN[pl];
-    double sc[kMaxSlots], dl[kMaxSlots];
-    int cj[kMaxSlots];
-    bool valid[kMaxSlots], sel[kMaxSlots];
+  {
+    constexpr int NS = kMaxSlots;
+    float skr[NS];   // |ksel_c| of this lane's slots, shared by every proxy
+    int cid[NS];
 #pragma unroll
-    for (int s = 0; s < kMaxSlots; ++s) {
-      const int c = s * 64 + l;
-      valid[s] = c < nc;
-      cj[s] = c;
-      sc[s] = valid[s] ? (double)S[pl * LY::SLD + c] : 0.0;
-      dl[s] = valid[s] ? kG32 * sqrt((double)pn * (double)KN[c]) + 0x1p-1000 : 0.0;
+    for (int s = 0; s < NS; ++s) {
+      cid[s] = s * 64 + l;
+      skr[s] = cid[s] < ncmax ? SKN[cid[s]] : 0.f;
     }
-    if (select_scored<D, kMaxSlots>(histw, sc, dl, cj, valid, C, sel, PVw, kbase, diag))
-      write_sorted_lds<kMaxSlots>(sel, cj, lout, gout, dm.n_cand);
-    else if (l == 0)
-      defp[atomicAdd(&defn[0], 1)] = pl;
+    for (int pl = w; pl < kPX; pl += kPW) {
+      int h, gm, nc;
+      if (!proxy(pl, h, gm, nc)) continue;
+      const int C = min(dm.n_cand, nc);
+      int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
+      uint16_t *lout = LIST + pl * kPCap;
+      if (diag && l == 0) atomicAdd(&diag[0], 1);
+      if (C >= nc) {   // every candidate
+        for (int c = l; c < nc; c += 64) lout[c] = (uint16_t)c;
+        if (gout)
+          for (int c = l; c < dm.n_cand; c += 64) gout[c] = c < nc ? c : -1;
+        continue;
+      }
+      const float cb = kG * SPN[pl];
+      const int nsl = (nc + 63) / 64;
+      float sc[NS], dl[NS];
+      bool valid[NS], sel[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        valid[s] = cid[s] < nc;
+        sc[s] = (s < nsl && valid[s]) ? S[pl * LY::SLD + cid[s]] : 0.f;
+        dl[s] = fmaf(cb, skr[s], kAbsBound);
+      }
+      if (fast_select<NS>(sc, dl, valid, nsl, C, sel)) {
+        write_sorted_lds<NS>(sel, cid, lout, gout, dm.n_cand);
+      } else {
+        const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
+        if (!rescore_select<D, NS>(S + pl * LY::SLD, nullptr, nc, C, cb, SKN, vec, PVw, kbase, lout, gout,
+                                   dm.n_cand, diag) &&
+            l == 0)
+          defp[atomicAdd(&defn[0], 1)] = pl;
+      }
+    }
   }
   __syncthreads();
-  if (w == 0) {   // undecided proxies: select_row's exact path
+  if (w == 0) {   // undecided proxies: the exact tier
     const int nd = defn[0];
     for (int q = 0; q < nd; ++q) {
       const int pl = defp[q];
       int h, gm, nc;
       proxy(pl, h, gm, nc);
       const int C = min(dm.n_cand, nc);
-      load_p_wave<D>(sh, qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D);
-      bool sel[kMaxSlots];
-      int cj[kMaxSlots];
-      select_row<uint16_t, D, kMaxSlots>(sh, kbase, nullptr, nc, C, sel, cj, diag);
       int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
-      write_sorted_lds<kMaxSlots>(sel, cj, LIST + pl * kPCap, gout, dm.n_cand);
-      if (diag && l == 0) atomicAdd(&diag[2], 1);
+      exact_select<D, kMaxSlots>(sh, kbase, nullptr, nc, C, qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D,
+                                 LIST + pl * kPCap, gout, dm.n_cand, diag);
     }
   }
   __syncthreads();
   if (dm.topk == 0) return;
 
   // ---- 3. members: top-k of the proxy's list
-  float *Mw = S + w * kPG * LY::MLD;
+  float *Mw = S + w * kPM * LY::MLD;
   for (int pl = w; pl < kPX; pl += kPW) {
     int h, gm, nc;
     if (!proxy(pl, h, gm, nc)) continue;
@@ -750,63 +857,79 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       }
       continue;
     }
-    // member queries as B (lane lq = member), scores of the list rows as A
-    const bool mval = lq < t1 - t0;
-    u32x4_t mq[KS];
-    float q2 = 0.f;
+    constexpr int NS = kPCap / 64;
+    int cj[NS];
+    float skm[NS];
+    bool valid[NS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      mq[ks] = mval ? *reinterpret_cast<const u32x4_t *>(Q + (qrow0 + t0 + lq) * D + 16 * ks + 8 * hl)
-                    : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q2 += bf16lo(mq[ks][i]) * bf16lo(mq[ks][i]) + bf16hi(mq[ks][i]) * bf16hi(mq[ks][i]);
+    for (int s = 0; s < NS; ++s) {
+      const int pos = s * 64 + l;
+      valid[s] = pos < C;
+      cj[s] = valid[s] ? (int)list[pos] : 0;
+      skm[s] = SKN[cj[s]];
     }
-    q2 = pair_sum_f(q2);
+    const int nsl = (C + 63) / 64;
     const int nct = (C + 31) / 32;
-    for (int ct = 0; ct < nct; ++ct) {
-      const int pos = ct * 32 + lq;
-      const int j = list[pos < C ? pos : 0];
-      u32x4_t ka[KS];
+    for (int m0 = t0; m0 < t1; m0 += kPM) {
+      const int nm = min(kPM, t1 - m0);
+      // member queries as B (lane lq = member), the gathered list rows as A
+      const bool mval = lq < nm;
+      u32x4_t mq[KS];
+      float q2 = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)j * D + 16 * ks + 8 * hl);
-      f32x16_t acc = f32x16_t{};
+      for (int ks = 0; ks < KS; ++ks) {
+        mq[ks] = mval ? *reinterpret_cast<const u32x4_t *>(Q + (qrow0 + m0 + lq) * D + 16 * ks + 8 * hl)
+                      : u32x4_t{0, 0, 0, 0};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], mq[ks], acc);
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int p0 = ct * 32 + 8 * g4 + 4 * hl;
-        if (mval)
-          *reinterpret_cast<f32x4_t *>(Mw + lq * LY::MLD + p0) =
-              f32x4_t{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+        for (int i = 0; i < 4; ++i)
+          q2 += bf16lo(mq[ks][i]) * bf16lo(mq[ks][i]) + bf16hi(mq[ks][i]) * bf16hi(mq[ks][i]);
       }
-    }
-    wave_lds_sync();
-    for (int m = 0; m < t1 - t0; ++m) {
-      const int t = t0 + m;
-      const float qn = __shfl(q2, m);
-      if (diag && l == 0) atomicAdd(&diag[0], 1);
-      load_vec_f32<D>(PVw, Q + (qrow0 + t) * D);
-      constexpr int NS = kPCap / 64;
-      double sc[NS], dl[NS];
-      int cj[NS];
-      bool valid[NS], sel[NS];
+      q2 = pair_sum_f(q2);
+      const float qn = sqrtf(q2 + kSqFloor);
+      for (int ct = 0; ct < nct; ++ct) {
+        const int pos = ct * 32 + lq;
+        const int j = list[pos < C ? pos : 0];
+        u32x4_t ka[KS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int pos = s * 64 + l;
-        valid[s] = pos < C;
-        cj[s] = valid[s] ? (int)list[pos] : 0;
-        sc[s] = valid[s] ? (double)Mw[m * LY::MLD + pos] : 0.0;
-        dl[s] = valid[s] ? kG32 * sqrt((double)qn * (double)KN[cj[s]]) + 0x1p-1000 : 0.0;
+        for (int ks = 0; ks < KS; ++ks)
+          ka[ks] = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)j * D + 16 * ks + 8 * hl);
+        f32x16_t acc = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], mq[ks], acc);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int p0 = ct * 32 + 8 * g4 + 4 * hl;
+          if (mval)
+            *reinterpret_cast<f32x4_t *>(Mw + lq * LY::MLD + p0) =
+                f32x4_t{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+        }
       }
-      if (select_scored<D, NS>(histw, sc, dl, cj, valid, n_take, sel, PVw, kbase, diag))
-        write_sorted_lds<NS>(sel, cj, nullptr, idx + (qrow0 + t) * dm.topk, dm.topk);
-      else if (l == 0)
-        defm[atomicAdd(&defn[1], 1)] = t * 64 + pl;
+      wave_lds_sync();
+      for (int m = 0; m < nm; ++m) {
+        const int t = m0 + m;
+        if (diag && l == 0) atomicAdd(&diag[0], 1);
+        const float cb = kG * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qn), m));
+        float sc[NS], dl[NS];
+        bool sel[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          sc[s] = valid[s] ? Mw[m * LY::MLD + s * 64 + l] : 0.f;
+          dl[s] = fmaf(cb, skm[s], kAbsBound);
+        }
+        int32_t *out = idx + (qrow0 + t) * dm.topk;
+        if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel)) {
+          write_sorted_lds<NS>(sel, cj, nullptr, out, dm.topk);
+        } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, C, n_take, cb, SKN, Q + (qrow0 + t) * D, PVw,
+                                          kbase, nullptr, out, dm.topk, diag) &&
+                   l == 0) {
+          defm[atomicAdd(&defn[1], 1)] = t * 64 + pl;
+        }
+      }
+      wave_lds_sync();
     }
   }
   __syncthreads();
-  if (w == 0) {   // undecided members: select_row's exact path over the proxy's list
+  if (w == 0) {   // undecided members: the exact tier over the proxy's list
     const int nd = defn[1];
     for (int q = 0; q < nd; ++q) {
       const int t = defm[q] >> 6, pl = defm[q] & 63;
@@ -814,15 +937,9 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       proxy(pl, h, gm, nc);
       const int C = min(dm.n_cand, nc);
       const int n_take = min(dm.topk, C);
-      for (int c = l; c < C; c += 64) sh.clist[c] = LIST[pl * kPCap + c];
-      load_p_wave<D>(sh, Q + ((size_t)(b * dm.Hq + h) * dm.L + t) * D);
-      bool sel[kPCap / 64];
-      int cj[kPCap / 64];
-      select_row<uint16_t, D, kPCap / 64>(sh, kbase, sh.clist, C, n_take, sel, cj, diag);
-      write_sorted_lds<kPCap / 64>(sel, cj, nullptr, idx + ((size_t)(b * dm.Hq + h) * dm.L + t) * dm.topk,
-                                   dm.topk);
-      if (diag && l == 0) atomicAdd(&diag[2], 1);
-      wave_lds_sync();
+      const size_t row = (size_t)(b * dm.Hq + h) * dm.L + t;
+      exact_select<D, kPCap / 64>(sh, kbase, LIST + pl * kPCap, C, n_take, Q + row * D, nullptr,
+                                  idx + row * dm.topk, dm.topk, diag);
     }
   }
 }
