@@ -9,7 +9,9 @@ rational score (ties to the lower block index).
 Definition followed: the PISA page, technical summary section 2 (N_t / D_t
 with exact terms over selected blocks and, for non-selected blocks,
 alpha_{t,j} = exp(q_t . kbar_j) times the block value sum plus the first-order
-term, alpha * n_j in the denominator); the PIVOT page's steps 1-4 (proxy =
+term, alpha * n_j in the denominator; the hybrid order's global first-order
+correction q_t Hbar sum_j alpha_{t,j} with Hbar the mean of the per-block
+matrices over all blocks); the PIVOT page's steps 1-4 (proxy =
 mean of g consecutive queries, candidates re-ranked per member); the Sliding
 Window Attention page's causal mask 0 <= t - s < w.
 """
@@ -72,6 +74,8 @@ def run(q, k, v, P):
                 sg.append([sum(v[b][hk][s][e] for s in blocks[j]) for e in range(d)])
                 Hm.append([[sum((k[b][hk][s][c] - mean[c]) * v[b][hk][s][e] for s in blocks[j])
                             for e in range(d)] for c in range(d)])
+
+            Hbar = [[sum(Hm[j][c][e] for j in range(nb)) / nb for e in range(d)] for c in range(d)]
 
             def geometry(start):
                 own = start // bs
@@ -137,6 +141,10 @@ def run(q, k, v, P):
                 m = max(x for x, _, _ in terms)
                 D = sum(math.exp(x - m) * w for x, w, _ in terms)
                 N = [sum(math.exp(x - m) * vec[e] for x, _, vec in terms) for e in range(d)]
+                if P.taylor == "hybrid" and U:
+                    asum = sum(math.exp(sc * sum(qt[c] * kb[j][c] for c in range(d)) - m) for j in U)
+                    for e in range(d):
+                        N[e] += asum * sc * sum(qt[c] * Hbar[c][e] for c in range(d))
                 res_O[(b, h, t)] = [N[e] / D for e in range(d)]
                 res_lse[(b, h, t)] = m + math.log(D)
     return dict(idx=res_idx, O=res_O, lse=res_lse)

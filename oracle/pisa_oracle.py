@@ -28,6 +28,9 @@ The definition implemented (notation of the PISA page):
     non-kept candidate block, alpha = exp(scale q_t . kbar_j) times
     (sigma_j + scale q_t H_j) in N_t and alpha * n_j in D_t (first order per
     block; order 0 drops the H term; "none" drops the block).
+  * Hybrid order ([PISA] section 2, the global first-order correction): zero
+    order per non-kept block plus scale q_t Hbar sum_{j in U} alpha_{t,j} in
+    N_t, Hbar = the mean of H_j over all blocks of the (batch, KV head).
 Readings of points the pages leave open are listed in the design notes and
 repeated at the functions that take them.
 """
@@ -39,7 +42,7 @@ from fractions import Fraction
 
 import numpy as np
 
-TAYLOR_MODES = ("none", "order0", "order1")
+TAYLOR_MODES = ("none", "order0", "order1", "hybrid")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -151,7 +154,10 @@ def pooled_mean(x: np.ndarray, axis: int, dtype: str) -> np.ndarray:
 def block_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: Problem) -> dict:
     """Per KV block: n_j, kbar_j (float64 mean), ksel_j = RNE_dtype(kbar_j),
     sigma_j = sum v, H_j = sum_n (k_n - kbar_j)^T v_n with H_j[c, e] indexed
-    (key channel c, value channel e).  Per query selection row: qsel =
+    (key channel c, value channel e), and Hbar = mean_j H_j over all n_blk
+    blocks ([PISA] section 2, the global statistic of the hybrid order; the
+    pages average over all blocks, read here as every block of the sequence,
+    each with weight 1 / n_blk, also when the rows are causal).  Per query selection row: qsel =
     RNE_dtype(mean of the rows of query block i), or in PIVOT mode the proxy
     RNE_dtype(mean of queries g*gamma .. g*gamma+g-1) (a last partial group
     averages its actual members)."""
@@ -175,7 +181,8 @@ def block_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: Problem) -> dict
     for r in range(ns):
         qsel[:, :, r] = pooled_mean(q[:, :, r * span:min(L, (r + 1) * span), :], 2, P.dtype)
     qsel = rne(qsel, P.dtype)
-    return dict(n=n, kbar=kbar, ksel=ksel, vsum=vsum, H=H, qsel=qsel)
+    Hbar = H.mean(axis=2)
+    return dict(n=n, kbar=kbar, ksel=ksel, vsum=vsum, H=H, Hbar=Hbar, qsel=qsel)
 
 
 # ----------------------------------------------------------------------------
@@ -304,6 +311,7 @@ def attend_tokens(q, k, v, st, idx, P: Problem, b: int, h: int, tokens) -> tuple
                                                          a_j = scale q.kbar_j
       D_t = sum_E e^{x-m} + sum_U e^{a-m} n_j
       N_t = sum_E e^{x-m} v_s + sum_U e^{a-m} (sigma_j + [order1] scale q H_j)
+            + [hybrid] scale (q Hbar) sum_U e^{a-m}
       o_t = N_t / D_t,  lse_t = m + ln D_t
     E_t: tokens of kept blocks (s <= t when causal); U_t: Taylor blocks."""
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -333,6 +341,8 @@ def attend_tokens(q, k, v, st, idx, P: Problem, b: int, h: int, tokens) -> tuple
         if P.taylor == "order1" and len(Uj):
             qH = np.einsum("nc,jce->nje", qt, st["H"][b, hk, Uj])
             N = N + sc * np.einsum("nj,nje->ne", pa, qH)
+        if P.taylor == "hybrid" and len(Uj):
+            N = N + sc * (qt @ st["Hbar"][b, hk]) * pa.sum(axis=1)[:, None]
         out[sel] = N / D[:, None]
         lse[sel] = m + np.log(D)
     return out, lse

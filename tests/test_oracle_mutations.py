@@ -138,8 +138,25 @@ def check_pivot_mean(m):
     return r["idx"][0, 0, 56].tolist() == [3] and r["idx"][0, 0, 57].tolist() == [3]
 
 
+def check_hybrid(m):
+    """Hbar by the uncentred identity, and the hybrid output as the order-1
+    output averaged over cyclic relabelings of the blocks' H."""
+    B, H, L, d, bs = 1, 2, 70, 8, 10
+    q, k, v = _rand((B, H, L, d), 16), _rand((B, H, L, d), 17, scale=2.0) + 1.0, _rand((B, H, L, d), 18)
+    kw = dict(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=bs, topk=2, causal=True, window=15)
+    Ph, P1 = m.Problem(taylor="hybrid", **kw), m.Problem(taylor="order1", **kw)
+    st = m.block_stats(q, k, v, Ph)
+    raw = np.einsum("bhsc,bhse->bhce", k, v) - np.einsum("bhjc,bhje->bhce", st["kbar"], st["vsum"])
+    ok = np.abs(st["Hbar"] - raw / Ph.n_blk).max() < 1e-11
+    idx, _ = m.select(q, st, Ph)
+    oh, _ = m.attention(q, k, v, st, idx, Ph)
+    acc = sum(m.attention(q, k, v, dict(st, H=np.roll(st["H"], s, axis=2)), idx, P1)[0]
+              for s in range(Ph.n_blk)) / Ph.n_blk
+    return ok and np.abs(oh - acc).max() < 1e-12
+
+
 CHECKS = [check_pivot_mean, check_swa_count, check_dense, check_constant_v, check_orders, check_ties,
-          check_pivot_reuse, check_pooled_selection]
+          check_pivot_reuse, check_pooled_selection, check_hybrid]
 
 MUTATIONS = {
     "H transposed": ('H[:, :, j] = np.einsum("bhnc,bhne->bhce", kc, vj)',
@@ -161,6 +178,12 @@ MUTATIONS = {
                               "qsel[:, :, r] = q[:, :, r * span, :]"),
     "pivot members ignore proxy list": ("tt = top_n(q[b, h, t], Kb[cl], cl, k)",
                                         "tt = top_n(q[b, h, t], Kb[:nc], np.arange(nc), k)"),
+    "hybrid Hbar is the sum": ("Hbar = H.mean(axis=2)", "Hbar = H.sum(axis=2)"),
+    "hybrid Hbar over the tail only": ('(qt @ st["Hbar"][b, hk])', '(qt @ st["H"][b, hk, Uj].mean(axis=0))'),
+    "hybrid Hbar transposed": ('(qt @ st["Hbar"][b, hk])', '(qt @ st["Hbar"][b, hk].T)'),
+    "hybrid term without scale": ('N = N + sc * (qt @ st["Hbar"]', 'N = N + 1.0 * (qt @ st["Hbar"]'),
+    "hybrid weights include exact terms": ('* pa.sum(axis=1)[:, None]',
+                                           '* (pa.sum(axis=1) + px.sum(axis=1))[:, None]'),
     "scale not applied to exact logits": ("x = sc * (qt @ k[b, hk, keys].T)", "x = (qt @ k[b, hk, keys].T)"),
 }
 

@@ -156,7 +156,7 @@ def test_p3_topk_all_is_dense(causal, Hq, Hkv, L, bs, taylor):
 # ---------------------------------------------------------------------------
 # P4: Taylor term exact when all keys of a block coincide
 
-@pytest.mark.parametrize("taylor", ["order0", "order1"])
+@pytest.mark.parametrize("taylor", ["order0", "order1", "hybrid"])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 20)])
 def test_p4_identical_keys_exact(taylor, causal, window):
     B, H, L, d, bs = 1, 2, 96, 8, 8
@@ -199,7 +199,7 @@ def test_p5_convergence_orders():
 # ---------------------------------------------------------------------------
 # P6: block size 1 makes every Taylor mode exact, for any k
 
-@pytest.mark.parametrize("taylor,k", [("order0", 0), ("order1", 3), ("order1", 0)])
+@pytest.mark.parametrize("taylor,k", [("order0", 0), ("order1", 3), ("order1", 0), ("hybrid", 2)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_p6_block_size_one(taylor, k, causal):
     B, H, L, d = 1, 2, 40, 8
@@ -212,7 +212,7 @@ def test_p6_block_size_one(taylor, k, causal):
 # ---------------------------------------------------------------------------
 # P7: normalisation consistency (terms inside both N and D)
 
-@pytest.mark.parametrize("taylor", ["none", "order0", "order1"])
+@pytest.mark.parametrize("taylor", ["none", "order0", "order1", "hybrid"])
 def test_p7_constant_values(taylor):
     B, Hq, Hkv, L, d, bs = 1, 4, 2, 130, 16, 16
     q, k = _rand((B, Hq, L, d), 41, "bf16"), _rand((B, Hkv, L, d), 42, "bf16")
@@ -230,8 +230,8 @@ def test_p7_constant_values(taylor):
 # ---------------------------------------------------------------------------
 # P8: a common shift of all keys changes neither selections nor outputs
 
-@pytest.mark.parametrize("pivot", [False, True])
-def test_p8_key_shift_invariance(pivot):
+@pytest.mark.parametrize("pivot,taylor", [(False, "order1"), (True, "order1"), (False, "hybrid")])
+def test_p8_key_shift_invariance(pivot, taylor):
     B, Hq, Hkv, L, d, bs = 1, 2, 1, 128, 8, 16
     rng = np.random.default_rng(51)
     # dyadic values so that means and shifts stay exact in float32
@@ -240,7 +240,7 @@ def test_p8_key_shift_invariance(pivot):
     v = rng.integers(-64, 64, (B, Hkv, L, d)) / 32.0
     c = rng.integers(-64, 64, d) / 16.0
     kw = dict(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, dtype="f32", block=bs, topk=2, causal=True,
-              window=20, taylor="order1")
+              window=20, taylor=taylor)
     if pivot:
         kw.update(group=4, n_cand=4)
     P = po.Problem(**kw)
@@ -316,6 +316,10 @@ BRUTE_CASES = [
          dtype="f32"),
     dict(Hq=1, Hkv=1, L=29, block=4, topk=1, group=4, n_cand=2, causal=True, window=9,
          taylor="order1", dtype="f32"),
+    dict(Hq=2, Hkv=1, L=38, block=8, topk=1, causal=False, taylor="hybrid", dtype="bf16"),
+    dict(Hq=2, Hkv=2, L=45, block=8, topk=2, causal=True, window=12, taylor="hybrid", dtype="f32"),
+    dict(Hq=2, Hkv=1, L=40, block=8, topk=2, group=4, n_cand=3, causal=True, taylor="hybrid",
+         dtype="bf16"),
 ]
 
 
@@ -394,6 +398,52 @@ def test_p11_first_order_algebra():
             np.testing.assert_allclose(blockwise, tokenwise, atol=1e-12)
             # the first-order denominator term vanishes: sum_n q.(k_n - kbar) = 0
             assert abs(sum(qs @ (kj[n] - st["kbar"][0, 0, j]) for n in range(bs))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P12: the hybrid order is the order-1 output averaged over relabelings of H.
+# N_t is affine in the per-block matrices H_j and D_t does not depend on them,
+# so replacing every H_j by the mean over the n_blk cyclic shifts H_{(j+s) mod
+# n_blk} (which is Hbar for every j) averages the order-1 outputs of the
+# shifted statistics.  Pins the hybrid term's placement, scale, sign,
+# orientation and the set it averages over (all blocks, not the tail).
+
+@pytest.mark.parametrize("causal,window,group", [(False, 0, 0), (True, 20, 0), (True, 0, 4)])
+def test_p12_hybrid_is_mean_over_relabelled_order1(causal, window, group):
+    B, Hq, Hkv, L, d, bs = 1, 2, 1, 86, 8, 12
+    q, k, v = _rand((B, Hq, L, d), 111), _rand((B, Hkv, L, d), 112), _rand((B, Hkv, L, d), 113)
+    kw = dict(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, dtype="f32", block=bs, topk=2, causal=causal,
+              window=window, group=group, n_cand=3 if group else 0)
+    Ph = po.Problem(taylor="hybrid", **kw)
+    P1 = po.Problem(taylor="order1", **kw)
+    st = po.block_stats(q, k, v, Ph)
+    idx, _ = po.select(q, st, Ph)
+    oh, lh = po.attention(q, k, v, st, idx, Ph)
+    nb = Ph.n_blk
+    acc = np.zeros_like(oh)
+    for s in range(nb):
+        o1, l1 = po.attention(q, k, v, dict(st, H=np.roll(st["H"], s, axis=2)), idx, P1)
+        acc += o1 / nb
+        np.testing.assert_allclose(l1, lh, atol=1e-12)     # the denominator ignores H
+    np.testing.assert_allclose(oh, acc, atol=1e-12)
+    o1, _ = po.attention(q, k, v, st, idx, P1)
+    assert np.abs(oh - o1).max() > 1e-3                      # the blocks' H_j differ here
+
+
+# ---------------------------------------------------------------------------
+# P13: Hbar by the uncentred identity
+#   sum_j H_j = sum_s k_s^T v_s - sum_j kbar_j^T sigma_j
+# (the centring of H_j expanded), computed from the raw tokens.
+
+def test_p13_hbar_uncentred_identity():
+    B, Hkv, L, d, bs = 2, 2, 70, 8, 16
+    q = _rand((B, Hkv, L, d), 121)
+    k, v = _rand((B, Hkv, L, d), 122, scale=3.0) + 2.0, _rand((B, Hkv, L, d), 123)
+    P = po.Problem(B=B, Hq=Hkv, Hkv=Hkv, L=L, d=d, dtype="f32", block=bs, topk=1, taylor="hybrid")
+    st = po.block_stats(q, k, v, P)
+    raw = np.einsum("bhsc,bhse->bhce", k, v)
+    corr = np.einsum("bhjc,bhje->bhce", st["kbar"], st["vsum"])
+    np.testing.assert_allclose(st["Hbar"], (raw - corr) / P.n_blk, rtol=0, atol=1e-11)
 
 
 # ---------------------------------------------------------------------------
