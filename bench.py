@@ -34,7 +34,8 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
     from the selections actually made (idx: [B, Hq, n_rows, k], -1 padded).
       exact pairs  (t, s), s in a kept block (s <= t when causal): 4 d FLOPs
       Taylor pairs (t, j), j a non-kept candidate block: 4 d (logit + zero
-      order) + 2 d^2 (first order) FLOPs
+      order) + 2 d^2 (first order) FLOPs; the hybrid order instead adds
+      2 d^2 once per row that has a Taylor block (q Hbar)
       dense-equivalent: 4 d per (t, s) pair of full (causal) attention."""
     B, Hq, Hkv, L, d, bs = (knobs[k] for k in ("B", "Hq", "Hkv", "L", "d", "block"))
     causal, window, group, taylor = knobs["causal"], knobs["window"], knobs["group"], knobs["taylor"]
@@ -42,6 +43,7 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
     nj = np.minimum(bs, L - bs * np.arange(n_blk)).astype(np.int64)
     exact = 0
     taylor_pairs = 0
+    taylor_rows = 0
     pivot = group >= 1
     n_rows = idx.shape[2]
     for r in range(n_rows):
@@ -66,9 +68,11 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
             exact += int(kept_keys.sum()) * len(tokens)
         if taylor != "none":
             taylor_pairs += int((nc - n_kept).sum()) * len(tokens)
+            taylor_rows += int((nc - n_kept > 0).sum()) * len(tokens)
     flop_exact = 4 * d * exact
     flop_t0 = 4 * d * taylor_pairs if taylor != "none" else 0
-    flop_t1 = 2 * d * d * taylor_pairs if taylor == "order1" else 0
+    flop_t1 = (2 * d * d * taylor_pairs if taylor == "order1"
+               else 2 * d * d * taylor_rows if taylor == "hybrid" else 0)
     dense_pairs = (L * (L + 1) // 2) if causal else L * L
     dense = 4 * d * dense_pairs * B * Hq
     es = 2 if knobs["dtype"] == "bf16" else 4
@@ -79,6 +83,8 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
         stats_out += 2 * B * Hkv * n_blk * d * 4
     if taylor == "order1":
         stats_out += B * Hkv * n_blk * d * d * es
+    if taylor == "hybrid":
+        stats_out += B * Hkv * d * d * es
     return {k: int(v) for k, v in dict(flop_exact=flop_exact, flop_taylor0=flop_t0, flop_taylor1=flop_t1,
                                         flop_attn=flop_exact + flop_t0 + flop_t1, flop_dense=dense,
                                         stats_bytes=qkv + stats_out, exact_pairs=exact,
@@ -148,6 +154,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_dit")
+    ap.add_argument("--taylor", default=None, choices=["none", "order0", "order1", "hybrid"],
+                    help="run the workload with another treatment of the non-kept blocks "
+                         "(reported as workload <name>_<mode>)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -175,6 +184,8 @@ def main():
     from piecewise_attention_dit_amd import workloads as W
 
     wl = W.WORKLOADS[args.workload]
+    if args.taylor and args.taylor != wl.taylor:
+        wl = wl.replace(name=f"{wl.name}_{args.taylor}", taylor=args.taylor)
     knobs = wl.knobs()
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
     q, k, v = W.make_inputs(wl)

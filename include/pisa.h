@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PISA_ABI_VERSION 1
+#define PISA_ABI_VERSION 2
 
 typedef enum {
   PISA_OK = 0,
@@ -72,7 +72,11 @@ typedef enum { PISA_BF16 = 0, PISA_F32 = 1 } pisa_dtype;
 typedef enum {
   PISA_TAYLOR_NONE = 0,    /* drop them (keep-or-drop block sparsity) */
   PISA_TAYLOR_ORDER0 = 1,  /* exp(q.kbar_j) * sum_n v_n ; exp(q.kbar_j) * n_j */
-  PISA_TAYLOR_ORDER1 = 2   /* adds exp(q.kbar_j) * q H_j to the numerator */
+  PISA_TAYLOR_ORDER1 = 2,  /* adds exp(q.kbar_j) * q H_j to the numerator */
+  PISA_TAYLOR_HYBRID = 3   /* zero order per block, plus one global first-order
+                              term q Hbar * sum_j exp(q.kbar_j) in the numerator,
+                              Hbar = mean of H_j over all blocks of the (b, kv
+                              head) ([PISA] section 2, hybrid order) */
 } pisa_taylor;
 
 /* Problem statement.  Supported today: d in {64, 128}; block in {64, 128};
@@ -103,10 +107,14 @@ typedef struct {
  *   ksel  dtype [B, Hkv, n_blk, d]: RNE_dtype(float64 mean key of block j)
  *   kbar  fp32 [B, Hkv, n_blk, d]: the mean key, rounded to fp32 (Taylor term)
  *   vsum  fp32 [B, Hkv, n_blk, d]: sum of the block's value rows
- *   HT    [B, Hkv, n_blk, d, d], bf16 for bf16 inputs and fp32 for fp32
- *         inputs: the transposed first-order matrix,
- *         HT[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c)
- * kbar, vsum and HT are read only when taylor != NONE and may be NULL then. */
+ *   HT    bf16 for bf16 inputs and fp32 for fp32 inputs.  ORDER1:
+ *         [B, Hkv, n_blk, d, d], the transposed first-order matrix,
+ *         HT[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c).  HYBRID: [B, Hkv, d, d],
+ *         the transposed mean of those matrices over the n_blk blocks of the
+ *         (b, kv head) (every block, also for causal rows).  Not used by the
+ *         other modes.
+ * kbar and vsum are read only when taylor != NONE, HT only for ORDER1 and
+ * HYBRID; they may be NULL otherwise. */
 typedef struct {
   void *qsel;
   void *ksel;
@@ -130,17 +138,24 @@ pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]);
 pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]);
 
 /* Workspace bytes call `op` needs (0 = block_stats, 1 = indexer_topk,
- * 2 = sparse_attn_fwd).  All three need none today; a non-NULL workspace of
- * at least PISA_DIAG_BYTES passed to pisa_indexer_topk receives diagnostic
- * counters (int32: rows, rows decided by exact rational re-scoring,
- * candidates re-scored exactly). */
+ * 2 = sparse_attn_fwd).  block_stats needs one for the HYBRID order with bf16
+ * inputs (fp32 partial sums of the mean first-order matrix, 16-byte aligned,
+ * contents need not be initialised and are garbage afterwards); every other
+ * call and mode needs none.  A non-NULL workspace of at least
+ * PISA_DIAG_BYTES passed to pisa_indexer_topk receives diagnostic counters
+ * (int32: rows selected, rows whose fast selection was not certified and went
+ * to a float64 re-score or an exact comparison, rows or candidates decided by
+ * exact comparison).  The counters are updated with atomics on one address
+ * and slow the call down; they are for diagnosis, not for timed runs. */
 #define PISA_DIAG_BYTES 64
 pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes);
 
 /* ---- the hot path ------------------------------------------------------- */
 
 /* Stage A.  Reads Q, K, V; writes every non-NULL statistics buffer of *out
- * (qsel and ksel are required; kbar, vsum, HT when taylor != NONE). */
+ * (qsel and ksel are required; kbar and vsum when taylor != NONE, HT for
+ * ORDER1 and HYBRID).  ws: at least pisa_workspace_size(p, 0) bytes, else
+ * PISA_E_WORKSPACE. */
 pisa_status pisa_block_stats(const pisa_params *p, const void *Q, const void *K,
                              const void *V, const pisa_stats *out, void *ws,
                              size_t ws_bytes, hipStream_t stream);
@@ -166,6 +181,7 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
  *   U_t = candidates of r not in T_r (empty when taylor == NONE)
  *   N_t = sum_{s in E_t} e^{q_s.k_s} v_s
  *       + sum_{j in U_t} e^{q_s.kbar_j} (vsum_j + [ORDER1] q_s H_j)
+ *       + [HYBRID] (q_s Hbar) sum_{j in U_t} e^{q_s.kbar_j}
  *   D_t = sum_{s in E_t} e^{q_s.k_s} + sum_{j in U_t} e^{q_s.kbar_j} n_j
  *   O_t = N_t / D_t rounded to nearest-even in dtype;
  *   lse_t = max-shifted ln D_t (fp32 [B, Hq, L]) if lse != NULL.

@@ -407,7 +407,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
     uint8_t *sth = lds + LY::TY_STH, *stl = lds + LY::TY_STL;
     uint16_t *alpha = reinterpret_cast<uint16_t *>(lds + LY::TY_ALPHA) + w * kTyBatch * NQ * 32;
     float *nj = reinterpret_cast<float *>(lds + LY::TY_NJ);
-    const bool order1 = taylor == 2;
+    const bool order1 = taylor == 2, hybrid = taylor == 3;
+    float a_run[NQ];   // hybrid: sum of the rows' Taylor weights, on the scale of d_run
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) a_run[n] = 0.f;
     Cursor cur[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) cursor_init(cur[n], list[n], valid[n] && pivot ? topk : 0);
@@ -415,6 +418,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < NQ; ++n) tmask[n] = 0;
     if (order1) dma_tile<D, D, 0, NW>(HTh + (size_t)tyl[0] * D * D, D, lds + LY::TY_H, w, l);
+    else if (hybrid)   // the mean matrix Hbar^T of this kv head
+      dma_tile<D, D, 0, NW>(static_cast<const uint16_t *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D, D,
+                            lds + LY::TY_H, w, l);
     for (int eg = 0; eg < n_ty; ++eg) {
       const int e = eg & (kTyBatch - 1);
       if (e == 0) {
@@ -508,21 +514,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
             if (ballot64(grow)) {
               const float corr = grow ? fast_exp2(m_run[n] - mloc) : 1.f;
               d_run[n] *= corr;
+              a_run[n] *= corr;
 #pragma unroll
               for (int et = 0; et < NE; ++et) oacc[n][et] *= corr;
               m_run[n] = grow ? mloc : m_run[n];
             }
             const float mref = m_run[n] == kNegInf ? 0.f : m_run[n];
-            float dpart = 0.f;
+            float dpart = 0.f, apart = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int en = 8 * (r >> 2) + 4 * hl + (r & 3);
               const float al = fast_exp2(at[n][r] - mref);
               at[n][r] = al;
               dpart += al * nj[en];
+              apart += al;
             }
             dpart += __shfl_xor(dpart, 32);
             d_run[n] += dpart;
+            if (hybrid) a_run[n] += apart + __shfl_xor(apart, 32);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -590,6 +599,30 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
 #pragma unroll
             for (int n = 0; n < NQ; ++n) oacc[n][et] = mfma32(hf, bq[n], oacc[n][et]);
           }
+        }
+      }
+    }
+    if (hybrid) {   // O^T += Hbar^T (scale * sum alpha) q^T, once per row
+      wait_vmcnt<0>();
+      __syncthreads();
+      const uint8_t *hlp = lds + LY::TY_H;
+      float al[NQ];
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) al[n] = a_run[n] * dm.scale;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4_t bq[NQ];
+#pragma unroll
+        for (int n = 0; n < NQ; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            bq[n][i] = pack_bf16x2(bf16lo(qf[n][ks][i]) * al[n], bf16hi(qf[n][ks][i]) * al[n]);
+        const int ch = (2 * ks + hl) ^ xk;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+          const u32x4_t hf = *reinterpret_cast<const u32x4_t *>(hlp + (et * 32 + lq) * (2 * D) + (ch << 4));
+#pragma unroll
+          for (int n = 0; n < NQ; ++n) oacc[n][et] = mfma32(hf, bq[n], oacc[n][et]);
         }
       }
     }

@@ -29,7 +29,9 @@
 //   * the Taylor phase walks the union of the parts' Taylor blocks, 16 per
 //     logits batch (a^T = Kbar Q^T, zero order Sigma^T alpha^T with bf16
 //     hi/lo splits), and per block the first order u = H_j^T Q^T, added as
-//     O^T += (alpha scale) u in fp32; H tiles in a 3-deep ring, two ahead;
+//     O^T += (alpha scale) u in fp32; H tiles in a 3-deep ring, two ahead
+//     (hybrid order: the zero order only, plus one u = Hbar^T Q^T per row
+//     scaled by the row's summed Taylor weights);
 //   * row maxima move only when a logit exceeds them by more than 2^8.
 #include "attn_tiles.h"
 
@@ -486,7 +488,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     float *alp = reinterpret_cast<float *>(lds + C::TY_AL) + w * kNB * 32;
     float *nj = reinterpret_cast<float *>(lds + C::TY_NJ);
     const uint32_t *kb_me = kbm + part * 32;
-    const bool order1 = taylor == 2;
+    const bool order1 = taylor == 2, hybrid = taylor == 3;
+    float a_run = 0.f;   // hybrid: sum of this row's Taylor weights, on the scale of d_run
     // Loads of the Taylor phase are issued by waves 0..NDW-1 (as in the exact
     // phase): H_j tiles (PH kilobytes per issuing wave) and, half a batch
     // ahead, the next batch's kbar and vsum rows into an LDS staging area.
@@ -527,6 +530,10 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     if (order1) {
       dma_h(0);
       if (n_ty > 1) dma_h(1);
+    } else if (hybrid && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
+      const uint16_t *src = static_cast<const uint16_t *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
+#pragma unroll
+      for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], lds + C::TY_H + (w + NDW * u) * 1024);
     }
     const float *stg = reinterpret_cast<const float *>(lds + C::TY_STG);
     uint32_t tmask = 0;
@@ -613,22 +620,25 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           if (ballot64(grow)) {
             const float corr = grow ? fast_exp2(m_run - mx) : 1.f;
             d_run *= corr;
+            a_run *= corr;
 #pragma unroll
             for (int et = 0; et < NE; ++et) oacc[et] *= corr;
             m_run = grow ? mx : m_run;
           }
           const float mref = m_run == kNegInf ? 0.f : m_run;
-          float dpart = 0.f;
+          float dpart = 0.f, apart = 0.f;
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
             const int en = 8 * (r >> 2) + 4 * hl + (r & 3);
             const float al = fast_exp2(at[r] - mref);
             at[r] = al;
             dpart += al * nj[en];
+            apart += al;
             if (order1) alp[en * 32 + lq] = al * dm.scale;
           }
           dpart = pair_sum(dpart);
           d_run += dpart;
+          if (hybrid) a_run += pair_sum(apart);
           u32x4_t ph, pl;
           pack8_split(at, 0, ph, pl);
           // zero order: O^T += Sigma^T alpha^T  (hi*hi + lo*hi + hi*lo)
@@ -684,6 +694,20 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = NMT - KS - 1; c < NMT; ++c) fchunk(u, c);
+      }
+    }
+    if (hybrid) {   // O^T += (scale sum alpha) Hbar^T Q^T, once per row
+      wait_vmcnt<0>();
+      __syncthreads();
+      const uint8_t *hp = lds + C::TY_H;
+      const float al = a_run * dm.scale;
+#pragma unroll
+      for (int et = 0; et < NE; ++et) {
+        f32x16_t u = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) u = mfma32(frag_a<D>(hp, et * 32 + lq, 2 * ks + hl), qf[ks], u);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[et][r] = fmaf(al, u[r], oacc[et][r]);
       }
     }
   }

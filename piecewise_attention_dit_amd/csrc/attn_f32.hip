@@ -1,7 +1,8 @@
 // Stage C, fp32 path: a plain VALU kernel (one wave per query row at a
 // time) computing the same definition as the bf16 MFMA kernel -- PISA page,
 // section 2: o_t = N_t / D_t with exact terms over the kept blocks and the
-// per-block first-order Taylor term for the other candidates.  Used for fp32
+// per-block first-order Taylor term for the other candidates (or, in the
+// hybrid order, zero order per block plus q Hbar times the blocks' weights).  Used for fp32
 // problems, where bf16 MFMA operands would not meet fp32 accuracy.
 #include "attn_common.h"
 
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     int own, lo;
     const int nc = pisa_row_geometry(dm, pivot ? t : r * dm.bs, &own, &lo);
     const int32_t *list = a.idx ? a.idx + ((size_t)bh * dm.n_rows + r) * dm.topk : nullptr;
-    float m = kNegInf, dsum = 0.f, o[NE];
+    float m = kNegInf, dsum = 0.f, asum = 0.f, o[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) o[i] = 0.f;
     // exact blocks: the kept list, then the window range [lo, own] (causal)
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
         const float al = exp2f(x - mn);
         const float njf = (float)min(dm.bs, dm.L - j * dm.bs);
         dsum = dsum * corr + al * njf;
+        asum = asum * corr + al;
         m = mn;
         const float *vs = a.vsum + soff + (size_t)j * D;
         const float *Hj = static_cast<const float *>(a.HT) + (soff + (size_t)j * D) * D;
@@ -122,6 +124,16 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
             num = fmaf(dm.scale, qh, num);
           }
           o[i] = fmaf(al, num, o[i] * corr);
+        }
+      }
+      if (dm.taylor == 3 && asum > 0.f) {   // hybrid: + (scale sum alpha) q Hbar
+        const float *Hb = static_cast<const float *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+          const int e = l + 64 * i;
+          float qh = 0.f;
+          for (int c = 0; c < D; ++c) qh = fmaf(qs[w][c], Hb[(size_t)e * D + c], qh);
+          o[i] = fmaf(dm.scale * asum, qh, o[i]);
         }
       }
     }

@@ -46,7 +46,7 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
   if (p->block != 64 && p->block != 128)
     return fail(PISA_E_UNSUPPORTED, "block size %d not supported (64 or 128)", p->block);
   if (p->causal != 0 && p->causal != 1) return fail(PISA_E_ARG, "causal must be 0 or 1");
-  if (p->taylor < PISA_TAYLOR_NONE || p->taylor > PISA_TAYLOR_ORDER1)
+  if (p->taylor < PISA_TAYLOR_NONE || p->taylor > PISA_TAYLOR_HYBRID)
     return fail(PISA_E_ARG, "unknown taylor mode %d", p->taylor);
   if (p->topk < 0) return fail(PISA_E_ARG, "topk must be >= 0");
   if (p->topk > kMaxTopk) return fail(PISA_E_UNSUPPORTED, "topk %d > %d", p->topk, kMaxTopk);
@@ -135,7 +135,9 @@ pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]) {
   bytes[1] = kv * dm.d * es;
   bytes[2] = kv * dm.d * sizeof(float);
   bytes[3] = kv * dm.d * sizeof(float);
-  bytes[4] = kv * dm.d * dm.d * es;
+  bytes[4] = dm.taylor == PISA_TAYLOR_ORDER1   ? kv * dm.d * dm.d * es
+             : dm.taylor == PISA_TAYLOR_HYBRID ? (size_t)dm.B * dm.Hkv * dm.d * dm.d * es
+                                               : 0;
   return PISA_OK;
 }
 
@@ -153,7 +155,7 @@ pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes) {
   PISA_TRY(make_dims(p, &dm));
   if (!bytes) return fail(PISA_E_ARG, "bytes is NULL");
   if (op < 0 || op > 2) return fail(PISA_E_ARG, "unknown op %d", op);
-  *bytes = 0;
+  *bytes = op == 0 ? hbar_workspace_bytes(dm) : 0;
   return PISA_OK;
 }
 
@@ -170,10 +172,12 @@ pisa_status pisa_block_stats(const pisa_params *p, const void *Q, const void *K,
   PISA_TRY(check_ptr(out->ksel, "stats.ksel", true));
   PISA_TRY(check_ptr(out->kbar, "stats.kbar", ty));
   PISA_TRY(check_ptr(out->vsum, "stats.vsum", ty));
-  PISA_TRY(check_ptr(out->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1));
-  PISA_TRY(check_ws(ws, ws_bytes, 0));
+  PISA_TRY(check_ptr(out->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
+  const size_t need = hbar_workspace_bytes(dm);
+  PISA_TRY(check_ws(ws, ws_bytes, need));
+  if (need && !aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
   return launched(launch_block_stats(dm, Q, K, V, out->qsel, out->ksel, out->kbar, out->vsum,
-                                     out->HT, stream),
+                                     out->HT, need ? ws : nullptr, stream),
                   "block_stats");
 }
 
@@ -215,7 +219,7 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
     if (!stats) return fail(PISA_E_ARG, "stats is NULL but taylor != NONE");
     PISA_TRY(check_ptr(stats->kbar, "stats.kbar", true));
     PISA_TRY(check_ptr(stats->vsum, "stats.vsum", true));
-    PISA_TRY(check_ptr(stats->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1));
+    PISA_TRY(check_ptr(stats->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
   }
   PISA_TRY(check_ws(ws, ws_bytes, 0));
   return launched(launch_attn(dm, Q, K, V, ty ? stats->kbar : nullptr, ty ? stats->vsum : nullptr,

@@ -17,7 +17,7 @@ struct PisaDims {
   int group;       // 0: block rows; >= 1 PIVOT
   int n_cand;
   int causal;
-  int taylor;      // 0 none, 1 order0, 2 order1
+  int taylor;      // 0 none, 1 order0, 2 order1, 3 hybrid
   int ratio;       // Hq / Hkv
   int n_sel;       // rows of qsel
   int n_rows;      // rows of idx
@@ -47,9 +47,19 @@ inline int pisa_row_geometry(const PisaDims &dm, int start_token, int *own, int 
   return l;
 }
 
+// Hybrid order, bf16: the mean first-order matrix is summed over runs of
+// kHbarRun consecutive blocks into an fp32 workspace [B, Hkv, runs, d, d],
+// then the runs are added in order.
+constexpr int kHbarRun = 16;
+inline size_t hbar_workspace_bytes(const PisaDims &dm) {
+  if (dm.taylor != 3 || dm.dtype != 0) return 0;
+  const size_t runs = (size_t)(dm.n_blk + kHbarRun - 1) / kHbarRun;
+  return (size_t)dm.B * dm.Hkv * runs * dm.d * dm.d * sizeof(float);
+}
+
 // launchers (return the hipError_t of the launch)
 hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, const void *V,
-                              void *qsel, void *ksel, float *kbar, float *vsum, void *HT,
+                              void *qsel, void *ksel, float *kbar, float *vsum, void *HT, void *ws,
                               hipStream_t st);
 hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
                           int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);

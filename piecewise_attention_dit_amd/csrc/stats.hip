@@ -7,10 +7,14 @@
 //                vsum_j = sum of value rows, HT_j[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c)
 //   q_pool       one thread per (selection row, 16-byte column chunk):
 //                qsel = RNE_dtype(mean of the row's queries)
+//   hbar_*       hybrid order: HbarT = transposed mean of H_j over all blocks
+//                of a (b, kv head) (the global first-order statistic)
 //
 // The means are float64 cascaded sums divided once (IEEE division) and rounded
 // once into the dtype.  HBM-bound: Q, K and V are read exactly once.
-#include "device_common.h"
+#include "attn_tiles.h"
+
+using namespace pisa_attn;
 
 namespace {
 
@@ -251,6 +255,191 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_f32(PisaDims dm, const
 }
 
 // ---------------------------------------------------------------------------
+// Hybrid order: HbarT[e][c] = (1 / n_blk) sum_j H_j[c][e] (PISA page, section
+// 2: the global first-order statistic, the mean of the per-block matrices).
+//
+// bf16, two kernels:
+//   hbar_run    one workgroup of four waves per (b, kv head, run of kHbarRun
+//               consecutive blocks).  Each block of the run is staged in LDS
+//               by DMA (K and V tiles in the transposed-read layout, two
+//               slots); the waves form its raw moment R_j^T[e][c] =
+//               sum_n v_{n,e} k_{n,c} on MFMA (exact bf16 products, fp32 sums
+//               of at most 128 terms) and add H_j^T = R_j^T - sigma_j kbar_j^T
+//               to the run's fp32 sum in the workspace;
+//   hbar_final  one thread per (b, kv head, e, c): the runs in order, / n_blk.
+// The centring follows the exact products, so no rounded centred key enters,
+// and every sum has a fixed order, so the result is deterministic.
+template <int D, int BS>
+struct HbarCfg {
+  static constexpr int NE = D / 32;              // 32 x 32 tiles per dimension
+  static constexpr int TPW = NE * NE / 4;        // tiles per wave: one e tile, TPW c tiles
+  static constexpr int TILE = BS * D * 2;        // bytes of one K (or V) tile
+  static constexpr int CPW = TILE / 1024 / 4;    // DMA kilobytes per wave and tile
+  static constexpr int TOTAL = 4 * TILE;         // two slots of (K, V)
+  static_assert(CPW >= 1 && (TILE / 1024) % 4 == 0, "tile must split over four waves");
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void hbar_run(PisaDims dm, const uint16_t *__restrict__ K,
+                                                const uint16_t *__restrict__ V,
+                                                const float *__restrict__ kbar,
+                                                const float *__restrict__ vsum, float *__restrict__ ws) {
+  using C = HbarCfg<D, BS>;
+  constexpr int NE = C::NE, TPW = C::TPW, TILE = C::TILE, CPW = C::CPW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrun = (dm.n_blk + kHbarRun - 1) / kHbarRun;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);   // a head's runs share an XCD
+  const int run = logical % nrun, bh = logical / nrun;
+  const int j0 = run * kHbarRun, j1 = min(dm.n_blk, j0 + kHbarRun);
+  const int et = (w * TPW) / NE;                           // this wave's e tile
+  const int ct0 = (w * TPW) % NE;                          // and its first c tile
+  const size_t base = (size_t)bh * dm.L * D;
+  const uint16_t *Kb = K + base, *Vb = V + base;
+  const float *kb = kbar + (size_t)bh * dm.n_blk * D;
+  const float *vs = vsum + (size_t)bh * dm.n_blk * D;
+  int off[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int pos = (w + 4 * u) * 64 + l;
+    const int row = pos / (D / 8), phys = pos % (D / 8);
+    off[u] = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
+  }
+  auto dma = [&](int j) {
+    const int k0 = j * BS, bytes = max(dm.L - k0, 0) * D * 2;   // past the last key: zeros
+    uint8_t *dk = lds + ((j - j0) & 1) * 2 * TILE, *dv = dk + TILE;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      dma16_buf(Kb + (size_t)k0 * D, bytes, off[u], dk + (w + 4 * u) * 1024);
+      dma16_buf(Vb + (size_t)k0 * D, bytes, off[u], dv + (w + 4 * u) * 1024);
+    }
+  };
+  // accumulator entries of this lane: column c = 32 ct + lq, rows
+  // e = 32 et + 8 g + 4 hl + q at register 4 g + q
+  auto ldstat = [&](int j, float (&k1)[TPW], f32x4_t (&v4)[4]) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) k1[i] = kb[(size_t)j * D + (ct0 + i) * 32 + lq];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v4[g] = *reinterpret_cast<const f32x4_t *>(vs + (size_t)j * D + et * 32 + 8 * g + 4 * hl);
+  };
+  const int srow = (l & 15) >> 2, ecol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  f32x16_t tot[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) tot[i] = f32x16_t{};
+  float ck[TPW];
+  f32x4_t cv[4];
+  ldstat(j0, ck, cv);
+  dma(j0);
+  for (int j = j0; j < j1; ++j) {
+    wait_vmcnt<0>();
+    __syncthreads();   // block j landed for every wave; the other slot is free
+    float nk[TPW] = {};
+    f32x4_t nv[4] = {};
+    if (j + 1 < j1) {
+      ldstat(j + 1, nk, nv);
+      dma(j + 1);
+    }
+    const uint8_t *kt = lds + ((j - j0) & 1) * 2 * TILE, *vt = kt + TILE;
+    f32x16_t r[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) r[i] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < BS / 16; ++s) {
+      const int r1 = 16 * s + 4 * hl + srow;
+      const u32x4_t av = frag_vt<D>(vt, r1, et * 32 + ecol);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) r[i] = mfma32(av, frag_vt<D>(kt, r1, (ct0 + i) * 32 + ecol), r[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[i][4 * g + q] += r[i][4 * g + q] - cv[g][q] * ck[i];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) ck[i] = nk[i];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) cv[g] = nv[g];
+  }
+  float *out = ws + ((size_t)bh * nrun + run) * D * D;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        out[(size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq] = tot[i][4 * g + q];
+}
+
+__global__ __launch_bounds__(256) void hbar_final(PisaDims dm, const float *__restrict__ ws,
+                                                  uint16_t *__restrict__ HbT) {
+  const int DD = dm.d * dm.d;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)dm.B * dm.Hkv * DD) return;
+  const int nrun = (dm.n_blk + kHbarRun - 1) / kHbarRun;
+  const long long bh = gid / DD;
+  const int o = (int)(gid % DD);
+  const float *src = ws + (size_t)bh * nrun * DD + o;
+  float s = 0.f;
+  for (int r = 0; r < nrun; ++r) s += src[(size_t)r * DD];
+  HbT[gid] = (uint16_t)f32_to_bf16(s / (float)dm.n_blk);
+}
+
+// fp32: one thread per (e, c), the same order of operations on the VALU.
+template <int D, int BS>
+__global__ __launch_bounds__(kStatsThreads) void hbar_f32(PisaDims dm, const float *__restrict__ K,
+                                                          const float *__restrict__ V,
+                                                          const float *__restrict__ kbar,
+                                                          const float *__restrict__ vsum,
+                                                          float *__restrict__ HbT) {
+  constexpr int PER = D * D / kStatsThreads;
+  const int bh = blockIdx.x / PER;
+  const int o = (blockIdx.x % PER) * kStatsThreads + threadIdx.x;
+  const int e = o / D, c = o % D;
+  const float *Kb = K + (size_t)bh * dm.L * D, *Vb = V + (size_t)bh * dm.L * D;
+  const float *kb = kbar + (size_t)bh * dm.n_blk * D, *vs = vsum + (size_t)bh * dm.n_blk * D;
+  float tot = 0.f;
+  for (int j = 0; j < dm.n_blk; ++j) {
+    const int t1 = min(dm.L, (j + 1) * BS);
+    float r = 0.f;
+    for (int t = j * BS; t < t1; ++t) r = fmaf(Vb[(size_t)t * D + e], Kb[(size_t)t * D + c], r);
+    tot += r - vs[(size_t)j * D + e] * kb[(size_t)j * D + c];
+  }
+  HbT[(size_t)bh * D * D + o] = tot / (float)dm.n_blk;
+}
+
+template <int D, int BS>
+hipError_t launch_hbar(const PisaDims &dm, const void *K, const void *V, const float *kbar, const float *vsum,
+                       void *HT, void *ws, hipStream_t st) {
+  if (dm.dtype == 0) {
+    using C = HbarCfg<D, BS>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hbar_run<D, BS>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    const int nrun = (dm.n_blk + kHbarRun - 1) / kHbarRun;
+    hbar_run<D, BS><<<(unsigned)dm.B * dm.Hkv * nrun, 256, C::TOTAL, st>>>(
+        dm, static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V), kbar, vsum,
+        static_cast<float *>(ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long n = (long long)dm.B * dm.Hkv * D * D;
+    hbar_final<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dm, static_cast<const float *>(ws),
+                                                             static_cast<uint16_t *>(HT));
+  } else {
+    const unsigned grid = (unsigned)dm.B * dm.Hkv * (D * D / kStatsThreads);
+    hbar_f32<D, BS><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const float *>(K),
+                                                    static_cast<const float *>(V), kbar, vsum,
+                                                    static_cast<float *>(HT));
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // query pooling: one thread per (selection row, 16-byte chunk of the row)
 template <typename T, int D>
 __global__ __launch_bounds__(kStatsThreads) void q_pool(PisaDims dm, const T *__restrict__ Q, T *__restrict__ qsel) {
@@ -328,7 +517,7 @@ hipError_t launch_kv_f32(const PisaDims &dm, const void *K, const void *V, void 
 }  // namespace
 
 hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, const void *V, void *qsel,
-                              void *ksel, float *kbar, float *vsum, void *HT, hipStream_t st) {
+                              void *ksel, float *kbar, float *vsum, void *HT, void *ws, hipStream_t st) {
   hipError_t e;
   const bool bf = dm.dtype == 0;
   if (bf) {
@@ -343,6 +532,13 @@ hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, 
                          : launch_kv_f32<128, 128>(dm, K, V, ksel, kbar, vsum, HT, st);
   }
   if (e != hipSuccess) return e;
+  if (dm.taylor == 3) {   // hybrid: the mean first-order matrix, after kbar and vsum
+    if (dm.d == 64) e = dm.bs == 64 ? launch_hbar<64, 64>(dm, K, V, kbar, vsum, HT, ws, st)
+                                    : launch_hbar<64, 128>(dm, K, V, kbar, vsum, HT, ws, st);
+    else e = dm.bs == 64 ? launch_hbar<128, 64>(dm, K, V, kbar, vsum, HT, ws, st)
+                         : launch_hbar<128, 128>(dm, K, V, kbar, vsum, HT, ws, st);
+    if (e != hipSuccess) return e;
+  }
   if (bf) return dm.d == 64 ? launch_q_pool<uint16_t, 64>(dm, Q, qsel, st) : launch_q_pool<uint16_t, 128>(dm, Q, qsel, st);
   return dm.d == 64 ? launch_q_pool<float, 64>(dm, Q, qsel, st) : launch_q_pool<float, 128>(dm, Q, qsel, st);
 }

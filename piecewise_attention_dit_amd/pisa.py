@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libpisa.so")
 
 PISA_OK, PISA_E_ARG, PISA_E_UNSUPPORTED, PISA_E_WORKSPACE, PISA_E_HIP = range(5)
 DTYPES = {"bf16": 0, "f32": 1}
-TAYLOR = {"none": 0, "order0": 1, "order1": 2}
+TAYLOR = {"none": 0, "order0": 1, "order1": 2, "hybrid": 3}
 DIAG_BYTES = 64
 
 
@@ -136,6 +136,8 @@ def alloc_stats(p: Params, device="cuda") -> dict:
         st["vsum"] = torch.empty((p.B, p.Hkv, n_blk, p.d), dtype=torch.float32, device=device)
     if p.taylor == TAYLOR["order1"]:
         st["HT"] = torch.empty((p.B, p.Hkv, n_blk, p.d, p.d), dtype=td, device=device)
+    elif p.taylor == TAYLOR["hybrid"]:   # the transposed mean first-order matrix
+        st["HT"] = torch.empty((p.B, p.Hkv, p.d, p.d), dtype=td, device=device)
     return st
 
 
@@ -144,11 +146,16 @@ def _cstats(st: dict) -> Stats:
                    for k in ("qsel", "ksel", "kbar", "vsum", "HT")))
 
 
-def block_stats(p: Params, q, k, v, stats=None, stream=None) -> dict:
+def block_stats(p: Params, q, k, v, stats=None, ws=None, stream=None) -> dict:
+    """Stage A.  ws: a device byte buffer of at least workspace_size(p, 0)
+    bytes (allocated here when the mode needs one and none is given)."""
     st = stats if stats is not None else alloc_stats(p, q.device)
     cs = _cstats(st)
+    need = workspace_size(p, 0)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(lib().pisa_block_stats(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
-                                  None, 0, _stream(stream)))
+                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
     return st
 
 

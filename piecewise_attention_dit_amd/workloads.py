@@ -114,6 +114,21 @@ PARITY_CASES = {
     "llm_swa_s_b128": WORKLOADS["llm_swa"].replace(name="llm_swa_s_b128", B=1, Hq=4,
                                                    Hkv=1, L=1900, block=128, window=300,
                                                    topk=3, taylor="order0"),
+    # hybrid order: every attention kernel and both Hbar kernels
+    "tiny_f32_hyb": WORKLOADS["tiny_f32"].replace(name="tiny_f32_hyb", L=1000, grid=(),
+                                                  recipe="gauss", topk=3, taylor="hybrid"),
+    "image_dit_s_hyb": WORKLOADS["image_dit"].replace(name="image_dit_s_hyb", B=1, Hq=2,
+                                                      Hkv=2, L=1024, grid=(32, 32), topk=4,
+                                                      taylor="hybrid"),
+    "video_dit_s_hyb": WORKLOADS["video_dit"].replace(name="video_dit_s_hyb", Hq=2, Hkv=2,
+                                                      L=1000, grid=(1, 20, 50), topk=2,
+                                                      taylor="hybrid"),
+    "llm_swa_s_hyb": WORKLOADS["llm_swa"].replace(name="llm_swa_s_hyb", B=2, Hq=4, Hkv=2,
+                                                  L=2048 + 24, window=384, topk=4,
+                                                  taylor="hybrid"),
+    "llm_pivot_s_hyb": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_hyb", Hq=4, Hkv=2,
+                                                      L=1024 + 40, topk=4, n_cand=8,
+                                                      taylor="hybrid"),
 }
 
 

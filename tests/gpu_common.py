@@ -53,6 +53,13 @@ def compare_stats(g: dict, st: dict, P: po.Problem):
         den = np.linalg.norm(H.reshape(-1, P.d * P.d), axis=1) + 1e-30
         rel = (num / den).max()
         assert rel < TOL[P.dtype]["H"], f"H relative Frobenius error {rel}"
+    if P.taylor == "hybrid":
+        Hb = st["Hbar"]                                # [B, Hkv, c, e]
+        HbT = to64(gs["HT"])                           # [B, Hkv, e, c]
+        num = np.linalg.norm((np.swapaxes(HbT, -1, -2) - Hb).reshape(-1, P.d * P.d), axis=1)
+        den = np.linalg.norm(Hb.reshape(-1, P.d * P.d), axis=1) + 1e-30
+        rel = (num / den).max()
+        assert rel < TOL[P.dtype]["H"], f"Hbar relative Frobenius error {rel}"
 
 
 def compare_idx(g: dict, idx: np.ndarray, cand, rows=None):

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = pisa.lib()
-    assert L.pisa_abi_version() == 1
+    assert L.pisa_abi_version() == 2
     assert L.pisa_status_string(pisa.PISA_E_UNSUPPORTED).decode() == "PISA_E_UNSUPPORTED"
 
 
@@ -86,6 +86,18 @@ def test_layouts():
     assert pisa.index_layout(q) == [4 * 1000 * 4 * 4, 4 * 125 * 16 * 4]
     for op in (0, 1, 2):
         assert pisa.workspace_size(p, op) == 0
+    # the first-order statistic: per block for order 1, one mean matrix for
+    # the hybrid order, none otherwise
+    h = _p(L=1000, group=0, taylor="hybrid")
+    assert pisa.stats_layout(h)[4] == 2 * 128 * 128 * 2
+    assert pisa.stats_layout(h)[2:4] == sizes[2:4]
+    for mode in ("none", "order0"):
+        assert pisa.stats_layout(_p(L=1000, group=0, taylor=mode, topk=2))[4] == 0
+    # the hybrid order's bf16 statistics need fp32 run sums: ceil(16 / 16) runs here
+    assert pisa.workspace_size(h, 0) == 1 * 2 * 1 * 128 * 128 * 4
+    assert pisa.workspace_size(_p(L=64 * 40, taylor="hybrid"), 0) == 2 * 3 * 128 * 128 * 4
+    assert pisa.workspace_size(_p(L=1000, taylor="hybrid", dtype="f32"), 0) == 0
+    assert all(pisa.workspace_size(h, op) == 0 for op in (1, 2))
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
@@ -105,6 +117,10 @@ def test_launch_calls_reject_before_launch():
     assert b"aligned" in L.pisa_last_error()
     assert _call_stats(p, st=pisa.Stats(FAKE, FAKE, None, FAKE, FAKE)) == pisa.PISA_E_ARG
     assert _call_stats(p, ws=None, ws_bytes=128) == pisa.PISA_E_ARG
+    hy = _p(taylor="hybrid")                                      # needs a workspace
+    assert _call_stats(hy) == pisa.PISA_E_WORKSPACE
+    assert _call_stats(hy, ws=FAKE, ws_bytes=pisa.workspace_size(hy, 0) - 16) == pisa.PISA_E_WORKSPACE
+    assert _call_stats(hy, ws=FAKE + 4, ws_bytes=pisa.workspace_size(hy, 0)) == pisa.PISA_E_ARG
     assert _call_stats(_p(d=80)) == pisa.PISA_E_UNSUPPORTED
     assert L.pisa_block_stats(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, 0, None) == pisa.PISA_E_ARG
     st = pisa.Stats(FAKE, FAKE, FAKE, FAKE, FAKE)

@@ -46,6 +46,9 @@ def test_parity_cases(name):
     dict(L=640, block=128, topk=2, group=8, n_cand=5, causal=False, taylor="order0"),
     dict(L=600, block=64, topk=2, d=64, Hq=2, Hkv=2, taylor="order1", dtype="f32", causal=True,
          window=100),
+    dict(L=700, block=64, topk=0, taylor="hybrid"),               # hybrid, all blocks Taylor
+    dict(L=777, block=128, topk=1, d=64, taylor="hybrid"),        # hybrid, d 64 with 128-blocks
+    dict(L=300, block=128, topk=1, d=128, taylor="hybrid", dtype="f32"),
 ])
 def test_edge_cases(kw):
     base = dict(B=1, Hq=2, Hkv=2, L=256, d=128, dtype="bf16", block=64, topk=2, window=0, group=0,
