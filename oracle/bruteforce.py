@@ -13,7 +13,9 @@ term, alpha * n_j in the denominator; the hybrid order's global first-order
 correction q_t Hbar sum_j alpha_{t,j} with Hbar the mean of the per-block
 matrices over all blocks); the PIVOT page's steps 1-4 (proxy =
 mean of g consecutive queries, candidates re-ranked per member); the Sliding
-Window Attention page's causal mask 0 <= t - s < w.
+Window Attention page's causal mask 0 <= t - s < w, and its attention sinks
+(the first blocks of the sequence kept beside the window; the top-k is chosen
+among the other candidates).
 """
 from __future__ import annotations
 
@@ -97,21 +99,25 @@ def run(q, k, v, P):
 
             # selection
             kept_of = {}
+            sink = getattr(P, "sink", 0)
             if P.group >= 1:
                 g = P.group
                 for gm in range(-(-L // g)):
                     members = list(range(gm * g, min(L, (gm + 1) * g)))
                     _, proxy = _pool([q[b][h][t] for t in members], P.dtype)
                     _, _, cands = geometry(gm * g)
-                    clist = rank(proxy, cands, min(P.n_cand, len(cands)))
+                    rest = cands[sink:]
+                    clist = rank(proxy, rest, min(P.n_cand, len(rest)))
                     for t in members:
-                        kept_of[t] = rank(q[b][h][t], clist, min(P.topk, len(clist)))
+                        own_sinks = geometry(t)[2][:sink]
+                        kept_of[t] = own_sinks + rank(q[b][h][t], clist, min(P.topk, len(clist)))
                         res_idx[(b, h, t)] = kept_of[t]
             else:
                 for i in range(nb):
                     _, qs = _pool([q[b][h][t] for t in blocks[i]], P.dtype)
                     _, _, cands = geometry(i * bs)
-                    kept_of[i] = rank(qs, cands, min(P.topk, len(cands)))
+                    rest = cands[sink:]
+                    kept_of[i] = cands[:sink] + rank(qs, rest, min(P.topk, len(rest)))
                     res_idx[(b, h, i)] = kept_of[i]
             # attention, token by token
             for t in range(L):

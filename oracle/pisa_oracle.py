@@ -28,6 +28,11 @@ The definition implemented (notation of the PISA page):
     non-kept candidate block, alpha = exp(scale q_t . kbar_j) times
     (sigma_j + scale q_t H_j) in N_t and alpha * n_j in D_t (first order per
     block; order 0 drops the H term; "none" drops the block).
+  * Attention sinks ([SWA] glossary, attention sinks: StreamingLLM keeps the
+    first tokens beside the window): with ``sink`` = s > 0 the first s key
+    blocks that are candidates of a row are always kept exactly; the row's
+    top-k is chosen among its other candidates, and its kept list holds the
+    sink blocks followed by the top-k (width k + s).
   * Hybrid order ([PISA] section 2, the global first-order correction): zero
     order per non-kept block plus scale q_t Hbar sum_{j in U} alpha_{t,j} in
     N_t, Hbar = the mean of H_j over all blocks of the (batch, KV head).
@@ -63,6 +68,7 @@ class Problem:
     causal: bool = False
     taylor: str = "order1"
     scale: float = 0.0       # <= 0 -> 1/sqrt(d)
+    sink: int = 0            # leading key blocks always kept (attention sinks)
 
     @property
     def sm_scale(self) -> float:
@@ -80,6 +86,11 @@ class Problem:
     def n_rows(self) -> int:
         """Rows of the index list: query blocks, or tokens in PIVOT mode."""
         return self.L if self.pivot else self.n_blk
+
+    @property
+    def klist(self) -> int:
+        """Width of a kept list: the sink blocks and the top-k."""
+        return self.topk + self.sink
 
     @property
     def n_sel(self) -> int:
@@ -204,6 +215,12 @@ def row_geometry(P: Problem, r: int):
     return own, lo, lo
 
 
+def sink_count(P: Problem, nc: int) -> int:
+    """Sink blocks of a row with nc candidates: the first min(s, nc) candidate
+    blocks (sinks inside the exact window range are kept by the range)."""
+    return min(P.sink, nc)
+
+
 def group_candidates(P: Problem, gamma: int) -> int:
     """Candidate block count of PIVOT group gamma: the candidates of its first
     member, blocks [0, lo) (a prefix of every member's candidate range)."""
@@ -251,17 +268,19 @@ def top_n(p: np.ndarray, K: np.ndarray, ids: np.ndarray, n: int) -> np.ndarray:
 
 
 def select(q: np.ndarray, st: dict, P: Problem):
-    """Kept top-k lists.  Returns (idx, cand):
-      idx  int64 [B, Hq, n_rows, topk], ascending, -1 padded; row = query block
-           (block rows) or token (PIVOT);
+    """Kept lists.  Returns (idx, cand):
+      idx  int64 [B, Hq, n_rows, topk + sink], ascending, -1 padded; row =
+           query block (block rows) or token (PIVOT);
       cand int64 [B, Hq, n_groups, n_cand] PIVOT proxy lists (None otherwise).
-    Block rows: T_r = top-min(k, |cand_r|) of the candidates by qsel_r . ksel_j.
-    PIVOT: Cand_gamma = top-min(C, |cand_gamma|) by the proxy's score, then each
-    member t keeps T_t = top-min(k, |Cand_gamma|) of Cand_gamma by q_t . ksel_j
-    (C = k is PIVOT-Reuse; g = 1 with C >= |cand| is the dense indexer)."""
+    With c0 = min(sink, |cand_r|) sink blocks 0 .. c0-1 first, then:
+    Block rows: T_r = top-min(k, |cand_r| - c0) of candidates c0 .. by qsel_r . ksel_j.
+    PIVOT: Cand_gamma = top-min(C, ..) of the group's candidates past its sinks
+    by the proxy's score, then each member t keeps T_t = top-min(k,
+    |Cand_gamma|) of Cand_gamma by q_t . ksel_j, after its own sinks (C = k is
+    PIVOT-Reuse; g = 1 with C >= |cand| is the dense indexer)."""
     B, Hq, Hkv = P.B, P.Hq, P.Hkv
     k = P.topk
-    idx = np.full((B, Hq, P.n_rows, k), -1, dtype=np.int64)
+    idx = np.full((B, Hq, P.n_rows, P.klist), -1, dtype=np.int64)
     ksel, qsel = st["ksel"], st["qsel"]
     cand = None
     if P.pivot:
@@ -275,16 +294,19 @@ def select(q: np.ndarray, st: dict, P: Problem):
             if not P.pivot:
                 for r in range(P.n_rows):
                     nc = row_geometry(P, r)[2]
-                    t = top_n(qsel[b, h, r], Kb[:nc], np.arange(nc), k)
-                    idx[b, h, r, :len(t)] = t
+                    c0 = sink_count(P, nc)
+                    t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k)
+                    idx[b, h, r, :c0 + len(t)] = np.concatenate([np.arange(c0), t])
             else:
                 for gm in range(P.n_sel):
                     nc = group_candidates(P, gm)
-                    cl = top_n(qsel[b, h, gm], Kb[:nc], np.arange(nc), C)
+                    c0 = sink_count(P, nc)
+                    cl = top_n(qsel[b, h, gm], Kb[c0:nc], np.arange(c0, nc), C)
                     cand[b, h, gm, :len(cl)] = cl
                     for t in range(gm * P.group, min(P.L, (gm + 1) * P.group)):
+                        ct = sink_count(P, row_geometry(P, t)[2])
                         tt = top_n(q[b, h, t], Kb[cl], cl, k)
-                        idx[b, h, t, :len(tt)] = tt
+                        idx[b, h, t, :ct + len(tt)] = np.concatenate([np.arange(ct), tt])
     return idx, cand
 
 

@@ -155,8 +155,28 @@ def check_hybrid(m):
     return ok and np.abs(oh - acc).max() < 1e-12
 
 
+def check_sinks(m):
+    """One-token blocks, no top-k: the kept set is the first `sink` tokens and
+    the window; and a sink does not take a place in the top-k."""
+    B, H, L, d = 1, 1, 30, 6
+    q, k, v = _rand((B, H, L, d), 19), _rand((B, H, L, d), 20), _rand((B, H, L, d), 21)
+    P = m.Problem(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=1, topk=0, window=4, causal=True,
+                  taylor="none", sink=3)
+    t, s_ = np.arange(L)[:, None], np.arange(L)[None, :]
+    mask = (s_ <= t) & ((t - s_ < 4) | (s_ < 3))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=torch.from_numpy(mask),
+        scale=P.sm_scale).numpy()
+    ok = np.abs(m.run(q, k, v, P)["O"] - o).max() < 1e-12
+    P2 = m.Problem(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=1, topk=2, window=4, causal=True,
+                   taylor="none", sink=3)
+    r = m.run(q, k, v, P2)
+    row = r["idx"][0, 0, L - 1]
+    return ok and row[:3].tolist() == [0, 1, 2] and (row[3:] >= 3).all() and len(set(row.tolist())) == 5
+
+
 CHECKS = [check_pivot_mean, check_swa_count, check_dense, check_constant_v, check_orders, check_ties,
-          check_pivot_reuse, check_pooled_selection, check_hybrid]
+          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks]
 
 MUTATIONS = {
     "H transposed": ('H[:, :, j] = np.einsum("bhnc,bhne->bhce", kc, vj)',
@@ -184,6 +204,10 @@ MUTATIONS = {
     "hybrid term without scale": ('N = N + sc * (qt @ st["Hbar"]', 'N = N + 1.0 * (qt @ st["Hbar"]'),
     "hybrid weights include exact terms": ('* pa.sum(axis=1)[:, None]',
                                            '* (pa.sum(axis=1) + px.sum(axis=1))[:, None]'),
+    "sinks take top-k places": ("t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k)",
+                                "t = top_n(qsel[b, h, r], Kb[:nc], np.arange(nc), k)[:max(0, k - c0)]"),
+    "sinks not kept": ("idx[b, h, r, :c0 + len(t)] = np.concatenate([np.arange(c0), t])",
+                       "idx[b, h, r, :len(t)] = t"),
     "scale not applied to exact logits": ("x = sc * (qt @ k[b, hk, keys].T)", "x = (qt @ k[b, hk, keys].T)"),
 }
 

@@ -320,6 +320,11 @@ BRUTE_CASES = [
     dict(Hq=2, Hkv=2, L=45, block=8, topk=2, causal=True, window=12, taylor="hybrid", dtype="f32"),
     dict(Hq=2, Hkv=1, L=40, block=8, topk=2, group=4, n_cand=3, causal=True, taylor="hybrid",
          dtype="bf16"),
+    dict(Hq=2, Hkv=1, L=57, block=4, topk=2, causal=True, window=9, sink=2, taylor="order1",
+         dtype="bf16"),
+    dict(Hq=2, Hkv=2, L=40, block=8, topk=1, causal=False, sink=1, taylor="hybrid", dtype="f32"),
+    dict(Hq=2, Hkv=1, L=48, block=4, topk=2, group=2, n_cand=3, causal=True, window=6, sink=2,
+         taylor="order0", dtype="bf16"),
 ]
 
 
@@ -444,6 +449,56 @@ def test_p13_hbar_uncentred_identity():
     raw = np.einsum("bhsc,bhse->bhce", k, v)
     corr = np.einsum("bhjc,bhje->bhce", st["kbar"], st["vsum"])
     np.testing.assert_allclose(st["Hbar"], (raw - corr) / P.n_blk, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# P14: attention sinks ([SWA] glossary: StreamingLLM keeps the first tokens
+# beside the window).  With one-token blocks, no top-k and no Taylor term the
+# kept set is exactly {s : s < sink or 0 <= t - s < w}, s <= t: the output is
+# dense attention under that mask (torch SDPA with the mask built here).
+
+@pytest.mark.parametrize("window,sink", [(5, 3), (1, 1), (12, 4), (3, 40)])
+def test_p14_sinks_are_streaming_mask(window, sink):
+    B, H, L, d = 1, 2, 40, 8
+    q, k, v = (_rand((B, H, L, d), s) for s in (131, 132, 133))
+    P = po.Problem(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=1, topk=0, window=window,
+                   causal=True, taylor="none", sink=sink)
+    t = np.arange(L)[:, None]
+    s_ = np.arange(L)[None, :]
+    mask = (s_ <= t) & ((t - s_ < window) | (s_ < sink))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask), scale=P.sm_scale).numpy()
+    np.testing.assert_allclose(po.run(q, k, v, P)["O"], o, atol=1e-13)
+
+
+@pytest.mark.parametrize("pivot", [False, True])
+def test_p14_sinks_do_not_use_the_topk_budget(pivot):
+    """Block 0 and blocks 2, 5, 9 are planted with exactly equal scores (the
+    other blocks score 0).  Without sinks a top-3 keeps 0, 2, 5 (ties to the
+    lower index); with one sink block the list is the sink 0 followed by the
+    top-3 of the rest: 2, 5, 9."""
+    B, Hq, Hkv, L, d, bs = 1, 2, 1, 512, 16, 32
+    u = np.zeros(d)
+    u[3] = 1.0
+    rng = np.random.default_rng(141)
+    q = po.rne(0.05 * rng.standard_normal((B, Hq, L, d)) + 2.0 * u, "bf16")
+    k = np.zeros((B, Hkv, L, d))
+    for j in (0, 2, 5, 9):
+        k[0, 0, j * bs:(j + 1) * bs] += 4.0 * u
+    k = po.rne(k, "bf16")
+    v = _rand((B, Hkv, L, d), 142, "bf16")
+    kw = dict(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=bs, topk=3, taylor="order0", causal=True)
+    if pivot:
+        kw.update(group=8, n_cand=5)
+    for sink, want in ((0, [0, 2, 5]), (1, [0, 2, 5, 9])):
+        P = po.Problem(sink=sink, **kw)
+        r = po.run(q, k, v, P)
+        for row in range(P.n_rows):
+            nc = po.row_geometry(P, row)[2]
+            if nc > 10:
+                got = r["idx"][0, 0, row]
+                assert got[got >= 0].tolist() == want, (sink, row, got)
 
 
 # ---------------------------------------------------------------------------
