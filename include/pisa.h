@@ -96,6 +96,10 @@ typedef struct {
   int32_t causal;   /* 0 or 1 */
   int32_t taylor;   /* pisa_taylor */
   float scale;      /* softmax scale; <= 0 selects 1/sqrt(d) */
+  int32_t sink;     /* attention sinks ([SWA] glossary): the first min(sink,
+                       |cand_r|) candidate blocks of every row are always kept
+                       exactly and head its kept list; the top-k is chosen
+                       among the other candidates.  topk + sink <= 64. */
 } pisa_params;
 
 /* Block statistics ([PISA] precompute; [PIVOT] step 2).  Caller-allocated,
@@ -132,9 +136,9 @@ pisa_status pisa_validate(const pisa_params *p);
  * (qsel, ksel, kbar, vsum, HT). */
 pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]);
 
-/* Byte sizes of the index list idx (int32 [B, Hq, n_rows, topk], n_rows =
- * n_blk for group == 0 else L) and of the PIVOT proxy list cand (int32
- * [B, Hq, ceil(L / g), n_cand]; 0 when group == 0). */
+/* Byte sizes of the index list idx (int32 [B, Hq, n_rows, topk + sink],
+ * n_rows = n_blk for group == 0 else L) and of the PIVOT proxy list cand
+ * (int32 [B, Hq, ceil(L / g), n_cand]; 0 when group == 0). */
 pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]);
 
 /* Workspace bytes call `op` needs (0 = block_stats, 1 = indexer_topk,
@@ -167,10 +171,13 @@ pisa_status pisa_block_stats(const pisa_params *p, const void *Q, const void *K,
  * block index.  Candidates: every block when non-causal; when causal, blocks
  * [0, lo_r) where lo_r = blk(max(0, start_r - w + 1)) (w > 0) or the row's
  * own block (w = 0), start_r being the first token of the row; the range
- * [lo_r, own block] is kept implicitly and not stored.  PIVOT: the proxy of
- * group gamma keeps the top-min(C, |cand|) of its first member's candidates;
- * each member keeps the top-min(k, C') of that list by its own score.
- * Writes idx (ascending, -1 padded) and, if non-NULL, cand. */
+ * [lo_r, own block] is kept implicitly and not stored.  With sinks, the
+ * first c0 = min(sink, |cand_r|) candidates are kept and listed first, and
+ * the top-k is taken over the candidates from c0 on.  PIVOT: the proxy of
+ * group gamma keeps the top-min(C, |cand| - c0) of its first member's
+ * candidates past their sinks; each member keeps its own sinks and the
+ * top-min(k, C') of that list by its own score.
+ * Writes idx (ascending, -1 padded to topk + sink) and, if non-NULL, cand. */
 pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_stats *stats,
                               int32_t *idx, int32_t *cand, void *ws, size_t ws_bytes,
                               hipStream_t stream);

@@ -101,10 +101,11 @@ struct Shared {
   int64_t kul[kLimbs * 64];
 };
 
-// Rank the candidates cand(c) = (list ? list[c] : c), c < nc, of one row and
-// mark the n_take best in sel[].  NS slots per lane (candidate c = s*64+lane).
+// Rank the candidates cand(c) = (list ? list[c] : base + c), c < nc, of one
+// row and mark the n_take best in sel[].  NS slots per lane (candidate
+// c = s*64+lane).
 template <typename T, int D, int NS>
-PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int nc, int n_take,
+PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int base, int nc, int n_take,
                          bool (&sel)[NS], int (&cj)[NS], int32_t *diag) {
   const int l = lane_id();
   bool valid[NS];
@@ -112,7 +113,7 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int nc
   for (int s = 0; s < NS; ++s) {
     const int c = s * 64 + l;
     valid[s] = c < nc;
-    cj[s] = valid[s] ? (list ? list[c] : c) : 0;
+    cj[s] = valid[s] ? (list ? list[c] : base + c) : 0;
     sel[s] = false;
   }
   if (n_take <= 0) return;
@@ -323,12 +324,15 @@ __global__ __launch_bounds__(64) void indexer_blockrows(PisaDims dm, const T *__
   const T *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
   int own, lo;
   const int nc = pisa_row_geometry(dm, i * dm.bs, &own, &lo);
-  const int n_take = min(dm.topk, nc);
+  const int c0 = min(dm.sink, nc);            // sink blocks, kept and listed first
+  const int n_take = min(dm.topk, nc - c0);
   load_p<T, D>(sh, qsel + ((size_t)bh * dm.n_sel + i) * D);
   bool sel[kMaxSlots];
   int cj[kMaxSlots];
-  select_row<T, D, kMaxSlots>(sh, kbase, nullptr, nc, n_take, sel, cj, diag);
-  write_sorted<kMaxSlots>(sel, cj, idx + ((size_t)bh * dm.n_rows + i) * dm.topk, dm.topk);
+  select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, n_take, sel, cj, diag);
+  int32_t *out = idx + ((size_t)bh * dm.n_rows + i) * dm.klist;
+  for (int c = lane_id(); c < c0; c += 64) out[c] = c;
+  write_sorted<kMaxSlots>(sel, cj, out + c0, dm.klist - c0);
 }
 
 template <typename T, int D>
@@ -346,13 +350,14 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
   const int g = dm.group;
   int own, lo;
   const int nc = pisa_row_geometry(dm, gm * g, &own, &lo);
-  const int C = min(dm.n_cand, nc);
-  // proxy pass over every candidate block
+  const int c0 = min(dm.sink, nc);
+  const int C = min(dm.n_cand, nc - c0);
+  // proxy pass over every candidate block past the sinks
   load_p<T, D>(sh, qsel + ((size_t)bh * dm.n_sel + gm) * D);
   {
     bool sel[kMaxSlots];
     int cj[kMaxSlots];
-    select_row<T, D, kMaxSlots>(sh, kbase, nullptr, nc, C, sel, cj, diag);
+    select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C, sel, cj, diag);
     write_sorted<kMaxSlots>(sel, cj, sh.clist, C);
     if (cand) {
       __syncthreads();
@@ -361,16 +366,19 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
     }
   }
   __syncthreads();
-  if (dm.topk == 0) return;
-  // member pass over the proxy's list
+  if (dm.klist == 0) return;
+  // member pass over the proxy's list, after each member's own sinks
   const int n_take = min(dm.topk, C);
   const int t1 = min(dm.L, (gm + 1) * g);
   for (int t = gm * g; t < t1; ++t) {
     load_p<T, D>(sh, Q + ((size_t)bh * dm.L + t) * D);
     bool sel[4];
     int cj[4];
-    select_row<T, D, 4>(sh, kbase, sh.clist, C, n_take, sel, cj, diag);
-    write_sorted<4>(sel, cj, idx + ((size_t)bh * dm.n_rows + t) * dm.topk, dm.topk);
+    select_row<T, D, 4>(sh, kbase, sh.clist, 0, C, n_take, sel, cj, diag);
+    const int ct = min(dm.sink, pisa_row_geometry(dm, t, &own, &lo));
+    int32_t *out = idx + ((size_t)bh * dm.n_rows + t) * dm.klist;
+    for (int c = lane_id(); c < ct; c += 64) out[c] = c;
+    write_sorted<4>(sel, cj, out + ct, dm.klist - ct);
     __syncthreads();
   }
 }
@@ -619,12 +627,13 @@ PISA_DEV void load_vec_f32(float *dst, const uint16_t *src) {
 
 // Re-score tier for one row whose fast selection was not certified.  srow:
 // fp32 scores by list position; list: block ids by position (nullptr: the
-// position is the id); nc positions; bounds cb |k_j| + 2^-110 as in the fast
-// tier; vec: the row's own vector (bf16, global), staged to pv.  On success
-// writes the row like write_sorted_lds and returns true.
+// position is the id); positions lo .. nc-1 are candidates; bounds
+// cb |k_j| + 2^-110 as in the fast tier; vec: the row's own vector (bf16,
+// global), staged to pv.  On success writes the row like write_sorted_lds
+// and returns true.
 template <int D, int NS>
-__device__ __attribute__((noinline)) bool rescore_select(const float *srow, const uint16_t *list, int nc,
-                                                         int n_take, float cb, const float *skn,
+__device__ __attribute__((noinline)) bool rescore_select(const float *srow, const uint16_t *list, int lo,
+                                                         int nc, int n_take, float cb, const float *skn,
                                                          const uint16_t *vec, float *pv, const uint16_t *kbase,
                                                          uint16_t *lout, int32_t *gout, int len, int32_t *diag) {
   const int l = lane_id();
@@ -635,7 +644,7 @@ __device__ __attribute__((noinline)) bool rescore_select(const float *srow, cons
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int pos = s * 64 + l;
-    valid[s] = pos < nc;
+    valid[s] = pos >= lo && pos < nc;
     cj[s] = valid[s] ? (list ? (int)list[pos] : pos) : 0;
     sc[s] = valid[s] ? (double)srow[pos] : 0.0;
     dl[s] = valid[s] ? (double)fmaf(cb, skn[cj[s]], kAbsBound) : 0.0;
@@ -669,12 +678,13 @@ __device__ __attribute__((noinline)) bool rescore_select(const float *srow, cons
   return true;
 }
 
-// Exact tier for one row: select_row over the candidates (list: block ids in
-// LDS, or nullptr for 0..nc-1), written like write_sorted_lds.
+// Exact tier for one row: select_row over the candidates (list: nc block
+// ids in LDS, or nullptr for base .. base+nc-1), written like
+// write_sorted_lds.
 template <int D, int NS>
 __device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_t *kbase, const uint16_t *list,
-                                                       int nc, int n_take, const uint16_t *vec, uint16_t *lout,
-                                                       int32_t *gout, int len, int32_t *diag) {
+                                                       int base, int nc, int n_take, const uint16_t *vec,
+                                                       uint16_t *lout, int32_t *gout, int len, int32_t *diag) {
   const int l = lane_id();
   if (list)
     for (int c = l; c < nc; c += 64) sh.clist[c] = list[c];
@@ -686,7 +696,7 @@ __device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_
   wave_lds_sync();
   bool sel[NS];
   int cj[NS];
-  select_row<uint16_t, D, NS>(sh, kbase, list ? sh.clist : nullptr, nc, n_take, sel, cj, diag);
+  select_row<uint16_t, D, NS>(sh, kbase, list ? sh.clist : nullptr, base, nc, n_take, sel, cj, diag);
   write_sorted_lds<NS>(sel, cj, lout, gout, len);
   if (diag && l == 0) atomicAdd(&diag[2], 1);
   wave_lds_sync();
@@ -792,14 +802,15 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
     for (int pl = w; pl < kPX; pl += kPW) {
       int h, gm, nc;
       if (!proxy(pl, h, gm, nc)) continue;
-      const int C = min(dm.n_cand, nc);
+      const int c0 = min(dm.sink, nc);   // sink blocks are no candidates of the list
+      const int C = min(dm.n_cand, nc - c0);
       int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
       uint16_t *lout = LIST + pl * kPCap;
       if (diag && l == 0) atomicAdd(&diag[0], 1);
-      if (C >= nc) {   // every candidate
-        for (int c = l; c < nc; c += 64) lout[c] = (uint16_t)c;
+      if (C >= nc - c0) {   // every candidate
+        for (int c = l; c < C; c += 64) lout[c] = (uint16_t)(c0 + c);
         if (gout)
-          for (int c = l; c < dm.n_cand; c += 64) gout[c] = c < nc ? c : -1;
+          for (int c = l; c < dm.n_cand; c += 64) gout[c] = c < C ? c0 + c : -1;
         continue;
       }
       const float cb = kG * SPN[pl];
@@ -808,7 +819,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       bool valid[NS], sel[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        valid[s] = cid[s] < nc;
+        valid[s] = cid[s] < nc && cid[s] >= c0;
         sc[s] = (s < nsl && valid[s]) ? S[pl * LY::SLD + cid[s]] : 0.f;
         dl[s] = fmaf(cb, skr[s], kAbsBound);
       }
@@ -816,7 +827,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         write_sorted_lds<NS>(sel, cid, lout, gout, dm.n_cand);
       } else {
         const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
-        if (!rescore_select<D, NS>(S + pl * LY::SLD, nullptr, nc, C, cb, SKN, vec, PVw, kbase, lout, gout,
+        if (!rescore_select<D, NS>(S + pl * LY::SLD, nullptr, c0, nc, C, cb, SKN, vec, PVw, kbase, lout, gout,
                                    dm.n_cand, diag) &&
             l == 0)
           defp[atomicAdd(&defn[0], 1)] = pl;
@@ -830,29 +841,41 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       const int pl = defp[q];
       int h, gm, nc;
       proxy(pl, h, gm, nc);
-      const int C = min(dm.n_cand, nc);
+      const int c0 = min(dm.sink, nc);
+      const int C = min(dm.n_cand, nc - c0);
       int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
-      exact_select<D, kMaxSlots>(sh, kbase, nullptr, nc, C, qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D,
-                                 LIST + pl * kPCap, gout, dm.n_cand, diag);
+      exact_select<D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C,
+                                 qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D, LIST + pl * kPCap, gout,
+                                 dm.n_cand, diag);
     }
   }
   __syncthreads();
-  if (dm.topk == 0) return;
+  if (dm.klist == 0) return;
 
-  // ---- 3. members: top-k of the proxy's list
+  // ---- 3. members: their sinks, then the top-k of the proxy's list
+  // member t's row: sink blocks 0 .. ct-1, then ascending selected ids
+  auto member_row = [&](size_t qrow0, int t, int &ct) -> int32_t * {
+    int own, lo;
+    ct = min(dm.sink, pisa_row_geometry(dm, t, &own, &lo));
+    int32_t *out = idx + (qrow0 + t) * dm.klist;
+    for (int c = l; c < ct; c += 64) out[c] = c;
+    return out + ct;
+  };
   float *Mw = S + w * kPM * LY::MLD;
   for (int pl = w; pl < kPX; pl += kPW) {
     int h, gm, nc;
     if (!proxy(pl, h, gm, nc)) continue;
-    const int C = min(dm.n_cand, nc);
+    const int C = min(dm.n_cand, nc - min(dm.sink, nc));
     const int n_take = min(dm.topk, C);
     const uint16_t *list = LIST + pl * kPCap;
     const int t0 = gm * g, t1 = min(dm.L, t0 + g);
     const size_t qrow0 = (size_t)(b * dm.Hq + h) * dm.L;
-    if (n_take >= C) {   // the whole list
+    if (n_take == 0 || n_take >= C) {   // nothing to choose: none, or the whole list
+      const int m = n_take == 0 ? 0 : C;
       for (int t = t0; t < t1; ++t) {
-        int32_t *out = idx + (qrow0 + t) * dm.topk;
-        for (int c = l; c < dm.topk; c += 64) out[c] = c < C ? (int32_t)list[c] : -1;
+        int ct;
+        int32_t *out = member_row(qrow0, t, ct);
+        for (int c = l; c < dm.klist - ct; c += 64) out[c] = c < m ? (int32_t)list[c] : -1;
         if (diag && l == 0) atomicAdd(&diag[0], 1);
       }
       continue;
@@ -916,11 +939,12 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
           sc[s] = valid[s] ? Mw[m * LY::MLD + s * 64 + l] : 0.f;
           dl[s] = fmaf(cb, skm[s], kAbsBound);
         }
-        int32_t *out = idx + (qrow0 + t) * dm.topk;
+        int ct;
+        int32_t *out = member_row(qrow0, t, ct);
         if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel)) {
-          write_sorted_lds<NS>(sel, cj, nullptr, out, dm.topk);
-        } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, C, n_take, cb, SKN, Q + (qrow0 + t) * D, PVw,
-                                          kbase, nullptr, out, dm.topk, diag) &&
+          write_sorted_lds<NS>(sel, cj, nullptr, out, dm.klist - ct);
+        } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, 0, C, n_take, cb, SKN, Q + (qrow0 + t) * D,
+                                          PVw, kbase, nullptr, out, dm.klist - ct, diag) &&
                    l == 0) {
           defm[atomicAdd(&defn[1], 1)] = t * 64 + pl;
         }
@@ -935,11 +959,13 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       const int t = defm[q] >> 6, pl = defm[q] & 63;
       int h, gm, nc;
       proxy(pl, h, gm, nc);
-      const int C = min(dm.n_cand, nc);
+      const int C = min(dm.n_cand, nc - min(dm.sink, nc));
       const int n_take = min(dm.topk, C);
       const size_t row = (size_t)(b * dm.Hq + h) * dm.L + t;
-      exact_select<D, kPCap / 64>(sh, kbase, LIST + pl * kPCap, C, n_take, Q + row * D, nullptr,
-                                  idx + row * dm.topk, dm.topk, diag);
+      int own, lo;
+      const int ct = min(dm.sink, pisa_row_geometry(dm, t, &own, &lo));
+      exact_select<D, kPCap / 64>(sh, kbase, LIST + pl * kPCap, 0, C, n_take, Q + row * D, nullptr,
+                                  idx + row * dm.klist + ct, dm.klist - ct, diag);
     }
   }
 }

@@ -49,7 +49,10 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
   if (p->taylor < PISA_TAYLOR_NONE || p->taylor > PISA_TAYLOR_HYBRID)
     return fail(PISA_E_ARG, "unknown taylor mode %d", p->taylor);
   if (p->topk < 0) return fail(PISA_E_ARG, "topk must be >= 0");
+  if (p->sink < 0) return fail(PISA_E_ARG, "sink must be >= 0");
   if (p->topk > kMaxTopk) return fail(PISA_E_UNSUPPORTED, "topk %d > %d", p->topk, kMaxTopk);
+  if (p->topk + p->sink > kMaxTopk)
+    return fail(PISA_E_UNSUPPORTED, "topk + sink = %d > %d", p->topk + p->sink, kMaxTopk);
   if (p->window < 0) return fail(PISA_E_ARG, "window must be >= 0");
   if (p->window > 0 && !p->causal)
     return fail(PISA_E_UNSUPPORTED, "a sliding window needs causal attention");
@@ -62,8 +65,8 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
     if (p->n_cand > kMaxCand) return fail(PISA_E_UNSUPPORTED, "n_cand %d > %d", p->n_cand, kMaxCand);
   }
   if (!std::isfinite(p->scale)) return fail(PISA_E_ARG, "scale is not finite");
-  if (!p->causal && p->topk == 0 && p->taylor == PISA_TAYLOR_NONE)
-    return fail(PISA_E_ARG, "non-causal with topk = 0 and no Taylor term attends to nothing");
+  if (!p->causal && p->topk == 0 && p->sink == 0 && p->taylor == PISA_TAYLOR_NONE)
+    return fail(PISA_E_ARG, "non-causal with topk = 0, no sinks and no Taylor term attends to nothing");
   const long long n_blk = (p->L + (long long)p->block - 1) / p->block;
   if (n_blk > kMaxBlocks) return fail(PISA_E_UNSUPPORTED, "%lld blocks > %d", n_blk, kMaxBlocks);
   const double elems = (double)p->B * p->Hq * p->L * p->d;
@@ -75,6 +78,8 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
   dm->n_sel = p->group >= 1 ? (p->L + p->group - 1) / p->group : (int)n_blk;
   dm->n_rows = p->group >= 1 ? p->L : (int)n_blk;
   dm->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+  dm->sink = p->sink;
+  dm->klist = p->topk + p->sink;
   return PISA_OK;
 }
 
@@ -145,7 +150,7 @@ pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]) {
   PisaDims dm;
   PISA_TRY(make_dims(p, &dm));
   if (!bytes) return fail(PISA_E_ARG, "bytes is NULL");
-  bytes[0] = (size_t)dm.B * dm.Hq * dm.n_rows * dm.topk * sizeof(int32_t);
+  bytes[0] = (size_t)dm.B * dm.Hq * dm.n_rows * dm.klist * sizeof(int32_t);
   bytes[1] = dm.group >= 1 ? (size_t)dm.B * dm.Hq * dm.n_sel * dm.n_cand * sizeof(int32_t) : 0;
   return PISA_OK;
 }
@@ -190,7 +195,7 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
   if (!stats) return fail(PISA_E_ARG, "stats is NULL");
   PISA_TRY(check_ptr(stats->qsel, "stats.qsel", true));
   PISA_TRY(check_ptr(stats->ksel, "stats.ksel", true));
-  PISA_TRY(check_ptr(idx, "idx", dm.topk > 0));
+  PISA_TRY(check_ptr(idx, "idx", dm.klist > 0));
   PISA_TRY(check_ptr(cand, "cand", false));
   PISA_TRY(check_ws(ws, ws_bytes, 0));
   int32_t *diag = nullptr;
@@ -198,7 +203,7 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
     if (!aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
     diag = static_cast<int32_t *>(ws);
   }
-  if (dm.topk == 0 && !(dm.group >= 1 && cand)) return PISA_OK;  // nothing to select or write
+  if (dm.klist == 0 && !(dm.group >= 1 && cand)) return PISA_OK;  // nothing to select or write
   return launched(launch_indexer(dm, Q, stats->qsel, stats->ksel, idx, cand, diag, stream),
                   "indexer_topk");
 }
@@ -213,7 +218,7 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
   PISA_TRY(check_ptr(V, "V", true));
   PISA_TRY(check_ptr(O, "O", true));
   PISA_TRY(check_ptr(lse, "lse", false));
-  PISA_TRY(check_ptr(idx, "idx", dm.topk > 0));
+  PISA_TRY(check_ptr(idx, "idx", dm.klist > 0));
   const bool ty = dm.taylor != PISA_TAYLOR_NONE;
   if (ty) {
     if (!stats) return fail(PISA_E_ARG, "stats is NULL but taylor != NONE");
@@ -222,6 +227,7 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
     PISA_TRY(check_ptr(stats->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
   }
   PISA_TRY(check_ws(ws, ws_bytes, 0));
+  dm.topk = dm.klist;   // the attention kernels take topk as the width of a kept list
   return launched(launch_attn(dm, Q, K, V, ty ? stats->kbar : nullptr, ty ? stats->vsum : nullptr,
                               ty ? stats->HT : nullptr, idx, O, lse, stream),
                   "sparse_attn_fwd");

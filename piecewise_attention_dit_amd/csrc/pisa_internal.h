@@ -22,6 +22,8 @@ struct PisaDims {
   int n_sel;       // rows of qsel
   int n_rows;      // rows of idx
   float scale;     // softmax scale (resolved)
+  int sink;        // leading candidate blocks always kept
+  int klist;       // entries of an idx row: topk + sink
 };
 
 // Selection-row geometry shared by the indexer and the attention kernels.

@@ -25,7 +25,7 @@ class Params(ctypes.Structure):
                 ("L", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("n_cand", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("taylor", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("taylor", ctypes.c_int32), ("scale", ctypes.c_float), ("sink", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -82,10 +82,10 @@ def _check(status: int):
 
 
 def make_params(B, Hq, Hkv, L, d, dtype="bf16", block=64, topk=0, window=0, group=0, n_cand=0,
-                causal=False, taylor="order1", scale=0.0) -> Params:
+                causal=False, taylor="order1", scale=0.0, sink=0) -> Params:
     return Params(B, Hq, Hkv, L, d, DTYPES[dtype] if isinstance(dtype, str) else int(dtype), block,
                   topk, window, group, n_cand, int(bool(causal)),
-                  TAYLOR[taylor] if isinstance(taylor, str) else int(taylor), float(scale))
+                  TAYLOR[taylor] if isinstance(taylor, str) else int(taylor), float(scale), int(sink))
 
 
 def validate(p: Params) -> None:
@@ -161,7 +161,7 @@ def block_stats(p: Params, q, k, v, stats=None, ws=None, stream=None) -> dict:
 
 def alloc_index(p: Params, device="cuda"):
     n_rows = p.L if p.group >= 1 else -(-p.L // p.block)
-    idx = torch.empty((p.B, p.Hq, n_rows, p.topk), dtype=torch.int32, device=device)
+    idx = torch.empty((p.B, p.Hq, n_rows, p.topk + p.sink), dtype=torch.int32, device=device)
     cand = None
     if p.group >= 1:
         cand = torch.empty((p.B, p.Hq, -(-p.L // p.group), p.n_cand), dtype=torch.int32, device=device)
@@ -194,12 +194,13 @@ def sparse_attn_fwd(p: Params, q, k, v, stats: dict, idx, out=None, lse=None, wa
 
 
 def attention(q, k, v, *, block=64, topk=0, window=0, group=0, n_cand=0, causal=False,
-              taylor="order1", scale=0.0, return_all=False):
+              taylor="order1", scale=0.0, sink=0, return_all=False):
     """Drop-in forward: (Q, K, V) -> O, running the three library calls."""
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     dtype = "bf16" if q.dtype == torch.bfloat16 else "f32"
-    p = make_params(B, Hq, Hkv, L, d, dtype, block, topk, window, group, n_cand, causal, taylor, scale)
+    p = make_params(B, Hq, Hkv, L, d, dtype, block, topk, window, group, n_cand, causal, taylor, scale,
+                    sink)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != _tdtype(p):
             raise ValueError(f"{name} must be a contiguous {_tdtype(p)} CUDA tensor")

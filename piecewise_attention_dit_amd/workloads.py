@@ -44,7 +44,8 @@ class Workload:
     group: int = 0        # 0 = block rows; g >= 1 = PIVOT proxies of g tokens
     n_cand: int = 0       # PIVOT proxy candidate list length C
     causal: bool = False
-    taylor: str = "order1"  # "none" | "order0" | "order1"
+    taylor: str = "order1"  # "none" | "order0" | "order1" | "hybrid"
+    sink: int = 0           # leading key blocks always kept (attention sinks)
     recipe: str = "gauss"   # input recipe, see make_inputs
     grid: tuple = ()        # spatial grid (row-major token order) for field recipes
     seed: int = 0
@@ -61,7 +62,7 @@ class Workload:
         return dict(B=self.B, Hq=self.Hq, Hkv=self.Hkv, L=self.L, d=self.d,
                     dtype=self.dtype, block=self.block, topk=self.topk,
                     window=self.window, group=self.group, n_cand=self.n_cand,
-                    causal=self.causal, taylor=self.taylor)
+                    causal=self.causal, taylor=self.taylor, sink=self.sink)
 
 
 # The five headline workloads.  "keep rho" is resolved as k = round(rho * n_blk)
@@ -129,6 +130,14 @@ PARITY_CASES = {
     "llm_pivot_s_hyb": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_hyb", Hq=4, Hkv=2,
                                                       L=1024 + 40, topk=4, n_cand=8,
                                                       taylor="hybrid"),
+    # attention sinks: block-row and PIVOT indexers, every attention kernel
+    "llm_swa_s_sink": WORKLOADS["llm_swa"].replace(name="llm_swa_s_sink", B=1, Hq=8, Hkv=2,
+                                                   L=2048 + 24, window=384, topk=4, sink=2),
+    "llm_pivot_s_sink": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_sink", Hq=8, Hkv=2,
+                                                       L=2048 + 40, topk=6, n_cand=12, sink=2),
+    "video_dit_s_sink": WORKLOADS["video_dit"].replace(name="video_dit_s_sink", Hq=2, Hkv=2,
+                                                       L=1000, grid=(1, 20, 50), topk=2, sink=1,
+                                                       taylor="hybrid"),
 }
 
 

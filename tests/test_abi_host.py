@@ -57,6 +57,8 @@ def _p(**kw):
     (dict(block=32), pisa.PISA_E_UNSUPPORTED),
     (dict(dtype=7), pisa.PISA_E_ARG),
     (dict(taylor=5), pisa.PISA_E_ARG),
+    (dict(sink=-1), pisa.PISA_E_ARG),
+    (dict(topk=40, sink=25), pisa.PISA_E_UNSUPPORTED),
     (dict(topk=-1), pisa.PISA_E_ARG),
     (dict(topk=65), pisa.PISA_E_UNSUPPORTED),
     (dict(window=64, causal=False), pisa.PISA_E_UNSUPPORTED),
@@ -80,6 +82,7 @@ def test_layouts():
     assert sizes == [1 * 4 * n_blk * 128 * 2, 1 * 2 * n_blk * 128 * 2, 2 * n_blk * 128 * 4,
                      2 * n_blk * 128 * 4, 2 * n_blk * 128 * 128 * 2]
     assert pisa.index_layout(p) == [1 * 4 * n_blk * 4 * 4, 0]
+    assert pisa.index_layout(_p(L=1000, sink=3)) == [1 * 4 * n_blk * (4 + 3) * 4, 0]
     q = _p(L=1000, group=8, n_cand=16, causal=True, dtype="f32")
     sz = pisa.stats_layout(q)
     assert sz[0] == 4 * 125 * 128 * 4 and sz[4] == 2 * n_blk * 128 * 128 * 4

@@ -49,6 +49,12 @@ def test_parity_cases(name):
     dict(L=700, block=64, topk=0, taylor="hybrid"),               # hybrid, all blocks Taylor
     dict(L=777, block=128, topk=1, d=64, taylor="hybrid"),        # hybrid, d 64 with 128-blocks
     dict(L=300, block=128, topk=1, d=128, taylor="hybrid", dtype="f32"),
+    dict(L=700, block=64, topk=0, sink=2, causal=True, window=130, taylor="order0"),  # sinks only
+    dict(L=600, block=64, topk=2, d=64, dtype="f32", causal=True, window=100, sink=2),
+    dict(L=500, block=64, topk=2, d=64, group=4, n_cand=5, dtype="f32", causal=True, sink=3,
+         taylor="none"),
+    dict(L=900, block=64, topk=3, group=4, n_cand=6, causal=True, window=150, sink=20,
+         taylor="order1"),                                        # sinks beyond most rows' reach
 ])
 def test_edge_cases(kw):
     base = dict(B=1, Hq=2, Hkv=2, L=256, d=128, dtype="bf16", block=64, topk=2, window=0, group=0,
