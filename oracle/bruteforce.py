@@ -15,7 +15,8 @@ matrices over all blocks); the PIVOT page's steps 1-4 (proxy =
 mean of g consecutive queries, candidates re-ranked per member); the Sliding
 Window Attention page's causal mask 0 <= t - s < w, and its attention sinks
 (the first blocks of the sequence kept beside the window; the top-k is chosen
-among the other candidates).
+among the other candidates); covariance-aware routing adds route_lambda times
+the Frobenius norm of H_j - Hbar to every selection score.
 """
 from __future__ import annotations
 
@@ -78,6 +79,9 @@ def run(q, k, v, P):
                             for e in range(d)] for c in range(d)])
 
             Hbar = [[sum(Hm[j][c][e] for j in range(nb)) / nb for e in range(d)] for c in range(d)]
+            lam = getattr(P, "route_lambda", 0.0)
+            Mcov = [math.sqrt(math.fsum((Hm[j][c][e] - Hbar[c][e]) ** 2 for c in range(d) for e in range(d)))
+                    for j in range(nb)]
 
             def geometry(start):
                 own = start // bs
@@ -93,6 +97,8 @@ def run(q, k, v, P):
                 keyed = []
                 for j in cands:
                     ex = sum((Fraction(pvec[c]) * Fraction(ks[j][c]) for c in range(d)), Fraction(0))
+                    if lam > 0:
+                        ex += Fraction(float(lam) * Mcov[j])
                     keyed.append((-ex, j))
                 keyed.sort()
                 return sorted(j for _, j in keyed[:n])

@@ -33,6 +33,11 @@ The definition implemented (notation of the PISA page):
     blocks that are candidates of a row are always kept exactly; the row's
     top-k is chosen among its other candidates, and its kept list holds the
     sink blocks followed by the top-k (width k + s).
+  * Covariance-aware routing ([PISA] section 2, covariance-aware routing):
+    with route_lambda = lam > 0 a block's selection score is the attention
+    score plus lam * M_j, M_j = ||H_j - Hbar|| (Frobenius; the rule that
+    combines the two and the weight are not given on the pages: the sum with
+    a caller's weight is the reading taken), at every selection stage.
   * Hybrid order ([PISA] section 2, the global first-order correction): zero
     order per non-kept block plus scale q_t Hbar sum_{j in U} alpha_{t,j} in
     N_t, Hbar = the mean of H_j over all blocks of the (batch, KV head).
@@ -69,6 +74,7 @@ class Problem:
     taylor: str = "order1"
     scale: float = 0.0       # <= 0 -> 1/sqrt(d)
     sink: int = 0            # leading key blocks always kept (attention sinks)
+    route_lambda: float = 0.0  # covariance-aware routing weight (0: attention score only)
 
     @property
     def sm_scale(self) -> float:
@@ -193,7 +199,9 @@ def block_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: Problem) -> dict
         qsel[:, :, r] = pooled_mean(q[:, :, r * span:min(L, (r + 1) * span), :], 2, P.dtype)
     qsel = rne(qsel, P.dtype)
     Hbar = H.mean(axis=2)
-    return dict(n=n, kbar=kbar, ksel=ksel, vsum=vsum, H=H, Hbar=Hbar, qsel=qsel)
+    # covariance norm of each block against the mean ([PISA] covariance-aware routing)
+    M = np.sqrt(((H - Hbar[:, :, None]) ** 2).sum(axis=(-2, -1)))
+    return dict(n=n, kbar=kbar, ksel=ksel, vsum=vsum, H=H, Hbar=Hbar, M=M, qsel=qsel)
 
 
 # ----------------------------------------------------------------------------
@@ -235,21 +243,23 @@ def exact_score(p: np.ndarray, kv: np.ndarray) -> Fraction:
     return sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(p, kv)), Fraction(0))
 
 
-def top_n(p: np.ndarray, K: np.ndarray, ids: np.ndarray, n: int) -> np.ndarray:
-    """The n best of candidates ``ids`` (rows of K) by exact real score p.K[j],
-    ties to the lower id; returned ascending.
+def top_n(p: np.ndarray, K: np.ndarray, ids: np.ndarray, n: int, bias=None) -> np.ndarray:
+    """The n best of candidates ``ids`` (rows of K) by exact real score
+    p.K[j] (+ bias[j], a float64 per candidate), ties to the lower id;
+    returned ascending.
 
     Float64 scores order the candidates; any boundary decision closer than
-    1e-12 * sum|p_c K_jc| (far above the float64 dot-product error) is re-made
-    with exact rational scores."""
+    1e-12 * (sum|p_c K_jc| + |bias_j|) (far above the float64 error) is
+    re-made with exact rational scores."""
     ids = np.asarray(ids)
     m = len(ids)
     if n >= m:
         return np.sort(ids)
     if n <= 0:
         return ids[:0]
-    s = K @ p
-    band = 1e-12 * (np.abs(K) @ np.abs(p)) + 1e-300
+    b = np.zeros(m) if bias is None else np.asarray(bias, dtype=np.float64)
+    s = K @ p + b
+    band = 1e-12 * (np.abs(K) @ np.abs(p) + np.abs(b)) + 1e-300
     order = np.lexsort((ids, -s))
     sel, rest = order[:n], order[n:]
     t_in = (s[sel] - band[sel]).min()
@@ -260,7 +270,7 @@ def top_n(p: np.ndarray, K: np.ndarray, ids: np.ndarray, n: int) -> np.ndarray:
     amb_rest = rest[s[rest] + band[rest] >= t_in]
     sure = np.setdiff1d(sel, amb_sel)
     amb = np.concatenate([amb_sel, amb_rest])
-    ex = [(exact_score(p, K[a]), -int(ids[a]), a) for a in amb]
+    ex = [(exact_score(p, K[a]) + Fraction(float(b[a])), -int(ids[a]), a) for a in amb]
     ex.sort(reverse=True)
     need = n - len(sure)
     chosen = np.array([a for _, _, a in ex[:need]], dtype=np.int64)
@@ -287,25 +297,28 @@ def select(q: np.ndarray, st: dict, P: Problem):
         C = P.n_cand
         ng = P.n_sel
         cand = np.full((B, Hq, ng, C), -1, dtype=np.int64)
+    lam = float(np.float32(P.route_lambda))
     for b in range(B):
         for h in range(Hq):
             hk = h * Hkv // Hq
             Kb = ksel[b, hk]
+            # covariance-aware routing: lam * M_j added at every selection stage
+            bias = lam * st["M"][b, hk] if lam > 0 else np.zeros(P.n_blk)
             if not P.pivot:
                 for r in range(P.n_rows):
                     nc = row_geometry(P, r)[2]
                     c0 = sink_count(P, nc)
-                    t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k)
+                    t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k, bias[c0:nc])
                     idx[b, h, r, :c0 + len(t)] = np.concatenate([np.arange(c0), t])
             else:
                 for gm in range(P.n_sel):
                     nc = group_candidates(P, gm)
                     c0 = sink_count(P, nc)
-                    cl = top_n(qsel[b, h, gm], Kb[c0:nc], np.arange(c0, nc), C)
+                    cl = top_n(qsel[b, h, gm], Kb[c0:nc], np.arange(c0, nc), C, bias[c0:nc])
                     cand[b, h, gm, :len(cl)] = cl
                     for t in range(gm * P.group, min(P.L, (gm + 1) * P.group)):
                         ct = sink_count(P, row_geometry(P, t)[2])
-                        tt = top_n(q[b, h, t], Kb[cl], cl, k)
+                        tt = top_n(q[b, h, t], Kb[cl], cl, k, bias[cl])
                         idx[b, h, t, :ct + len(tt)] = np.concatenate([np.arange(ct), tt])
     return idx, cand
 

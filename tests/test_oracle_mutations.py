@@ -175,8 +175,29 @@ def check_sinks(m):
     return ok and row[:3].tolist() == [0, 1, 2] and (row[3:] >= 3).all() and len(set(row.tolist())) == 5
 
 
+def check_routing(m):
+    """Equal attention scores, closed-form covariance norms (see the pins):
+    routing keeps the blocks farthest from the mean first-order matrix, at
+    the proxy and at the member stage."""
+    nb, bs, d = 8, 8, 8
+    a = np.array([0.5, 3.0, -1.0, 2.0, 0.0, 4.0, 1.0, -2.0])
+    u, w, c = np.zeros(d), np.zeros(d), np.zeros(d)
+    u[1], u[2], w[0], w[3], c[4] = 1.0, 2.0, 1.0, -1.0, 0.5
+    e = np.array([1.0, -1.0] * (bs // 2))
+    k = (c + (a[:, None] * e[None, :])[:, :, None] * u).reshape(1, 1, nb * bs, d)
+    v = (e[None, :, None] * w + 0.25).repeat(nb, axis=0).reshape(1, 1, nb * bs, d)
+    q = _rand((1, 1, nb * bs, d), 22, scale=0.3)
+    ok = True
+    for extra in (dict(), dict(group=4, n_cand=5)):
+        P = m.Problem(B=1, Hq=1, Hkv=1, L=nb * bs, d=d, dtype="f32", block=bs, topk=3, taylor="order1",
+                      route_lambda=0.5, **extra)
+        r = m.run(q, k, v, P)
+        ok &= all(r["idx"][0, 0, i].tolist() == [1, 5, 7] for i in range(r["idx"].shape[2]))
+    return ok
+
+
 CHECKS = [check_pivot_mean, check_swa_count, check_dense, check_constant_v, check_orders, check_ties,
-          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks]
+          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks, check_routing]
 
 MUTATIONS = {
     "H transposed": ('H[:, :, j] = np.einsum("bhnc,bhne->bhce", kc, vj)',
@@ -196,18 +217,23 @@ MUTATIONS = {
                      "hk = h % P.Hkv\n    sc = P.sm_scale"),
     "proxy is first member": ("qsel[:, :, r] = pooled_mean(q[:, :, r * span:min(L, (r + 1) * span), :], 2, P.dtype)",
                               "qsel[:, :, r] = q[:, :, r * span, :]"),
-    "pivot members ignore proxy list": ("tt = top_n(q[b, h, t], Kb[cl], cl, k)",
-                                        "tt = top_n(q[b, h, t], Kb[:nc], np.arange(nc), k)"),
+    "pivot members ignore proxy list": ("tt = top_n(q[b, h, t], Kb[cl], cl, k, bias[cl])",
+                                        "tt = top_n(q[b, h, t], Kb[:nc], np.arange(nc), k, bias[:nc])"),
     "hybrid Hbar is the sum": ("Hbar = H.mean(axis=2)", "Hbar = H.sum(axis=2)"),
     "hybrid Hbar over the tail only": ('(qt @ st["Hbar"][b, hk])', '(qt @ st["H"][b, hk, Uj].mean(axis=0))'),
     "hybrid Hbar transposed": ('(qt @ st["Hbar"][b, hk])', '(qt @ st["Hbar"][b, hk].T)'),
     "hybrid term without scale": ('N = N + sc * (qt @ st["Hbar"]', 'N = N + 1.0 * (qt @ st["Hbar"]'),
     "hybrid weights include exact terms": ('* pa.sum(axis=1)[:, None]',
                                            '* (pa.sum(axis=1) + px.sum(axis=1))[:, None]'),
-    "sinks take top-k places": ("t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k)",
-                                "t = top_n(qsel[b, h, r], Kb[:nc], np.arange(nc), k)[:max(0, k - c0)]"),
+    "sinks take top-k places": ("t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k, bias[c0:nc])",
+                                "t = top_n(qsel[b, h, r], Kb[:nc], np.arange(nc), k, bias[:nc])[:max(0, k - c0)]"),
     "sinks not kept": ("idx[b, h, r, :c0 + len(t)] = np.concatenate([np.arange(c0), t])",
                        "idx[b, h, r, :len(t)] = t"),
+    "routing bias subtracted": ("bias = lam * st[\"M\"][b, hk] if lam > 0", "bias = -lam * st[\"M\"][b, hk] if lam > 0"),
+    "routing norm not centred": ("M = np.sqrt(((H - Hbar[:, :, None]) ** 2).sum(axis=(-2, -1)))",
+                                 "M = np.sqrt((H ** 2).sum(axis=(-2, -1)))"),
+    "routing skipped for members": ("tt = top_n(q[b, h, t], Kb[cl], cl, k, bias[cl])",
+                                    "tt = top_n(q[b, h, t], Kb[cl], cl, k)"),
     "scale not applied to exact logits": ("x = sc * (qt @ k[b, hk, keys].T)", "x = (qt @ k[b, hk, keys].T)"),
 }
 

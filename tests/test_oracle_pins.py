@@ -325,6 +325,10 @@ BRUTE_CASES = [
     dict(Hq=2, Hkv=2, L=40, block=8, topk=1, causal=False, sink=1, taylor="hybrid", dtype="f32"),
     dict(Hq=2, Hkv=1, L=48, block=4, topk=2, group=2, n_cand=3, causal=True, window=6, sink=2,
          taylor="order0", dtype="bf16"),
+    dict(Hq=2, Hkv=1, L=40, block=4, topk=2, causal=False, route_lambda=0.05, taylor="order1",
+         dtype="f32"),
+    dict(Hq=2, Hkv=1, L=44, block=4, topk=2, group=2, n_cand=4, causal=True, window=5,
+         route_lambda=0.02, taylor="hybrid", dtype="bf16"),
 ]
 
 
@@ -499,6 +503,56 @@ def test_p14_sinks_do_not_use_the_topk_budget(pivot):
             if nc > 10:
                 got = r["idx"][0, 0, row]
                 assert got[got >= 0].tolist() == want, (sink, row, got)
+
+
+# ---------------------------------------------------------------------------
+# P15: covariance-aware routing.  Block j holds keys c + a_j e_n u and values
+# e_n w + v0 with e_n = +1, -1, +1, ... (sum zero over the block), so its
+# mean key is c, H_j = n a_j u w^T, Hbar = n abar u w^T and
+# ||H_j - Hbar||_F = n |a_j - abar| |u| |w| in closed form.  Every block then
+# has the same attention score (equal pooled keys), so without routing the
+# ties keep the lowest blocks and with any positive weight the largest
+# |a_j - abar| win.
+
+_A = [0.5, 3.0, -1.0, 2.0, 0.0, 4.0, 1.0, -2.0]
+
+
+def _routing_inputs(nb=8, bs=8, d=8, Hq=2):
+    L = nb * bs
+    u = np.zeros(d)
+    u[1], u[2] = 1.0, 2.0
+    w = np.zeros(d)
+    w[0], w[3] = 1.0, -1.0
+    c = np.zeros(d)
+    c[4] = 0.5
+    e = np.array([1.0, -1.0] * (bs // 2))
+    a = np.array(_A[:nb])
+    k = (c[None, None, :] + (a[:, None] * e[None, :])[:, :, None] * u[None, None, :]).reshape(1, 1, L, d)
+    v = (e[None, :, None] * w[None, None, :] + 0.25).repeat(nb, axis=0).reshape(1, 1, L, d)
+    q = _rand((1, Hq, L, d), 151, scale=0.3)
+    return q, k, v, a, np.linalg.norm(u) * np.linalg.norm(w) * bs
+
+
+def test_p15_covariance_norm_closed_form():
+    q, k, v, a, unit = _routing_inputs()
+    P = po.Problem(B=1, Hq=2, Hkv=1, L=64, d=8, dtype="f32", block=8, topk=3, taylor="order1")
+    st = po.block_stats(q, k, v, P)
+    np.testing.assert_allclose(st["M"][0, 0], unit * np.abs(a - a.mean()), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("pivot", [False, True])
+def test_p15_routing_prefers_high_covariance(pivot):
+    q, k, v, a, _ = _routing_inputs()
+    kw = dict(B=1, Hq=2, Hkv=1, L=64, d=8, dtype="f32", block=8, topk=3, taylor="order1")
+    if pivot:
+        kw.update(group=4, n_cand=5)
+    dev = np.abs(a - a.mean())
+    by_cov = sorted(sorted(range(8), key=lambda j: (-dev[j], j))[:3])     # [1, 5, 7]
+    for lam, want in ((0.0, [0, 1, 2]), (1e-3, by_cov), (1e3, by_cov)):
+        r = po.run(q, k, v, po.Problem(route_lambda=lam, **kw))
+        for h in range(2):
+            for row in range(r["idx"].shape[2]):
+                assert r["idx"][0, h, row].tolist() == want, (lam, h, row)
 
 
 # ---------------------------------------------------------------------------
