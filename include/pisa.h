@@ -100,6 +100,10 @@ typedef struct {
                        |cand_r|) candidate blocks of every row are always kept
                        exactly and head its kept list; the top-k is chosen
                        among the other candidates.  topk + sink <= 64. */
+  float route_lambda; /* covariance-aware routing ([PISA] section 2): >= 0;
+                       when > 0 every selection score (block rows, PIVOT
+                       proxies and members) is the attention score plus
+                       route_lambda * mcov_j.  Needs taylor != NONE. */
 } pisa_params;
 
 /* Block statistics ([PISA] precompute; [PIVOT] step 2).  Caller-allocated,
@@ -117,14 +121,19 @@ typedef struct {
  *         the transposed mean of those matrices over the n_blk blocks of the
  *         (b, kv head) (every block, also for causal rows).  Not used by the
  *         other modes.
+ *   mcov  fp32 [B, Hkv, n_blk]: ||H_j - Hbar||_F, the covariance norm of block
+ *         j against the mean first-order matrix ([PISA] covariance-aware
+ *         routing; the pages' norm read as Frobenius), written and read when
+ *         route_lambda > 0
  * kbar and vsum are read only when taylor != NONE, HT only for ORDER1 and
- * HYBRID; they may be NULL otherwise. */
+ * HYBRID, mcov only with routing; they may be NULL otherwise. */
 typedef struct {
   void *qsel;
   void *ksel;
   float *kbar;
   float *vsum;
   void *HT;
+  float *mcov;
 } pisa_stats;
 
 /* ---- host-only queries (no GPU needed) ---------------------------------- */
@@ -132,9 +141,9 @@ typedef struct {
 /* Check a problem statement; PISA_OK if every call can run it. */
 pisa_status pisa_validate(const pisa_params *p);
 
-/* Byte sizes of the five statistics buffers, in pisa_stats field order
- * (qsel, ksel, kbar, vsum, HT). */
-pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]);
+/* Byte sizes of the six statistics buffers, in pisa_stats field order
+ * (qsel, ksel, kbar, vsum, HT, mcov); 0 for a buffer the problem does not use. */
+pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[6]);
 
 /* Byte sizes of the index list idx (int32 [B, Hq, n_rows, topk + sink],
  * n_rows = n_blk for group == 0 else L) and of the PIVOT proxy list cand
@@ -143,9 +152,9 @@ pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]);
 
 /* Workspace bytes call `op` needs (0 = block_stats, 1 = indexer_topk,
  * 2 = sparse_attn_fwd).  block_stats needs one for the HYBRID order with bf16
- * inputs (fp32 partial sums of the mean first-order matrix, 16-byte aligned,
- * contents need not be initialised and are garbage afterwards); every other
- * call and mode needs none.  A non-NULL workspace of at least
+ * inputs and for routing (fp32 partial sums of the mean first-order matrix and
+ * an fp32 copy of it; 16-byte aligned, contents need not be initialised and
+ * are garbage afterwards); every other call and mode needs none.  A non-NULL workspace of at least
  * PISA_DIAG_BYTES passed to pisa_indexer_topk receives diagnostic counters
  * (int32: rows selected, rows whose fast selection was not certified and went
  * to a float64 re-score or an exact comparison, rows or candidates decided by
@@ -158,15 +167,17 @@ pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes);
 
 /* Stage A.  Reads Q, K, V; writes every non-NULL statistics buffer of *out
  * (qsel and ksel are required; kbar and vsum when taylor != NONE, HT for
- * ORDER1 and HYBRID).  ws: at least pisa_workspace_size(p, 0) bytes, else
- * PISA_E_WORKSPACE. */
+ * ORDER1 and HYBRID, mcov with routing).  ws: at least
+ * pisa_workspace_size(p, 0) bytes, else PISA_E_WORKSPACE. */
 pisa_status pisa_block_stats(const pisa_params *p, const void *Q, const void *K,
                              const void *V, const pisa_stats *out, void *ws,
                              size_t ws_bytes, hipStream_t stream);
 
-/* Stage B ([PISA] covariance-free routing by attention score; [PIVOT] steps
- * 1-4; [SWA] window).  Per selection row r the score of candidate block j is
- * the exact real dot product qsel_r . ksel_j (PIVOT members: q_t . ksel_j);
+/* Stage B ([PISA] routing by attention score, covariance-aware with
+ * route_lambda > 0; [PIVOT] steps 1-4; [SWA] window).  Per selection row r
+ * the score of candidate block j is the exact real dot product
+ * qsel_r . ksel_j (PIVOT members: q_t . ksel_j), plus route_lambda * mcov_j
+ * (the product and sum exact, mcov as given in the statistics);
  * the kept set T_r is the top-min(k, |cand_r|) candidates, ties to the lower
  * block index.  Candidates: every block when non-causal; when causal, blocks
  * [0, lo_r) where lo_r = blk(max(0, start_r - w + 1)) (w > 0) or the row's

@@ -44,42 +44,48 @@ PISA_DEV void decompose(float x, uint32_t &m, int &e) {
   e = ex - 24;
 }
 
-// Exact sign of  p . kb - p . ka  (p, kb, ka are fp32 / bf16 values) using a
-// per-lane fixed-point accumulator of kLimbs 32-bit digits held in LDS
+// Exact sign of  (p . kb + lam mb) - (p . ka + lam ma)  (p, kb, ka are fp32 /
+// bf16 values, lam, mb, ma fp32; lam = 0 without routing) using a per-lane
+// fixed-point accumulator of kLimbs 32-bit digits held in LDS
 // (acc[limb * 64 + lane]).
 template <typename T, int D>
-PISA_DEV int exact_cmp(const float *p, const T *kb, const T *ka, int64_t *acc) {
+PISA_DEV int exact_cmp(const float *p, const T *kb, const T *ka, float lam, float mb, float ma, int64_t *acc) {
   const int l = lane_id();
-  bool same = true;
+  bool same = lam == 0.f || mb == ma;
   for (int c = 0; c < D && same; ++c) same = kb[c] == ka[c];
-  if (same) return 0;  // identical pooled keys tie exactly
+  if (same) return 0;  // identical pooled keys (and routing terms) tie exactly
   for (int i = 0; i < kLimbs; ++i) acc[i * 64 + l] = 0;
+  // add (or subtract) the exact product x * y
+  auto add_product = [&](float x, float y, bool sub) {
+    if (x == 0.f || y == 0.f) return;
+    uint32_t mx, my;
+    int ex, ey;
+    decompose(x, mx, ex);
+    decompose(y, my, ey);
+    const bool neg = ((x < 0.f) != (y < 0.f)) != sub;
+    const uint64_t m = (uint64_t)mx * my;     // < 2^48
+    const int b = ex + ey + kExpOffset;       // >= 0
+    const int L = b >> 5, sh = b & 31;
+    const uint64_t lo = m << sh;
+    const uint64_t hi = sh ? (m >> (64 - sh)) : 0;
+    const int64_t p0 = (int64_t)(lo & 0xFFFFFFFFull), p1 = (int64_t)(lo >> 32), p2 = (int64_t)hi;
+    if (neg) {
+      acc[L * 64 + l] -= p0;
+      acc[(L + 1) * 64 + l] -= p1;
+      acc[(L + 2) * 64 + l] -= p2;
+    } else {
+      acc[L * 64 + l] += p0;
+      acc[(L + 1) * 64 + l] += p1;
+      acc[(L + 2) * 64 + l] += p2;
+    }
+  };
   for (int side = 0; side < 2; ++side) {
     const T *kr = side == 0 ? kb : ka;
-    for (int c = 0; c < D; ++c) {
-      const float x = p[c], y = load_elem(kr, c);
-      if (x == 0.f || y == 0.f) continue;
-      uint32_t mx, my;
-      int ex, ey;
-      decompose(x, mx, ex);
-      decompose(y, my, ey);
-      const bool neg = ((x < 0.f) != (y < 0.f)) != (side == 1);
-      const uint64_t m = (uint64_t)mx * my;     // < 2^48
-      const int b = ex + ey + kExpOffset;       // >= 0
-      const int L = b >> 5, sh = b & 31;
-      const uint64_t lo = m << sh;
-      const uint64_t hi = sh ? (m >> (64 - sh)) : 0;
-      const int64_t p0 = (int64_t)(lo & 0xFFFFFFFFull), p1 = (int64_t)(lo >> 32), p2 = (int64_t)hi;
-      if (neg) {
-        acc[L * 64 + l] -= p0;
-        acc[(L + 1) * 64 + l] -= p1;
-        acc[(L + 2) * 64 + l] -= p2;
-      } else {
-        acc[L * 64 + l] += p0;
-        acc[(L + 1) * 64 + l] += p1;
-        acc[(L + 2) * 64 + l] += p2;
-      }
-    }
+    for (int c = 0; c < D; ++c) add_product(p[c], load_elem(kr, c), side == 1);
+  }
+  if (lam != 0.f) {
+    add_product(lam, mb, false);
+    add_product(lam, ma, true);
   }
   int64_t carry = 0;
   bool nz = false;
@@ -103,10 +109,11 @@ struct Shared {
 
 // Rank the candidates cand(c) = (list ? list[c] : base + c), c < nc, of one
 // row and mark the n_take best in sel[].  NS slots per lane (candidate
-// c = s*64+lane).
+// c = s*64+lane).  Routing (mb non-null): a candidate's score gains
+// lam * mb[cand].
 template <typename T, int D, int NS>
 PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int base, int nc, int n_take,
-                         bool (&sel)[NS], int (&cj)[NS], int32_t *diag) {
+                         const float *mb, float lam, bool (&sel)[NS], int (&cj)[NS], int32_t *diag) {
   const int l = lane_id();
   bool valid[NS];
 #pragma unroll
@@ -159,6 +166,10 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int ba
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     dl[s] = gamma * sqrt(p2 * (double)k2[s]) + 0x1p-1000;
+    if (mb && valid[s]) {   // routing term: the product is exact, the sum rounds once
+      sc[s] += (double)lam * (double)mb[cj[s]];
+      dl[s] += 0x1p-52 * fabs(sc[s]);
+    }
     key[s] = valid[s] ? (((uint64_t)ord32((float)sc[s]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)cj[s])) : 0ull;
     if (valid[s]) {
       kmax = key[s] > kmax ? key[s] : kmax;
@@ -268,7 +279,8 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int ba
         if (sbv - dbv > sc[sa] + dl[sa]) beats = true;
         else if (sbv + dbv < sc[sa] - dl[sa]) beats = false;
         else {
-          const int c = exact_cmp<T, D>(sh.pf, kbase + (size_t)jb * D, kbase + (size_t)cj[sa] * D, sh.kul);
+          const int c = exact_cmp<T, D>(sh.pf, kbase + (size_t)jb * D, kbase + (size_t)cj[sa] * D, mb ? lam : 0.f,
+                                        mb ? mb[jb] : 0.f, mb ? mb[cj[sa]] : 0.f, sh.kul);
           beats = c > 0 || (c == 0 && jb < cj[sa]);
         }
         rank[sa] += beats;
@@ -313,8 +325,8 @@ PISA_DEV void load_p(Shared &sh, const T *src) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void indexer_blockrows(PisaDims dm, const T *__restrict__ qsel,
-                                                        const T *__restrict__ ksel, int32_t *__restrict__ idx,
-                                                        int32_t *diag) {
+                                                        const T *__restrict__ ksel, const float *__restrict__ mcov,
+                                                        int32_t *__restrict__ idx, int32_t *diag) {
   __shared__ Shared sh;
   const int unit = blockIdx.x;
   const int i = unit % dm.n_blk;
@@ -329,7 +341,8 @@ __global__ __launch_bounds__(64) void indexer_blockrows(PisaDims dm, const T *__
   load_p<T, D>(sh, qsel + ((size_t)bh * dm.n_sel + i) * D);
   bool sel[kMaxSlots];
   int cj[kMaxSlots];
-  select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, n_take, sel, cj, diag);
+  const float *mb = mcov ? mcov + ((size_t)b * dm.Hkv + hk) * dm.n_blk : nullptr;
+  select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, n_take, mb, dm.route_lambda, sel, cj, diag);
   int32_t *out = idx + ((size_t)bh * dm.n_rows + i) * dm.klist;
   for (int c = lane_id(); c < c0; c += 64) out[c] = c;
   write_sorted<kMaxSlots>(sel, cj, out + c0, dm.klist - c0);
@@ -338,8 +351,8 @@ __global__ __launch_bounds__(64) void indexer_blockrows(PisaDims dm, const T *__
 template <typename T, int D>
 __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__restrict__ Q,
                                                     const T *__restrict__ qsel, const T *__restrict__ ksel,
-                                                    int32_t *__restrict__ idx, int32_t *__restrict__ cand,
-                                                    int32_t *diag) {
+                                                    const float *__restrict__ mcov, int32_t *__restrict__ idx,
+                                                    int32_t *__restrict__ cand, int32_t *diag) {
   __shared__ Shared sh;
   const int unit = blockIdx.x;
   const int gm = unit % dm.n_sel;
@@ -352,12 +365,13 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
   const int nc = pisa_row_geometry(dm, gm * g, &own, &lo);
   const int c0 = min(dm.sink, nc);
   const int C = min(dm.n_cand, nc - c0);
+  const float *mb = mcov ? mcov + ((size_t)b * dm.Hkv + hk) * dm.n_blk : nullptr;
   // proxy pass over every candidate block past the sinks
   load_p<T, D>(sh, qsel + ((size_t)bh * dm.n_sel + gm) * D);
   {
     bool sel[kMaxSlots];
     int cj[kMaxSlots];
-    select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C, sel, cj, diag);
+    select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C, mb, dm.route_lambda, sel, cj, diag);
     write_sorted<kMaxSlots>(sel, cj, sh.clist, C);
     if (cand) {
       __syncthreads();
@@ -374,7 +388,7 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
     load_p<T, D>(sh, Q + ((size_t)bh * dm.L + t) * D);
     bool sel[4];
     int cj[4];
-    select_row<T, D, 4>(sh, kbase, sh.clist, 0, C, n_take, sel, cj, diag);
+    select_row<T, D, 4>(sh, kbase, sh.clist, 0, C, n_take, mb, dm.route_lambda, sel, cj, diag);
     const int ct = min(dm.sink, pisa_row_geometry(dm, t, &own, &lo));
     int32_t *out = idx + ((size_t)bh * dm.n_rows + t) * dm.klist;
     for (int c = lane_id(); c < ct; c += 64) out[c] = c;
@@ -437,7 +451,8 @@ struct PivotLayout {
                                                        // [kPW][kPM][MLD]; then select_row's Shared
   static constexpr int SKN = S + kPX * SLD * 4;        // fp32 [kPNc] |ksel_j|
   static constexpr int SPN = SKN + kPNc * 4;           // fp32 [kPX] |qsel_p|
-  static constexpr int PV = SPN + kPX * 4;             // fp32 [kPW][128] row vector under re-score
+  static constexpr int MC = SPN + kPX * 4;             // fp32 [kPNc] covariance norms (routing)
+  static constexpr int PV = MC + kPNc * 4;             // fp32 [kPW][128] row vector under re-score
   static constexpr int LIST = PV + kPW * 128 * 4;      // uint16 [kPX][kPCap] proxy lists, ascending
   static constexpr int DEFN = LIST + kPX * kPCap * 2;  // int [4]: deferred proxies, deferred members
   static constexpr int DEFP = DEFN + 16;               // int [kPX]
@@ -634,6 +649,7 @@ PISA_DEV void load_vec_f32(float *dst, const uint16_t *src) {
 template <int D, int NS>
 __device__ __attribute__((noinline)) bool rescore_select(const float *srow, const uint16_t *list, int lo,
                                                          int nc, int n_take, float cb, const float *skn,
+                                                         const float *mc, float lam,
                                                          const uint16_t *vec, float *pv, const uint16_t *kbase,
                                                          uint16_t *lout, int32_t *gout, int len, int32_t *diag) {
   const int l = lane_id();
@@ -649,6 +665,15 @@ __device__ __attribute__((noinline)) bool rescore_select(const float *srow, cons
     sc[s] = valid[s] ? (double)srow[pos] : 0.0;
     dl[s] = valid[s] ? (double)fmaf(cb, skn[cj[s]], kAbsBound) : 0.0;
   }
+  // routing term lam * mc[j]: the product is exact in float64, the sum rounds once
+  auto add_route = [&](int s) {
+    if (mc && valid[s]) {
+      sc[s] += (double)lam * (double)mc[cj[s]];
+      dl[s] += 0x1p-52 * fabs(sc[s]);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < NS; ++s) add_route(s);
   load_vec_f32<D>(pv, vec);
   provisional64<NS>(sc, valid, n_take, sel);
   double t_in, t_out;
@@ -671,6 +696,7 @@ __device__ __attribute__((noinline)) bool rescore_select(const float *srow, cons
         dl[s] = bnd;
       }
     }
+    if (amb) add_route(s);
   }
   provisional64<NS>(sc, valid, n_take, sel);
   if (!bounds64<NS>(sc, dl, valid, sel, t_in, t_out) || !(t_in > t_out)) return false;
@@ -683,8 +709,9 @@ __device__ __attribute__((noinline)) bool rescore_select(const float *srow, cons
 // write_sorted_lds.
 template <int D, int NS>
 __device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_t *kbase, const uint16_t *list,
-                                                       int base, int nc, int n_take, const uint16_t *vec,
-                                                       uint16_t *lout, int32_t *gout, int len, int32_t *diag) {
+                                                       int base, int nc, int n_take, const float *mb, float lam,
+                                                       const uint16_t *vec, uint16_t *lout, int32_t *gout, int len,
+                                                       int32_t *diag) {
   const int l = lane_id();
   if (list)
     for (int c = l; c < nc; c += 64) sh.clist[c] = list[c];
@@ -696,7 +723,7 @@ __device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_
   wave_lds_sync();
   bool sel[NS];
   int cj[NS];
-  select_row<uint16_t, D, NS>(sh, kbase, list ? sh.clist : nullptr, base, nc, n_take, sel, cj, diag);
+  select_row<uint16_t, D, NS>(sh, kbase, list ? sh.clist : nullptr, base, nc, n_take, mb, lam, sel, cj, diag);
   write_sorted_lds<NS>(sel, cj, lout, gout, len);
   if (diag && l == 0) atomicAdd(&diag[2], 1);
   wave_lds_sync();
@@ -706,6 +733,7 @@ template <int D>
 __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, const uint16_t *__restrict__ Q,
                                                                  const uint16_t *__restrict__ qsel,
                                                                  const uint16_t *__restrict__ ksel,
+                                                                 const float *__restrict__ mcov,
                                                                  int32_t *__restrict__ idx,
                                                                  int32_t *__restrict__ cand, int32_t *diag) {
   using LY = PivotLayout;
@@ -728,6 +756,9 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   float *S = reinterpret_cast<float *>(lds + LY::S);
   float *SKN = reinterpret_cast<float *>(lds + LY::SKN);
   float *SPN = reinterpret_cast<float *>(lds + LY::SPN);
+  float *MC = reinterpret_cast<float *>(lds + LY::MC);
+  const bool route = mcov != nullptr;
+  const float lam = dm.route_lambda;
   float *PVw = reinterpret_cast<float *>(lds + LY::PV) + w * 128;
   uint16_t *LIST = reinterpret_cast<uint16_t *>(lds + LY::LIST);
   int *defn = reinterpret_cast<int *>(lds + LY::DEFN);
@@ -748,6 +779,8 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   const bool pval = proxy(lq, ph, pgm, pnc);
   const int ncmax = __builtin_amdgcn_readfirstlane(wave_max_f32(pval ? (float)pnc : 0.f));
   if (tid < 4) defn[tid] = 0;
+  if (route)   // this kv head's covariance norms (routing term lam * MC[j])
+    for (int j = tid; j < dm.n_blk; j += kPW * 64) MC[j] = mcov[((size_t)b * dm.Hkv + hk) * dm.n_blk + j];
 
   // ---- 1. proxy scores, |k| and |p|
   u32x4_t pf[KS];
@@ -822,13 +855,17 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         valid[s] = cid[s] < nc && cid[s] >= c0;
         sc[s] = (s < nsl && valid[s]) ? S[pl * LY::SLD + cid[s]] : 0.f;
         dl[s] = fmaf(cb, skr[s], kAbsBound);
+        if (route && s < nsl && valid[s]) {   // + lam M_j: exact product, one rounding (covered below)
+          sc[s] = fmaf(lam, MC[cid[s]], sc[s]);
+          dl[s] = fmaf(0x1p-22f, fabsf(sc[s]), dl[s]);
+        }
       }
       if (fast_select<NS>(sc, dl, valid, nsl, C, sel)) {
         write_sorted_lds<NS>(sel, cid, lout, gout, dm.n_cand);
       } else {
         const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
-        if (!rescore_select<D, NS>(S + pl * LY::SLD, nullptr, c0, nc, C, cb, SKN, vec, PVw, kbase, lout, gout,
-                                   dm.n_cand, diag) &&
+        if (!rescore_select<D, NS>(S + pl * LY::SLD, nullptr, c0, nc, C, cb, SKN, route ? MC : nullptr, lam,
+                                   vec, PVw, kbase, lout, gout, dm.n_cand, diag) &&
             l == 0)
           defp[atomicAdd(&defn[0], 1)] = pl;
       }
@@ -844,7 +881,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       const int c0 = min(dm.sink, nc);
       const int C = min(dm.n_cand, nc - c0);
       int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
-      exact_select<D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C,
+      exact_select<D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C, route ? MC : nullptr, lam,
                                  qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D, LIST + pl * kPCap, gout,
                                  dm.n_cand, diag);
     }
@@ -938,13 +975,17 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         for (int s = 0; s < NS; ++s) {
           sc[s] = valid[s] ? Mw[m * LY::MLD + s * 64 + l] : 0.f;
           dl[s] = fmaf(cb, skm[s], kAbsBound);
+          if (route && valid[s]) {
+            sc[s] = fmaf(lam, MC[cj[s]], sc[s]);
+            dl[s] = fmaf(0x1p-22f, fabsf(sc[s]), dl[s]);
+          }
         }
         int ct;
         int32_t *out = member_row(qrow0, t, ct);
         if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel)) {
           write_sorted_lds<NS>(sel, cj, nullptr, out, dm.klist - ct);
-        } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, 0, C, n_take, cb, SKN, Q + (qrow0 + t) * D,
-                                          PVw, kbase, nullptr, out, dm.klist - ct, diag) &&
+        } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, 0, C, n_take, cb, SKN, route ? MC : nullptr, lam,
+                                          Q + (qrow0 + t) * D, PVw, kbase, nullptr, out, dm.klist - ct, diag) &&
                    l == 0) {
           defm[atomicAdd(&defn[1], 1)] = t * 64 + pl;
         }
@@ -964,8 +1005,8 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       const size_t row = (size_t)(b * dm.Hq + h) * dm.L + t;
       int own, lo;
       const int ct = min(dm.sink, pisa_row_geometry(dm, t, &own, &lo));
-      exact_select<D, kPCap / 64>(sh, kbase, LIST + pl * kPCap, 0, C, n_take, Q + row * D, nullptr,
-                                  idx + row * dm.klist + ct, dm.klist - ct, diag);
+      exact_select<D, kPCap / 64>(sh, kbase, LIST + pl * kPCap, 0, C, n_take, route ? MC : nullptr, lam,
+                                  Q + row * D, nullptr, idx + row * dm.klist + ct, dm.klist - ct, diag);
     }
   }
 }
@@ -975,8 +1016,8 @@ __global__ void zero_diag(int32_t *d) {
 }
 
 template <typename T, int D>
-hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, int32_t *idx,
-                    int32_t *cand, int32_t *diag, hipStream_t st) {
+hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, const float *mcov,
+                    int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st) {
   if (diag) zero_diag<<<1, 64, 0, st>>>(diag);
   if constexpr (sizeof(T) == 2) {
     if (dm.group >= 1 && dm.n_cand <= kPCap && dm.group <= kPG) {
@@ -992,30 +1033,30 @@ hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const v
       const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk * ((npb + kPX - 1) / kPX);
       indexer_pivot_mfma<D><<<grid, kPW * 64, LY::TOTAL, st>>>(dm, static_cast<const uint16_t *>(Q),
                                                                static_cast<const uint16_t *>(qsel),
-                                                               static_cast<const uint16_t *>(ksel), idx, cand,
-                                                               diag);
+                                                               static_cast<const uint16_t *>(ksel), mcov, idx,
+                                                               cand, diag);
       return hipGetLastError();
     }
   }
   if (dm.group >= 1) {
     const unsigned grid = (unsigned)dm.B * dm.Hq * dm.n_sel;
     indexer_pivot<T, D><<<grid, 64, 0, st>>>(dm, static_cast<const T *>(Q), static_cast<const T *>(qsel),
-                                             static_cast<const T *>(ksel), idx, cand, diag);
+                                             static_cast<const T *>(ksel), mcov, idx, cand, diag);
   } else {
     const unsigned grid = (unsigned)dm.B * dm.Hq * dm.n_blk;
     indexer_blockrows<T, D><<<grid, 64, 0, st>>>(dm, static_cast<const T *>(qsel), static_cast<const T *>(ksel),
-                                                 idx, diag);
+                                                 mcov, idx, diag);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, int32_t *idx,
-                          int32_t *cand, int32_t *diag, hipStream_t st) {
+hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, const float *mcov,
+                          int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st) {
   if (dm.dtype == 0)
-    return dm.d == 64 ? launch_t<uint16_t, 64>(dm, Q, qsel, ksel, idx, cand, diag, st)
-                      : launch_t<uint16_t, 128>(dm, Q, qsel, ksel, idx, cand, diag, st);
-  return dm.d == 64 ? launch_t<float, 64>(dm, Q, qsel, ksel, idx, cand, diag, st)
-                    : launch_t<float, 128>(dm, Q, qsel, ksel, idx, cand, diag, st);
+    return dm.d == 64 ? launch_t<uint16_t, 64>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
+                      : launch_t<uint16_t, 128>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st);
+  return dm.d == 64 ? launch_t<float, 64>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
+                    : launch_t<float, 128>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st);
 }

@@ -65,6 +65,10 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
     if (p->n_cand > kMaxCand) return fail(PISA_E_UNSUPPORTED, "n_cand %d > %d", p->n_cand, kMaxCand);
   }
   if (!std::isfinite(p->scale)) return fail(PISA_E_ARG, "scale is not finite");
+  if (!std::isfinite(p->route_lambda) || p->route_lambda < 0.f)
+    return fail(PISA_E_ARG, "route_lambda must be finite and >= 0");
+  if (p->route_lambda > 0.f && p->taylor == PISA_TAYLOR_NONE)
+    return fail(PISA_E_ARG, "covariance routing decides which blocks go to the Taylor term: taylor is NONE");
   if (!p->causal && p->topk == 0 && p->sink == 0 && p->taylor == PISA_TAYLOR_NONE)
     return fail(PISA_E_ARG, "non-causal with topk = 0, no sinks and no Taylor term attends to nothing");
   const long long n_blk = (p->L + (long long)p->block - 1) / p->block;
@@ -80,6 +84,7 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
   dm->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
   dm->sink = p->sink;
   dm->klist = p->topk + p->sink;
+  dm->route_lambda = p->route_lambda;
   return PISA_OK;
 }
 
@@ -130,7 +135,7 @@ pisa_status pisa_validate(const pisa_params *p) {
   return make_dims(p, &dm);
 }
 
-pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]) {
+pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[6]) {
   PisaDims dm;
   PISA_TRY(make_dims(p, &dm));
   if (!bytes) return fail(PISA_E_ARG, "bytes is NULL");
@@ -143,6 +148,7 @@ pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[5]) {
   bytes[4] = dm.taylor == PISA_TAYLOR_ORDER1   ? kv * dm.d * dm.d * es
              : dm.taylor == PISA_TAYLOR_HYBRID ? (size_t)dm.B * dm.Hkv * dm.d * dm.d * es
                                                : 0;
+  bytes[5] = dm.route_lambda > 0.f ? kv * sizeof(float) : 0;
   return PISA_OK;
 }
 
@@ -160,7 +166,7 @@ pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes) {
   PISA_TRY(make_dims(p, &dm));
   if (!bytes) return fail(PISA_E_ARG, "bytes is NULL");
   if (op < 0 || op > 2) return fail(PISA_E_ARG, "unknown op %d", op);
-  *bytes = op == 0 ? hbar_workspace_bytes(dm) : 0;
+  *bytes = op == 0 ? stats_workspace_bytes(dm) : 0;
   return PISA_OK;
 }
 
@@ -178,11 +184,13 @@ pisa_status pisa_block_stats(const pisa_params *p, const void *Q, const void *K,
   PISA_TRY(check_ptr(out->kbar, "stats.kbar", ty));
   PISA_TRY(check_ptr(out->vsum, "stats.vsum", ty));
   PISA_TRY(check_ptr(out->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
-  const size_t need = hbar_workspace_bytes(dm);
+  PISA_TRY(check_ptr(out->mcov, "stats.mcov", dm.route_lambda > 0.f));
+  const size_t need = stats_workspace_bytes(dm);
   PISA_TRY(check_ws(ws, ws_bytes, need));
   if (need && !aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
   return launched(launch_block_stats(dm, Q, K, V, out->qsel, out->ksel, out->kbar, out->vsum,
-                                     out->HT, need ? ws : nullptr, stream),
+                                     out->HT, dm.route_lambda > 0.f ? out->mcov : nullptr, need ? ws : nullptr,
+                                     stream),
                   "block_stats");
 }
 
@@ -195,6 +203,7 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
   if (!stats) return fail(PISA_E_ARG, "stats is NULL");
   PISA_TRY(check_ptr(stats->qsel, "stats.qsel", true));
   PISA_TRY(check_ptr(stats->ksel, "stats.ksel", true));
+  PISA_TRY(check_ptr(stats->mcov, "stats.mcov", dm.route_lambda > 0.f));
   PISA_TRY(check_ptr(idx, "idx", dm.klist > 0));
   PISA_TRY(check_ptr(cand, "cand", false));
   PISA_TRY(check_ws(ws, ws_bytes, 0));
@@ -204,7 +213,8 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
     diag = static_cast<int32_t *>(ws);
   }
   if (dm.klist == 0 && !(dm.group >= 1 && cand)) return PISA_OK;  // nothing to select or write
-  return launched(launch_indexer(dm, Q, stats->qsel, stats->ksel, idx, cand, diag, stream),
+  return launched(launch_indexer(dm, Q, stats->qsel, stats->ksel, dm.route_lambda > 0.f ? stats->mcov : nullptr,
+                                 idx, cand, diag, stream),
                   "indexer_topk");
 }
 

@@ -24,6 +24,7 @@ struct PisaDims {
   float scale;     // softmax scale (resolved)
   int sink;        // leading candidate blocks always kept
   int klist;       // entries of an idx row: topk + sink
+  float route_lambda;  // covariance-aware routing weight (0: off)
 };
 
 // Selection-row geometry shared by the indexer and the attention kernels.
@@ -49,22 +50,28 @@ inline int pisa_row_geometry(const PisaDims &dm, int start_token, int *own, int 
   return l;
 }
 
-// Hybrid order, bf16: the mean first-order matrix is summed over runs of
-// kHbarRun consecutive blocks into an fp32 workspace [B, Hkv, runs, d, d],
-// then the runs are added in order.
+// The mean first-order matrix Hbar (hybrid order, covariance routing).  bf16:
+// summed over runs of kHbarRun consecutive blocks into an fp32 workspace
+// [B, Hkv, runs, d, d], then the runs are added in order.  Routing also keeps
+// an fp32 copy of Hbar^T [B, Hkv, d, d] after the run sums.
 constexpr int kHbarRun = 16;
-inline size_t hbar_workspace_bytes(const PisaDims &dm) {
-  if (dm.taylor != 3 || dm.dtype != 0) return 0;
+inline bool needs_hbar(const PisaDims &dm) { return dm.taylor == 3 || dm.route_lambda > 0.f; }
+inline size_t hbar_runs_bytes(const PisaDims &dm) {
+  if (!needs_hbar(dm) || dm.dtype != 0) return 0;
   const size_t runs = (size_t)(dm.n_blk + kHbarRun - 1) / kHbarRun;
   return (size_t)dm.B * dm.Hkv * runs * dm.d * dm.d * sizeof(float);
+}
+inline size_t stats_workspace_bytes(const PisaDims &dm) {
+  const size_t hb32 = dm.route_lambda > 0.f ? (size_t)dm.B * dm.Hkv * dm.d * dm.d * sizeof(float) : 0;
+  return hbar_runs_bytes(dm) + hb32;
 }
 
 // launchers (return the hipError_t of the launch)
 hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, const void *V,
-                              void *qsel, void *ksel, float *kbar, float *vsum, void *HT, void *ws,
-                              hipStream_t st);
+                              void *qsel, void *ksel, float *kbar, float *vsum, void *HT, float *mcov,
+                              void *ws, hipStream_t st);
 hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
-                          int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);
+                          const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);
 hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const void *V,
                        const float *kbar, const float *vsum, const void *HT, const int32_t *idx,
                        void *O, float *lse, hipStream_t st);

@@ -372,8 +372,9 @@ __global__ __launch_bounds__(256) void hbar_run(PisaDims dm, const uint16_t *__r
         out[(size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq] = tot[i][4 * g + q];
 }
 
+// HbT (bf16, hybrid order) and hb32 (fp32 copy, routing): either may be null
 __global__ __launch_bounds__(256) void hbar_final(PisaDims dm, const float *__restrict__ ws,
-                                                  uint16_t *__restrict__ HbT) {
+                                                  uint16_t *__restrict__ HbT, float *__restrict__ hb32) {
   const int DD = dm.d * dm.d;
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (long long)dm.B * dm.Hkv * DD) return;
@@ -383,7 +384,134 @@ __global__ __launch_bounds__(256) void hbar_final(PisaDims dm, const float *__re
   const float *src = ws + (size_t)bh * nrun * DD + o;
   float s = 0.f;
   for (int r = 0; r < nrun; ++r) s += src[(size_t)r * DD];
-  HbT[gid] = (uint16_t)f32_to_bf16(s / (float)dm.n_blk);
+  const float m = s / (float)dm.n_blk;
+  if (HbT) HbT[gid] = (uint16_t)f32_to_bf16(m);
+  if (hb32) hb32[gid] = m;
+}
+
+// ---------------------------------------------------------------------------
+// Covariance-aware routing (PISA page, section 2): mcov_j = ||H_j - Hbar||_F.
+// bf16: one workgroup of four waves per (b, kv head, run of kMcovRun blocks);
+// H_j^T is formed as in hbar_run (raw MFMA moment minus sigma_j kbar_j^T, in
+// fp32), Hbar^T (fp32) held in registers for the run, and the squared
+// differences summed per lane, over the wave (fixed tree) and over the four
+// waves in order.
+constexpr int kMcovRun = 4;
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void mcov_bf16(PisaDims dm, const uint16_t *__restrict__ K,
+                                                 const uint16_t *__restrict__ V,
+                                                 const float *__restrict__ kbar,
+                                                 const float *__restrict__ vsum,
+                                                 const float *__restrict__ hb32, float *__restrict__ mcov) {
+  using C = HbarCfg<D, BS>;
+  constexpr int NE = C::NE, TPW = C::TPW, TILE = C::TILE, CPW = C::CPW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  float *red = reinterpret_cast<float *>(lds + C::TOTAL);   // [4] per-wave sums
+  const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrun = (dm.n_blk + kMcovRun - 1) / kMcovRun;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int run = logical % nrun, bh = logical / nrun;
+  const int j0 = run * kMcovRun, j1 = min(dm.n_blk, j0 + kMcovRun);
+  const int et = (w * TPW) / NE, ct0 = (w * TPW) % NE;
+  const size_t base = (size_t)bh * dm.L * D;
+  const uint16_t *Kb = K + base, *Vb = V + base;
+  const float *kb = kbar + (size_t)bh * dm.n_blk * D;
+  const float *vs = vsum + (size_t)bh * dm.n_blk * D;
+  float hb[TPW][16];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        hb[i][4 * g + q] = hb32[(size_t)bh * D * D + (size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq];
+  int off[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int pos = (w + 4 * u) * 64 + l;
+    const int row = pos / (D / 8), phys = pos % (D / 8);
+    off[u] = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
+  }
+  auto dma = [&](int j) {
+    const int k0 = j * BS, bytes = max(dm.L - k0, 0) * D * 2;
+    uint8_t *dk = lds + ((j - j0) & 1) * 2 * TILE, *dv = dk + TILE;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      dma16_buf(Kb + (size_t)k0 * D, bytes, off[u], dk + (w + 4 * u) * 1024);
+      dma16_buf(Vb + (size_t)k0 * D, bytes, off[u], dv + (w + 4 * u) * 1024);
+    }
+  };
+  const int srow = (l & 15) >> 2, ecol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  dma(j0);
+  for (int j = j0; j < j1; ++j) {
+    wait_vmcnt<0>();
+    __syncthreads();   // block j landed; the other slot and red are free
+    if (j + 1 < j1) dma(j + 1);
+    float ck[TPW];
+    f32x4_t cv[4];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) ck[i] = kb[(size_t)j * D + (ct0 + i) * 32 + lq];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) cv[g] = *reinterpret_cast<const f32x4_t *>(vs + (size_t)j * D + et * 32 + 8 * g + 4 * hl);
+    const uint8_t *kt = lds + ((j - j0) & 1) * 2 * TILE, *vt = kt + TILE;
+    f32x16_t r[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) r[i] = f32x16_t{};
+#pragma unroll
+    for (int st = 0; st < BS / 16; ++st) {
+      const int r1 = 16 * st + 4 * hl + srow;
+      const u32x4_t av = frag_vt<D>(vt, r1, et * 32 + ecol);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) r[i] = mfma32(av, frag_vt<D>(kt, r1, (ct0 + i) * 32 + ecol), r[i]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float h = r[i][4 * g + q] - cv[g][q] * ck[i] - hb[i][4 * g + q];
+          ss = fmaf(h, h, ss);
+        }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    if (l == 0) red[w] = ss;
+    __syncthreads();
+    if (tid == 0) mcov[(size_t)bh * dm.n_blk + j] = sqrtf(((red[0] + red[1]) + red[2]) + red[3]);
+  }
+}
+
+// fp32: one workgroup per (b, kv head, block), each thread D * D / 256 entries
+template <int D, int BS>
+__global__ __launch_bounds__(kStatsThreads) void mcov_f32(PisaDims dm, const float *__restrict__ K,
+                                                          const float *__restrict__ V,
+                                                          const float *__restrict__ kbar,
+                                                          const float *__restrict__ vsum,
+                                                          const float *__restrict__ hb32, float *__restrict__ mcov) {
+  __shared__ float red[kStatsThreads];
+  const int j = blockIdx.x % dm.n_blk, bh = blockIdx.x / dm.n_blk;
+  const int t0 = j * BS, t1 = min(dm.L, t0 + BS);
+  const float *Kb = K + (size_t)bh * dm.L * D, *Vb = V + (size_t)bh * dm.L * D;
+  const float *kb = kbar + ((size_t)bh * dm.n_blk + j) * D, *vs = vsum + ((size_t)bh * dm.n_blk + j) * D;
+  const float *hb = hb32 + (size_t)bh * D * D;
+  float ss = 0.f;
+  for (int o = threadIdx.x; o < D * D; o += kStatsThreads) {
+    const int e = o / D, c = o % D;
+    float r = 0.f;
+    for (int t = t0; t < t1; ++t) r = fmaf(Vb[(size_t)t * D + e], Kb[(size_t)t * D + c], r);
+    const float h = r - vs[e] * kb[c] - hb[o];
+    ss = fmaf(h, h, ss);
+  }
+  red[threadIdx.x] = ss;
+  __syncthreads();
+  for (int n = kStatsThreads / 2; n > 0; n >>= 1) {
+    if ((int)threadIdx.x < n) red[threadIdx.x] += red[threadIdx.x + n];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mcov[(size_t)bh * dm.n_blk + j] = sqrtf(red[0]);
 }
 
 // fp32: one thread per (e, c), the same order of operations on the VALU.
@@ -392,7 +520,7 @@ __global__ __launch_bounds__(kStatsThreads) void hbar_f32(PisaDims dm, const flo
                                                           const float *__restrict__ V,
                                                           const float *__restrict__ kbar,
                                                           const float *__restrict__ vsum,
-                                                          float *__restrict__ HbT) {
+                                                          float *__restrict__ HbT, float *__restrict__ hb32) {
   constexpr int PER = D * D / kStatsThreads;
   const int bh = blockIdx.x / PER;
   const int o = (blockIdx.x % PER) * kStatsThreads + threadIdx.x;
@@ -406,18 +534,27 @@ __global__ __launch_bounds__(kStatsThreads) void hbar_f32(PisaDims dm, const flo
     for (int t = j * BS; t < t1; ++t) r = fmaf(Vb[(size_t)t * D + e], Kb[(size_t)t * D + c], r);
     tot += r - vs[(size_t)j * D + e] * kb[(size_t)j * D + c];
   }
-  HbT[(size_t)bh * D * D + o] = tot / (float)dm.n_blk;
+  const float m = tot / (float)dm.n_blk;
+  if (HbT) HbT[(size_t)bh * D * D + o] = m;
+  if (hb32) hb32[(size_t)bh * D * D + o] = m;
 }
 
+// Hbar (hybrid order and/or routing), then the covariance norms (routing)
 template <int D, int BS>
 hipError_t launch_hbar(const PisaDims &dm, const void *K, const void *V, const float *kbar, const float *vsum,
-                       void *HT, void *ws, hipStream_t st) {
+                       void *HT, float *mcov, void *ws, hipStream_t st) {
+  const bool hybrid = dm.taylor == 3, route = dm.route_lambda > 0.f;
+  float *hb32 = route ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + hbar_runs_bytes(dm)) : nullptr;
+  const long long n = (long long)dm.B * dm.Hkv * D * D;
   if (dm.dtype == 0) {
     using C = HbarCfg<D, BS>;
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hbar_run<D, BS>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mcov_bf16<D, BS>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL + 16);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
@@ -427,14 +564,26 @@ hipError_t launch_hbar(const PisaDims &dm, const void *K, const void *V, const f
         static_cast<float *>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long n = (long long)dm.B * dm.Hkv * D * D;
     hbar_final<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dm, static_cast<const float *>(ws),
-                                                             static_cast<uint16_t *>(HT));
+                                                             hybrid ? static_cast<uint16_t *>(HT) : nullptr, hb32);
+    if (route) {
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int nmr = (dm.n_blk + kMcovRun - 1) / kMcovRun;
+      mcov_bf16<D, BS><<<(unsigned)dm.B * dm.Hkv * nmr, 256, C::TOTAL + 16, st>>>(
+          dm, static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V), kbar, vsum, hb32, mcov);
+    }
   } else {
     const unsigned grid = (unsigned)dm.B * dm.Hkv * (D * D / kStatsThreads);
     hbar_f32<D, BS><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const float *>(K),
                                                     static_cast<const float *>(V), kbar, vsum,
-                                                    static_cast<float *>(HT));
+                                                    hybrid ? static_cast<float *>(HT) : nullptr, hb32);
+    if (route) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      mcov_f32<D, BS><<<(unsigned)dm.B * dm.Hkv * dm.n_blk, kStatsThreads, 0, st>>>(
+          dm, static_cast<const float *>(K), static_cast<const float *>(V), kbar, vsum, hb32, mcov);
+    }
   }
   return hipGetLastError();
 }
@@ -517,7 +666,8 @@ hipError_t launch_kv_f32(const PisaDims &dm, const void *K, const void *V, void 
 }  // namespace
 
 hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, const void *V, void *qsel,
-                              void *ksel, float *kbar, float *vsum, void *HT, void *ws, hipStream_t st) {
+                              void *ksel, float *kbar, float *vsum, void *HT, float *mcov, void *ws,
+                              hipStream_t st) {
   hipError_t e;
   const bool bf = dm.dtype == 0;
   if (bf) {
@@ -532,11 +682,11 @@ hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, 
                          : launch_kv_f32<128, 128>(dm, K, V, ksel, kbar, vsum, HT, st);
   }
   if (e != hipSuccess) return e;
-  if (dm.taylor == 3) {   // hybrid: the mean first-order matrix, after kbar and vsum
-    if (dm.d == 64) e = dm.bs == 64 ? launch_hbar<64, 64>(dm, K, V, kbar, vsum, HT, ws, st)
-                                    : launch_hbar<64, 128>(dm, K, V, kbar, vsum, HT, ws, st);
-    else e = dm.bs == 64 ? launch_hbar<128, 64>(dm, K, V, kbar, vsum, HT, ws, st)
-                         : launch_hbar<128, 128>(dm, K, V, kbar, vsum, HT, ws, st);
+  if (needs_hbar(dm)) {   // the mean first-order matrix (and covariance norms), after kbar and vsum
+    if (dm.d == 64) e = dm.bs == 64 ? launch_hbar<64, 64>(dm, K, V, kbar, vsum, HT, mcov, ws, st)
+                                    : launch_hbar<64, 128>(dm, K, V, kbar, vsum, HT, mcov, ws, st);
+    else e = dm.bs == 64 ? launch_hbar<128, 64>(dm, K, V, kbar, vsum, HT, mcov, ws, st)
+                         : launch_hbar<128, 128>(dm, K, V, kbar, vsum, HT, mcov, ws, st);
     if (e != hipSuccess) return e;
   }
   if (bf) return dm.d == 64 ? launch_q_pool<uint16_t, 64>(dm, Q, qsel, st) : launch_q_pool<uint16_t, 128>(dm, Q, qsel, st);

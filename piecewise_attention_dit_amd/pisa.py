@@ -25,12 +25,13 @@ class Params(ctypes.Structure):
                 ("L", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("n_cand", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("taylor", ctypes.c_int32), ("scale", ctypes.c_float), ("sink", ctypes.c_int32)]
+                ("taylor", ctypes.c_int32), ("scale", ctypes.c_float), ("sink", ctypes.c_int32),
+                ("route_lambda", ctypes.c_float)]
 
 
 class Stats(ctypes.Structure):
     _fields_ = [("qsel", ctypes.c_void_p), ("ksel", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
-                ("vsum", ctypes.c_void_p), ("HT", ctypes.c_void_p)]
+                ("vsum", ctypes.c_void_p), ("HT", ctypes.c_void_p), ("mcov", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):
@@ -82,10 +83,11 @@ def _check(status: int):
 
 
 def make_params(B, Hq, Hkv, L, d, dtype="bf16", block=64, topk=0, window=0, group=0, n_cand=0,
-                causal=False, taylor="order1", scale=0.0, sink=0) -> Params:
+                causal=False, taylor="order1", scale=0.0, sink=0, route_lambda=0.0) -> Params:
     return Params(B, Hq, Hkv, L, d, DTYPES[dtype] if isinstance(dtype, str) else int(dtype), block,
                   topk, window, group, n_cand, int(bool(causal)),
-                  TAYLOR[taylor] if isinstance(taylor, str) else int(taylor), float(scale), int(sink))
+                  TAYLOR[taylor] if isinstance(taylor, str) else int(taylor), float(scale), int(sink),
+                  float(route_lambda))
 
 
 def validate(p: Params) -> None:
@@ -93,7 +95,7 @@ def validate(p: Params) -> None:
 
 
 def stats_layout(p: Params) -> list[int]:
-    arr = (ctypes.c_size_t * 5)()
+    arr = (ctypes.c_size_t * 6)()
     _check(lib().pisa_stats_layout(ctypes.byref(p), arr))
     return list(arr)
 
@@ -130,7 +132,7 @@ def alloc_stats(p: Params, device="cuda") -> dict:
     td = _tdtype(p)
     st = dict(qsel=torch.empty((p.B, p.Hq, n_sel, p.d), dtype=td, device=device),
               ksel=torch.empty((p.B, p.Hkv, n_blk, p.d), dtype=td, device=device),
-              kbar=None, vsum=None, HT=None)
+              kbar=None, vsum=None, HT=None, mcov=None)
     if p.taylor != TAYLOR["none"]:
         st["kbar"] = torch.empty((p.B, p.Hkv, n_blk, p.d), dtype=torch.float32, device=device)
         st["vsum"] = torch.empty((p.B, p.Hkv, n_blk, p.d), dtype=torch.float32, device=device)
@@ -138,12 +140,14 @@ def alloc_stats(p: Params, device="cuda") -> dict:
         st["HT"] = torch.empty((p.B, p.Hkv, n_blk, p.d, p.d), dtype=td, device=device)
     elif p.taylor == TAYLOR["hybrid"]:   # the transposed mean first-order matrix
         st["HT"] = torch.empty((p.B, p.Hkv, p.d, p.d), dtype=td, device=device)
+    if p.route_lambda > 0:              # covariance norms for routing
+        st["mcov"] = torch.empty((p.B, p.Hkv, n_blk), dtype=torch.float32, device=device)
     return st
 
 
 def _cstats(st: dict) -> Stats:
     return Stats(*(st[k].data_ptr() if st.get(k) is not None else None
-                   for k in ("qsel", "ksel", "kbar", "vsum", "HT")))
+                   for k in ("qsel", "ksel", "kbar", "vsum", "HT", "mcov")))
 
 
 def block_stats(p: Params, q, k, v, stats=None, ws=None, stream=None) -> dict:
@@ -194,13 +198,13 @@ def sparse_attn_fwd(p: Params, q, k, v, stats: dict, idx, out=None, lse=None, wa
 
 
 def attention(q, k, v, *, block=64, topk=0, window=0, group=0, n_cand=0, causal=False,
-              taylor="order1", scale=0.0, sink=0, return_all=False):
+              taylor="order1", scale=0.0, sink=0, route_lambda=0.0, return_all=False):
     """Drop-in forward: (Q, K, V) -> O, running the three library calls."""
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     dtype = "bf16" if q.dtype == torch.bfloat16 else "f32"
     p = make_params(B, Hq, Hkv, L, d, dtype, block, topk, window, group, n_cand, causal, taylor, scale,
-                    sink)
+                    sink, route_lambda)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != _tdtype(p):
             raise ValueError(f"{name} must be a contiguous {_tdtype(p)} CUDA tensor")

@@ -46,6 +46,7 @@ class Workload:
     causal: bool = False
     taylor: str = "order1"  # "none" | "order0" | "order1" | "hybrid"
     sink: int = 0           # leading key blocks always kept (attention sinks)
+    route_lambda: float = 0.0  # covariance-aware routing weight
     recipe: str = "gauss"   # input recipe, see make_inputs
     grid: tuple = ()        # spatial grid (row-major token order) for field recipes
     seed: int = 0
@@ -62,7 +63,8 @@ class Workload:
         return dict(B=self.B, Hq=self.Hq, Hkv=self.Hkv, L=self.L, d=self.d,
                     dtype=self.dtype, block=self.block, topk=self.topk,
                     window=self.window, group=self.group, n_cand=self.n_cand,
-                    causal=self.causal, taylor=self.taylor, sink=self.sink)
+                    causal=self.causal, taylor=self.taylor, sink=self.sink,
+                    route_lambda=self.route_lambda)
 
 
 # The five headline workloads.  "keep rho" is resolved as k = round(rho * n_blk)
@@ -138,6 +140,16 @@ PARITY_CASES = {
     "video_dit_s_sink": WORKLOADS["video_dit"].replace(name="video_dit_s_sink", Hq=2, Hkv=2,
                                                        L=1000, grid=(1, 20, 50), topk=2, sink=1,
                                                        taylor="hybrid"),
+    # covariance-aware routing, weights that make both terms of the score count
+    "llm_swa_s_route": WORKLOADS["llm_swa"].replace(name="llm_swa_s_route", B=1, Hq=8, Hkv=2,
+                                                    L=2048 + 24, window=384, topk=4,
+                                                    route_lambda=0.04),
+    "video_dit_s_route": WORKLOADS["video_dit"].replace(name="video_dit_s_route", Hq=2, Hkv=2,
+                                                        L=1000, grid=(1, 20, 50), topk=2,
+                                                        taylor="hybrid", route_lambda=0.05),
+    "llm_pivot_s_route": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_route", Hq=8, Hkv=2,
+                                                        L=2048 + 40, topk=6, n_cand=12,
+                                                        taylor="order0", route_lambda=0.016),
 }
 
 

@@ -58,6 +58,9 @@ def _p(**kw):
     (dict(dtype=7), pisa.PISA_E_ARG),
     (dict(taylor=5), pisa.PISA_E_ARG),
     (dict(sink=-1), pisa.PISA_E_ARG),
+    (dict(route_lambda=-1.0), pisa.PISA_E_ARG),
+    (dict(route_lambda=float("nan")), pisa.PISA_E_ARG),
+    (dict(route_lambda=0.5, taylor="none"), pisa.PISA_E_ARG),
     (dict(topk=40, sink=25), pisa.PISA_E_UNSUPPORTED),
     (dict(topk=-1), pisa.PISA_E_ARG),
     (dict(topk=65), pisa.PISA_E_UNSUPPORTED),
@@ -80,7 +83,7 @@ def test_layouts():
     n_blk = 16
     sizes = pisa.stats_layout(p)
     assert sizes == [1 * 4 * n_blk * 128 * 2, 1 * 2 * n_blk * 128 * 2, 2 * n_blk * 128 * 4,
-                     2 * n_blk * 128 * 4, 2 * n_blk * 128 * 128 * 2]
+                     2 * n_blk * 128 * 4, 2 * n_blk * 128 * 128 * 2, 0]
     assert pisa.index_layout(p) == [1 * 4 * n_blk * 4 * 4, 0]
     assert pisa.index_layout(_p(L=1000, sink=3)) == [1 * 4 * n_blk * (4 + 3) * 4, 0]
     q = _p(L=1000, group=8, n_cand=16, causal=True, dtype="f32")
@@ -101,6 +104,11 @@ def test_layouts():
     assert pisa.workspace_size(_p(L=64 * 40, taylor="hybrid"), 0) == 2 * 3 * 128 * 128 * 4
     assert pisa.workspace_size(_p(L=1000, taylor="hybrid", dtype="f32"), 0) == 0
     assert all(pisa.workspace_size(h, op) == 0 for op in (1, 2))
+    # routing: covariance norms per block, run sums and an fp32 Hbar copy
+    rt = _p(L=1000, route_lambda=0.5)
+    assert pisa.stats_layout(rt)[5] == 2 * n_blk * 4 and pisa.stats_layout(p)[5] == 0
+    assert pisa.workspace_size(rt, 0) == 2 * 1 * 128 * 128 * 4 + 2 * 128 * 128 * 4
+    assert pisa.workspace_size(_p(L=1000, route_lambda=0.5, dtype="f32"), 0) == 2 * 128 * 128 * 4
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
@@ -124,6 +132,9 @@ def test_launch_calls_reject_before_launch():
     assert _call_stats(hy) == pisa.PISA_E_WORKSPACE
     assert _call_stats(hy, ws=FAKE, ws_bytes=pisa.workspace_size(hy, 0) - 16) == pisa.PISA_E_WORKSPACE
     assert _call_stats(hy, ws=FAKE + 4, ws_bytes=pisa.workspace_size(hy, 0)) == pisa.PISA_E_ARG
+    rt = _p(route_lambda=0.5)                                     # routing needs mcov
+    assert _call_stats(rt, ws=FAKE, ws_bytes=pisa.workspace_size(rt, 0)) == pisa.PISA_E_ARG
+    assert b"mcov" in L.pisa_last_error()
     assert _call_stats(_p(d=80)) == pisa.PISA_E_UNSUPPORTED
     assert L.pisa_block_stats(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, 0, None) == pisa.PISA_E_ARG
     st = pisa.Stats(FAKE, FAKE, FAKE, FAKE, FAKE)

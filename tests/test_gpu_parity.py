@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_common import compare_idx, compare_out, compare_stats, problem, run_gpu
+from gpu_common import compare_idx, compare_idx_routed, compare_out, compare_stats, problem, run_gpu
 from oracle import pisa_oracle as po
 from piecewise_attention_dit_amd import workloads as W
 
@@ -21,8 +21,17 @@ def _check_case(knobs, q, k, v):
     g = run_gpu(knobs, q, k, v)
     ref = po.run(qa, ka, va, P)
     compare_stats(g, ref["stats"], P)
-    compare_idx(g, ref["idx"], ref["cand"])
-    mx, mn = compare_out(g, ref["O"], ref["lse"], P)
+    if P.route_lambda > 0:
+        same = compare_idx_routed(g, ref, P, qa)
+        # outputs of the tokens whose rows selected the same blocks
+        rows_t = np.arange(P.L) if P.pivot else np.arange(P.L) // P.block
+        sel = same[:, :, rows_t]
+        print(f"[parity] routing: {int((~same).sum())} of {same.size} rows differ within the margin",
+              flush=True)
+    else:
+        compare_idx(g, ref["idx"], ref["cand"])
+        sel = None
+    mx, mn = compare_out(g, ref["O"], ref["lse"], P, sel)
     print(f"[parity] ok max_abs={mx:.3e} mean_abs={mn:.3e} diag={g['diag'][:3].tolist()}", flush=True)
     return g, ref
 
@@ -55,6 +64,10 @@ def test_parity_cases(name):
          taylor="none"),
     dict(L=900, block=64, topk=3, group=4, n_cand=6, causal=True, window=150, sink=20,
          taylor="order1"),                                        # sinks beyond most rows' reach
+    dict(L=600, block=64, topk=2, d=64, dtype="f32", route_lambda=0.005),   # routing, fp32
+    dict(L=500, block=64, topk=2, d=64, group=4, n_cand=5, dtype="f32", causal=True,
+         taylor="order0", route_lambda=0.01),                    # routing, fp32 PIVOT
+    dict(L=777, block=128, topk=1, d=64, taylor="order1", route_lambda=0.02),
 ])
 def test_edge_cases(kw):
     base = dict(B=1, Hq=2, Hkv=2, L=256, d=128, dtype="bf16", block=64, topk=2, window=0, group=0,
