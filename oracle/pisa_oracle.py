@@ -404,6 +404,96 @@ def run(q, k, v, P: Problem):
 
 
 # ----------------------------------------------------------------------------
+# decode: one new token against a key/value cache ([HyLRA] section 2.3, hybrid
+# inference: sensitive layers select the top-k blocks, tolerant layers reuse
+# the lists of an earlier layer and attend to that part of the cache only;
+# [SWA] the w-slot ring buffer, position i in slot i mod w)
+
+def decode_geometry(P: Problem, pos: int):
+    """(own block, lo, number of candidates) of the token at position pos: the
+    causal token row of the prefill path (window widened to whole blocks)."""
+    own = pos // P.block
+    lo = (max(0, pos - P.window + 1) // P.block) if P.window > 0 else own
+    return own, lo, lo
+
+
+def decode_select(q: np.ndarray, st: dict, P: Problem, pos: int) -> np.ndarray:
+    """Kept list [B, Hq, topk + sink] of the new token q [B, Hq, d]: the sink
+    blocks, then the top-k of the other candidates by the exact score
+    q . ksel_j (+ lam M_j with routing), ties to the lower block."""
+    B, Hq = q.shape[:2]
+    own, lo, nc = decode_geometry(P, pos)
+    c0 = min(P.sink, nc)
+    lam = float(np.float32(P.route_lambda))
+    idx = np.full((B, Hq, P.klist), -1, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h * P.Hkv // P.Hq
+            bias = lam * st["M"][b, hk, c0:nc] if lam > 0 else None
+            t = top_n(q[b, h], st["ksel"][b, hk, c0:nc], np.arange(c0, nc), P.topk, bias)
+            idx[b, h, :c0 + len(t)] = np.concatenate([np.arange(c0), t])
+    return idx
+
+
+def decode_attend(q, k, v, st, idx, P: Problem, pos: int) -> tuple:
+    """o [B, Hq, d] and lse [B, Hq] of the token at position pos (keys 0..pos
+    of the cache k, v [B, Hkv, >= pos + 1, d]) with the kept lists idx
+    [B, Hq, >= 1] (-1 padded; from decode_select or reused from another
+    layer).  PISA page, section 2: exact terms over the kept blocks and the
+    window range [lo, own] (keys s <= pos), Taylor terms for the other
+    candidates [0, lo): alpha = e^{scale q . kbar_j} times (sigma_j + [order1]
+    scale q H_j) in N and alpha n_j in D, [hybrid] + scale (q Hbar) sum alpha."""
+    B, Hq, d = q.shape
+    sc, bs = P.sm_scale, P.block
+    own, lo, nc = decode_geometry(P, pos)
+    O = np.empty((B, Hq, d))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h * P.Hkv // P.Hq
+            T = sorted(int(j) for j in idx[b, h] if j >= 0)
+            kept = sorted(set(T) | set(range(lo, own + 1)))
+            keys = np.concatenate([np.arange(j * bs, min((j + 1) * bs, pos + 1)) for j in kept])
+            U = [] if P.taylor == "none" else [j for j in range(nc) if j not in set(T)]
+            qv = q[b, h]
+            x = sc * (k[b, hk, keys] @ qv)
+            a = sc * (st["kbar"][b, hk, U] @ qv) if U else np.zeros(0)
+            m = max(x.max(), a.max() if len(a) else -np.inf)
+            px, pa = np.exp(x - m), np.exp(a - m)
+            n_j = np.array([min(bs, P.L - j * bs) for j in U], dtype=np.float64)
+            D = px.sum() + pa @ n_j
+            N = px @ v[b, hk, keys]
+            if U:
+                N = N + pa @ st["vsum"][b, hk, U]
+                if P.taylor == "order1":
+                    N = N + sc * pa @ np.einsum("c,jce->je", qv, st["H"][b, hk, U])
+                if P.taylor == "hybrid":
+                    N = N + sc * pa.sum() * (qv @ st["Hbar"][b, hk])
+            O[b, h] = N / D
+            lse[b, h] = m + math.log(D)
+    return O, lse
+
+
+def decode_ring(q, kr, vr, P: Problem, pos: int, w: int) -> tuple:
+    """Sliding-window decode from a w-slot ring ([SWA]: token i in slot
+    i mod w): the new token at pos attends to tokens max(0, pos - w + 1) ..
+    pos exactly.  kr, vr [B, Hkv, w, d]."""
+    B, Hq, d = q.shape
+    toks = np.arange(max(0, pos - w + 1), pos + 1)
+    O = np.empty((B, Hq, d))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h * P.Hkv // P.Hq
+            x = P.sm_scale * (kr[b, hk, toks % w] @ q[b, h])
+            m = x.max()
+            p = np.exp(x - m)
+            O[b, h] = (p @ vr[b, hk, toks % w]) / p.sum()
+            lse[b, h] = m + math.log(p.sum())
+    return O, lse
+
+
+# ----------------------------------------------------------------------------
 # helpers used by pins and diagnostics
 
 def kept_pairs(P: Problem, idx: np.ndarray, b: int = 0, h: int = 0) -> np.ndarray:

@@ -196,8 +196,24 @@ def check_routing(m):
     return ok
 
 
+def check_decode(m):
+    """The decode step equals the prefill's causal token row at the same position."""
+    B, Hq, Hkv, L, d, bs = 1, 2, 1, 40, 6, 8
+    q, k, v = _rand((B, Hq, L, d), 23, "bf16"), _rand((B, Hkv, L, d), 24, "bf16"), _rand((B, Hkv, L, d), 25, "bf16")
+    ok = True
+    for taylor in ("order1", "hybrid"):
+        P = m.Problem(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=bs, topk=1, window=10, group=1, n_cand=8,
+                      causal=True, taylor=taylor)
+        r = m.run(q, k, v, P)
+        for pos in (5, 27, 39):
+            idx = m.decode_select(q[:, :, pos], r["stats"], P, pos)
+            o, _ = m.decode_attend(q[:, :, pos], k, v, r["stats"], idx, P, pos)
+            ok &= np.array_equal(idx, r["idx"][:, :, pos]) and np.abs(o - r["O"][:, :, pos]).max() < 1e-12
+    return ok
+
+
 CHECKS = [check_pivot_mean, check_swa_count, check_dense, check_constant_v, check_orders, check_ties,
-          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks, check_routing]
+          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks, check_routing, check_decode]
 
 MUTATIONS = {
     "H transposed": ('H[:, :, j] = np.einsum("bhnc,bhne->bhce", kc, vj)',
@@ -234,6 +250,11 @@ MUTATIONS = {
                                  "M = np.sqrt((H ** 2).sum(axis=(-2, -1)))"),
     "routing skipped for members": ("tt = top_n(q[b, h, t], Kb[cl], cl, k, bias[cl])",
                                     "tt = top_n(q[b, h, t], Kb[cl], cl, k)"),
+    "decode reads keys past the token": ("np.arange(j * bs, min((j + 1) * bs, pos + 1))", "np.arange(j * bs, (j + 1) * bs)"),
+    "decode hybrid term without scale": ("N = N + sc * pa.sum() * (qv @ st[\"Hbar\"][b, hk])",
+                                         "N = N + pa.sum() * (qv @ st[\"Hbar\"][b, hk])"),
+    "decode window not widened": ("lo = (max(0, pos - P.window + 1) // P.block) if P.window > 0 else own\n    return own, lo, lo",
+                                  "lo = (max(0, pos - P.window + 1 + P.block - 1) // P.block) if P.window > 0 else own\n    return own, min(lo, own), min(lo, own)"),
     "scale not applied to exact logits": ("x = sc * (qt @ k[b, hk, keys].T)", "x = (qt @ k[b, hk, keys].T)"),
 }
 

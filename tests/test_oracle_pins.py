@@ -556,6 +556,70 @@ def test_p15_routing_prefers_high_covariance(pivot):
 
 
 # ---------------------------------------------------------------------------
+# P16: decode.  The new token at position pos is the causal token row t = pos
+# of the prefill path (one-token proxies over every candidate), so its list
+# and output must equal that row's; with every block kept it is dense causal
+# attention; a reused list gives the prefill row's output for that list; the
+# ring buffer attends exactly to the last w tokens.
+
+@pytest.mark.parametrize("taylor,window,sink,lam", [("order1", 0, 0, 0.0), ("hybrid", 20, 1, 0.0),
+                                                     ("order0", 9, 0, 0.05), ("none", 13, 2, 0.0)])
+def test_p16_decode_is_the_prefill_token_row(taylor, window, sink, lam):
+    B, Hq, Hkv, L, d, bs = 1, 4, 2, 70, 8, 8
+    q, k, v = _rand((B, Hq, L, d), 161, "bf16"), _rand((B, Hkv, L, d), 162, "bf16"), \
+        _rand((B, Hkv, L, d), 163, "bf16")
+    P = po.Problem(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=bs, topk=2, window=window, group=1,
+                   n_cand=64, causal=True, taylor=taylor, sink=sink, route_lambda=lam)
+    r = po.run(q, k, v, P)
+    for pos in (0, 7, 8, 33, 55, L - 1):
+        idx = po.decode_select(q[:, :, pos], r["stats"], P, pos)
+        assert np.array_equal(idx, r["idx"][:, :, pos]), pos
+        o, lse = po.decode_attend(q[:, :, pos], k, v, r["stats"], idx, P, pos)
+        np.testing.assert_allclose(o, r["O"][:, :, pos], atol=1e-12)
+        np.testing.assert_allclose(lse, r["lse"][:, :, pos], atol=1e-12)
+        # a list reused from another query (another layer's selection)
+        other = po.decode_select(q[:, :, (pos * 7 + 3) % L] * -1.0, r["stats"], P, pos)
+        full = r["idx"].copy()
+        full[:, :, pos] = other
+        for h in range(Hq):
+            want, wl = po.attend_tokens(q, k, v, r["stats"], full, P, 0, h, [pos])
+            got, gl = po.decode_attend(q[:, :, pos], k, v, r["stats"], other, P, pos)
+            np.testing.assert_allclose(got[0, h], want[0], atol=1e-12)
+
+
+def test_p16_decode_all_kept_is_dense():
+    B, Hq, Hkv, L, d, bs = 1, 2, 1, 64, 8, 8
+    q, k, v = _rand((B, Hq, L, d), 171), _rand((B, Hkv, L, d), 172), _rand((B, Hkv, L, d), 173)
+    P = po.Problem(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, dtype="f32", block=bs, topk=8, causal=True,
+                   taylor="order1")
+    st = po.block_stats(q, k, v, P)
+    dense = _dense(q, k, v, P, True)
+    for pos in (3, 20, 63):
+        idx = po.decode_select(q[:, :, pos], st, P, pos)
+        o, _ = po.decode_attend(q[:, :, pos], k, v, st, idx, P, pos)
+        np.testing.assert_allclose(o, dense[:, :, pos], atol=1e-13)
+
+
+@pytest.mark.parametrize("w", [1, 5, 16])
+def test_p16_ring_is_the_sliding_window(w):
+    B, Hq, Hkv, L, d = 1, 2, 1, 40, 8
+    q, k, v = _rand((B, Hq, L, d), 181), _rand((B, Hkv, L, d), 182), _rand((B, Hkv, L, d), 183)
+    P = po.Problem(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, dtype="f32", block=8, topk=0, window=w, causal=True,
+                   taylor="none")
+    t, s_ = np.arange(L)[:, None], np.arange(L)[None, :]
+    mask = (s_ <= t) & (t - s_ < w)
+    o_ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k).repeat_interleave(Hq // Hkv, 1),
+        torch.from_numpy(v).repeat_interleave(Hq // Hkv, 1), attn_mask=torch.from_numpy(mask),
+        scale=P.sm_scale).numpy()
+    kr, vr = np.zeros((B, Hkv, w, d)), np.zeros((B, Hkv, w, d))
+    for pos in range(L):                       # the cache as a decoder fills it
+        kr[:, :, pos % w], vr[:, :, pos % w] = k[:, :, pos], v[:, :, pos]
+        o, _ = po.decode_ring(q[:, :, pos], kr, vr, P, pos, w)
+        np.testing.assert_allclose(o, o_ref[:, :, pos], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # planted selection: a known answer by construction
 
 @pytest.mark.parametrize("pivot", [False, True])
