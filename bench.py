@@ -148,12 +148,103 @@ def hbm_traffic(kernel_src: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def decode_bench(args):
+    """One decode step (decode_topk + decode_fwd) for every (batch, query head)
+    of the workload's cache at its last position; one JSON line with the
+    token rate and the decode kernel's HBM roofline.  Algorithmic bytes per
+    row: keys and values of the exact tokens (kept blocks + window range),
+    kbar and vsum of every Taylor block (+ H_j for order 1, + Hbar once for
+    the hybrid order), q and o."""
+    import torch
+
+    from piecewise_attention_dit_amd import pisa
+    from piecewise_attention_dit_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    if args.taylor:
+        wl = wl.replace(taylor=args.taylor)
+    kn = wl.knobs()
+    print(f"[bench] decode: generating the {wl.name} cache", file=sys.stderr, flush=True)
+    q, k, v = W.make_inputs(wl)
+    p = pisa.make_params(**kn)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    st = pisa.block_stats(p, dq, dk, dv)
+    pos = wl.L - 1
+    qt = dq[:, :, pos].contiguous()
+    idx = pisa.decode_topk(p, pos, qt, st)
+    out = torch.empty_like(qt)
+    lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pisa.workspace_size(p, 3), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pisa.decode_topk(p, pos, qt, st, idx)
+        pisa.decode_fwd(p, pos, qt, dk, dv, st, idx, out=out, lse=lse, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        pisa.decode_topk(p, pos, qt, st, idx)
+    ev[1].record(stream)
+    for _ in range(args.steps):
+        pisa.decode_fwd(p, pos, qt, dk, dv, st, idx, out=out, lse=lse, ws=ws)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    ms_topk = ev[0].elapsed_time(ev[1]) / args.steps
+    ms_fwd = ev[1].elapsed_time(ev[2]) / args.steps
+    # algorithmic bytes of decode_fwd: per (batch, kv head) the keys and values
+    # of the union of its query heads' exact tokens, the statistics of every
+    # block that is a Taylor block for one of them, once; q and o per row
+    bs, d, es = wl.block, wl.d, (2 if wl.dtype == "bf16" else 4)
+    own = pos // bs
+    lo = (max(0, pos - wl.window + 1) // bs) if wl.window > 0 else own
+    ii = idx.cpu().numpy()
+    ratio = wl.Hq // wl.Hkv
+    total = 0
+    for b in range(wl.B):
+        for hk in range(wl.Hkv):
+            lists = [set(int(j) for j in ii[b, hk * ratio + r] if 0 <= j < lo) for r in range(ratio)]
+            union, common = set().union(*lists), set.intersection(*lists)
+            total += (len(union) * bs + (pos + 1 - lo * bs)) * 2 * d * es
+            if wl.taylor != "none":
+                n_t = lo - len(common)
+                total += n_t * 2 * d * 4
+                if wl.taylor == "order1":
+                    total += n_t * d * d * es
+                if wl.taylor == "hybrid":
+                    total += d * d * es
+    total += wl.B * wl.Hq * 2 * d * es
+    per_row = np.array([total])
+    gbs = float(per_row.sum()) / (ms_fwd * 1e-3) / 1e9
+    rows = wl.B * wl.Hq
+    line = {"metric": "decode step: new tokens/s over every (batch, query head) of the cache",
+            "value": round(rows / ((ms_topk + ms_fwd) * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_topk + ms_fwd, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+            "data": "synthetic",
+            "config": {"workload": f"{wl.name}_decode", "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                       "cache": wl.L, "pos": pos, "d": d, "block": bs, "topk": wl.topk,
+                       "window": wl.window, "taylor": wl.taylor},
+            "roofline": {"bound": "hbm", "kernel": "pisa_decode_fwd", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": None},
+            "kernels": {"decode_topk": {"ms": round(ms_topk, 4)}, "decode_fwd": {"ms": round(ms_fwd, 4),
+                        "bytes": int(per_row.sum())}}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_dit")
+    ap.add_argument("--mode", default="prefill", choices=["prefill", "decode"],
+                    help="decode: one new token per (batch, query head) at the end of the "
+                         "workload's sequence, read as a cache")
     ap.add_argument("--taylor", default=None, choices=["none", "order0", "order1", "hybrid"],
                     help="run the workload with another treatment of the non-kept blocks "
                          "(reported as workload <name>_<mode>)")
@@ -177,6 +268,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "decode":
+        return decode_bench(args)
 
     import torch
 

@@ -151,7 +151,8 @@ pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[6]);
 pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]);
 
 /* Workspace bytes call `op` needs (0 = block_stats, 1 = indexer_topk,
- * 2 = sparse_attn_fwd).  block_stats needs one for the HYBRID order with bf16
+ * 2 = sparse_attn_fwd, 3 = decode_fwd).  decode_fwd always needs one
+ * (fp32 split-K partials).  block_stats needs one for the HYBRID order with bf16
  * inputs and for routing (fp32 partial sums of the mean first-order matrix and
  * an fp32 copy of it; 16-byte aligned, contents need not be initialised and
  * are garbage afterwards); every other call and mode needs none.  A non-NULL workspace of at least
@@ -210,6 +211,37 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
                                  const void *V, const pisa_stats *stats, const int32_t *idx,
                                  void *O, float *lse, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* ---- decode: one new token per (b, query head) ---------------------------
+ * [HyLRA] section 2.3 (hybrid inference: sensitive layers select the top-k
+ * blocks and pass them on, tolerant layers reuse an earlier layer's lists
+ * and attend to that part of the cache only); [SWA] the w-slot ring buffer.
+ * The token at position pos (0 <= pos < L) is the causal token row t = pos
+ * of the prefill path: p must be causal; L is the capacity of the cache,
+ * whose keys 0 .. pos are valid; group and n_cand are not used.
+ *   q      dtype [B, Hq, d]
+ *   K, V   dtype [B, Hkv, L, d], the cache (ring == 0), or
+ *          dtype [B, Hkv, ring, d], a ring buffer with token i in slot i mod ring
+ *   stats  block statistics of the cache (pisa_block_stats over it); only
+ *          blocks before the row's window range are read: qsel is not used
+ *   idx    int32 [B, Hq, topk + sink] kept lists (ascending not required,
+ *          -1 padded); entries at or past the window range are ignored
+ *   O      dtype [B, Hq, d];  lse  fp32 [B, Hq] or NULL
+ * pisa_decode_topk writes the lists of a sensitive layer: the sinks, then
+ * the top-min(k, |cand| - c0) of candidates [c0, lo) by q . ksel_j
+ * (+ route_lambda * mcov_j), certified exactly as pisa_indexer_topk.
+ * pisa_decode_fwd: exact terms over the listed blocks and the window range
+ * [lo, own] (keys s <= pos), Taylor terms (taylor mode of p) over the other
+ * candidates.  ring > 0: a pure sliding window over the last `ring` tokens
+ * (max(0, pos - ring + 1) .. pos exactly); needs topk == 0, sink == 0,
+ * taylor == NONE and window == ring; idx and stats are not read.
+ * ws: at least pisa_workspace_size(p, 3) bytes (split-K partials). */
+pisa_status pisa_decode_topk(const pisa_params *p, int32_t pos, const void *q, const pisa_stats *stats,
+                             int32_t *idx, hipStream_t stream);
+pisa_status pisa_decode_fwd(const pisa_params *p, int32_t pos, int32_t ring, const void *q,
+                            const void *K, const void *V, const pisa_stats *stats,
+                            const int32_t *idx, void *O, float *lse, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* ---- errors and version -------------------------------------------------- */
 const char *pisa_status_string(pisa_status s);

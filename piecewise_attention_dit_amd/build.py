@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpisa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["pisa_host.cpp", "stats.hip", "indexer.hip", "attn.hip", "attn_blocks.hip", "attn_f32.hip"]
+SOURCES = ["pisa_host.cpp", "stats.hip", "indexer.hip", "attn.hip", "attn_blocks.hip", "attn_f32.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 
 

@@ -1011,6 +1011,32 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   }
 }
 
+// Decode: the kept list of one new token (q [B, Hq, d]) at position pos, a
+// causal token row: sinks, then the top-k of candidates [c0, lo) by q . ksel_j
+// (+ lam mcov_j), as select_row decides it.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void indexer_decode(PisaDims dm, int pos, const T *__restrict__ q,
+                                                     const T *__restrict__ ksel, const float *__restrict__ mcov,
+                                                     int32_t *__restrict__ idx, int32_t *diag) {
+  __shared__ Shared sh;
+  const int row = blockIdx.x;   // b * Hq + h
+  const int b = row / dm.Hq, h = row % dm.Hq;
+  const int hk = h * dm.Hkv / dm.Hq;
+  const T *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
+  int own, lo;
+  const int nc = pisa_row_geometry(dm, pos, &own, &lo);
+  const int c0 = min(dm.sink, nc);
+  const int n_take = min(dm.topk, nc - c0);
+  load_p<T, D>(sh, q + (size_t)row * D);
+  bool sel[kMaxSlots];
+  int cj[kMaxSlots];
+  const float *mb = mcov ? mcov + ((size_t)b * dm.Hkv + hk) * dm.n_blk : nullptr;
+  select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, n_take, mb, dm.route_lambda, sel, cj, diag);
+  int32_t *out = idx + (size_t)row * dm.klist;
+  for (int c = lane_id(); c < c0; c += 64) out[c] = c;
+  write_sorted<kMaxSlots>(sel, cj, out + c0, dm.klist - c0);
+}
+
 __global__ void zero_diag(int32_t *d) {
   if (threadIdx.x < 16) d[threadIdx.x] = 0;
 }
@@ -1051,6 +1077,28 @@ hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const v
 }
 
 }  // namespace
+
+hipError_t launch_decode_topk(const PisaDims &dm, int pos, const void *q, const void *ksel, const float *mcov,
+                              int32_t *idx, int32_t *diag, hipStream_t st) {
+  if (diag) zero_diag<<<1, 64, 0, st>>>(diag);
+  const unsigned grid = (unsigned)dm.B * dm.Hq;
+  if (dm.dtype == 0) {
+    if (dm.d == 64)
+      indexer_decode<uint16_t, 64><<<grid, 64, 0, st>>>(dm, pos, static_cast<const uint16_t *>(q),
+                                                        static_cast<const uint16_t *>(ksel), mcov, idx, diag);
+    else
+      indexer_decode<uint16_t, 128><<<grid, 64, 0, st>>>(dm, pos, static_cast<const uint16_t *>(q),
+                                                         static_cast<const uint16_t *>(ksel), mcov, idx, diag);
+  } else {
+    if (dm.d == 64)
+      indexer_decode<float, 64><<<grid, 64, 0, st>>>(dm, pos, static_cast<const float *>(q),
+                                                     static_cast<const float *>(ksel), mcov, idx, diag);
+    else
+      indexer_decode<float, 128><<<grid, 64, 0, st>>>(dm, pos, static_cast<const float *>(q),
+                                                      static_cast<const float *>(ksel), mcov, idx, diag);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, const float *mcov,
                           int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st) {

@@ -165,8 +165,8 @@ pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes) {
   PisaDims dm;
   PISA_TRY(make_dims(p, &dm));
   if (!bytes) return fail(PISA_E_ARG, "bytes is NULL");
-  if (op < 0 || op > 2) return fail(PISA_E_ARG, "unknown op %d", op);
-  *bytes = op == 0 ? stats_workspace_bytes(dm) : 0;
+  if (op < 0 || op > 3) return fail(PISA_E_ARG, "unknown op %d", op);
+  *bytes = op == 0 ? stats_workspace_bytes(dm) : op == 3 ? decode_workspace_bytes(dm) : 0;
   return PISA_OK;
 }
 
@@ -241,6 +241,55 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
   return launched(launch_attn(dm, Q, K, V, ty ? stats->kbar : nullptr, ty ? stats->vsum : nullptr,
                               ty ? stats->HT : nullptr, idx, O, lse, stream),
                   "sparse_attn_fwd");
+}
+
+pisa_status pisa_decode_topk(const pisa_params *p, int32_t pos, const void *q, const pisa_stats *stats,
+                             int32_t *idx, hipStream_t stream) {
+  PisaDims dm;
+  PISA_TRY(make_dims(p, &dm));
+  if (!dm.causal) return fail(PISA_E_ARG, "decode needs causal attention");
+  if (pos < 0 || pos >= dm.L) return fail(PISA_E_ARG, "pos %d outside the cache [0, %d)", pos, dm.L);
+  PISA_TRY(check_ptr(q, "q", true));
+  if (!stats) return fail(PISA_E_ARG, "stats is NULL");
+  PISA_TRY(check_ptr(stats->ksel, "stats.ksel", true));
+  PISA_TRY(check_ptr(stats->mcov, "stats.mcov", dm.route_lambda > 0.f));
+  PISA_TRY(check_ptr(idx, "idx", dm.klist > 0));
+  if (dm.klist == 0) return PISA_OK;
+  return launched(launch_decode_topk(dm, pos, q, stats->ksel, dm.route_lambda > 0.f ? stats->mcov : nullptr, idx,
+                                     nullptr, stream),
+                  "decode_topk");
+}
+
+pisa_status pisa_decode_fwd(const pisa_params *p, int32_t pos, int32_t ring, const void *q, const void *K,
+                            const void *V, const pisa_stats *stats, const int32_t *idx, void *O, float *lse,
+                            void *ws, size_t ws_bytes, hipStream_t stream) {
+  PisaDims dm;
+  PISA_TRY(make_dims(p, &dm));
+  if (!dm.causal) return fail(PISA_E_ARG, "decode needs causal attention");
+  if (pos < 0 || pos >= dm.L) return fail(PISA_E_ARG, "pos %d outside the cache [0, %d)", pos, dm.L);
+  if (ring < 0) return fail(PISA_E_ARG, "ring must be >= 0");
+  if (ring > 0 && (dm.topk != 0 || dm.sink != 0 || dm.taylor != PISA_TAYLOR_NONE || dm.window != ring))
+    return fail(PISA_E_ARG, "a ring buffer holds a pure sliding window: topk = sink = 0, taylor NONE, window = ring");
+  PISA_TRY(check_ptr(q, "q", true));
+  PISA_TRY(check_ptr(K, "K", true));
+  PISA_TRY(check_ptr(V, "V", true));
+  PISA_TRY(check_ptr(O, "O", true));
+  PISA_TRY(check_ptr(lse, "lse", false));
+  PISA_TRY(check_ptr(idx, "idx", ring == 0 && dm.klist > 0));
+  const bool ty = dm.taylor != PISA_TAYLOR_NONE;
+  if (ty) {
+    if (!stats) return fail(PISA_E_ARG, "stats is NULL but taylor != NONE");
+    PISA_TRY(check_ptr(stats->kbar, "stats.kbar", true));
+    PISA_TRY(check_ptr(stats->vsum, "stats.vsum", true));
+    PISA_TRY(check_ptr(stats->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
+  }
+  const size_t need = decode_workspace_bytes(dm);
+  PISA_TRY(check_ws(ws, ws_bytes, need));
+  if (!aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
+  dm.topk = dm.klist;   // the kernels take topk as the width of a kept list
+  return launched(launch_decode(dm, pos, ring, q, K, V, ty ? stats->kbar : nullptr, ty ? stats->vsum : nullptr,
+                                ty ? stats->HT : nullptr, ring == 0 ? idx : nullptr, O, lse, ws, stream),
+                  "decode_fwd");
 }
 
 }  // extern "C"

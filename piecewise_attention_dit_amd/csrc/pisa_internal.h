@@ -72,6 +72,13 @@ hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, 
                               void *ws, hipStream_t st);
 hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
                           const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);
+// decode (one new token per row): split-K partials in a workspace, then a merge
+size_t decode_workspace_bytes(const PisaDims &dm);
+hipError_t launch_decode(const PisaDims &dm, int pos, int ring, const void *q, const void *K, const void *V,
+                         const float *kbar, const float *vsum, const void *HT, const int32_t *idx, void *O,
+                         float *lse, void *ws, hipStream_t st);
+hipError_t launch_decode_topk(const PisaDims &dm, int pos, const void *q, const void *ksel, const float *mcov,
+                              int32_t *idx, int32_t *diag, hipStream_t st);
 hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const void *V,
                        const float *kbar, const float *vsum, const void *HT, const int32_t *idx,
                        void *O, float *lse, hipStream_t st);

@@ -59,8 +59,12 @@ def lib() -> ctypes.CDLL:
         L.pisa_block_stats.argtypes = [P, vp, vp, vp, S, vp, sz, vp]
         L.pisa_indexer_topk.argtypes = [P, vp, S, vp, vp, vp, sz, vp]
         L.pisa_sparse_attn_fwd.argtypes = [P, vp, vp, vp, S, vp, vp, vp, vp, sz, vp]
+        i32 = ctypes.c_int32
+        L.pisa_decode_topk.argtypes = [P, i32, vp, S, vp, vp]
+        L.pisa_decode_fwd.argtypes = [P, i32, i32, vp, vp, vp, S, vp, vp, vp, vp, sz, vp]
         for f in ("pisa_validate", "pisa_stats_layout", "pisa_index_layout", "pisa_workspace_size",
-                  "pisa_block_stats", "pisa_indexer_topk", "pisa_sparse_attn_fwd"):
+                  "pisa_block_stats", "pisa_indexer_topk", "pisa_sparse_attn_fwd", "pisa_decode_topk",
+                  "pisa_decode_fwd"):
             getattr(L, f).restype = ctypes.c_int
         L.pisa_status_string.argtypes = [ctypes.c_int]
         L.pisa_status_string.restype = ctypes.c_char_p
@@ -194,6 +198,35 @@ def sparse_attn_fwd(p: Params, q, k, v, stats: dict, idx, out=None, lse=None, wa
     cs = _cstats(stats)
     _check(lib().pisa_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
                                       _ptr(idx), _ptr(out), _ptr(lse), None, 0, _stream(stream)))
+    return out, lse
+
+
+def decode_topk(p: Params, pos: int, q, stats: dict, idx=None, stream=None):
+    """Kept lists [B, Hq, topk + sink] of the new tokens q [B, Hq, d] at
+    position pos of the cache the statistics describe."""
+    if idx is None:
+        idx = torch.empty((p.B, p.Hq, p.topk + p.sink), dtype=torch.int32, device=q.device)
+    cs = _cstats(stats)
+    _check(lib().pisa_decode_topk(ctypes.byref(p), int(pos), _ptr(q), ctypes.byref(cs), _ptr(idx),
+                                  _stream(stream)))
+    return idx
+
+
+def decode_fwd(p: Params, pos: int, q, k, v, stats=None, idx=None, ring: int = 0, out=None, lse=None,
+               want_lse=True, ws=None, stream=None):
+    """One new token per (b, query head) at position pos: q [B, Hq, d] against
+    the cache k, v [B, Hkv, L, d] (or a ring of `ring` slots)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.B, p.Hq), dtype=torch.float32, device=q.device)
+    need = workspace_size(p, 3)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cs = _cstats(stats) if stats is not None else None
+    _check(lib().pisa_decode_fwd(ctypes.byref(p), int(pos), int(ring), _ptr(q), _ptr(k), _ptr(v),
+                                 ctypes.byref(cs) if cs is not None else None, _ptr(idx), _ptr(out), _ptr(lse),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
     return out, lse
 
 

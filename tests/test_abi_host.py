@@ -145,3 +145,20 @@ def test_launch_calls_reject_before_launch():
     assert L.pisa_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
                                   0, None) == pisa.PISA_E_ARG     # stats NULL with Taylor
     assert L.pisa_validate(None) == pisa.PISA_E_ARG
+    # decode: causal only, pos inside the cache, ring only for a pure window, workspace
+    dc = _p(causal=True, window=128, topk=2)
+    ws_need = pisa.workspace_size(dc, 3)
+    assert ws_need > 0
+    dfwd = lambda pp, pos=5, ring=0, ws=FAKE, wsb=ws_need: L.pisa_decode_fwd(
+        ctypes.byref(pp), pos, ring, FAKE, FAKE, FAKE, ctypes.byref(st), FAKE, FAKE, None, ws, wsb, None)
+    assert dfwd(_p(causal=False)) == pisa.PISA_E_ARG and b"causal" in L.pisa_last_error()
+    assert dfwd(dc, pos=1000) == pisa.PISA_E_ARG and b"pos" in L.pisa_last_error()
+    assert dfwd(dc, pos=-1) == pisa.PISA_E_ARG
+    assert dfwd(dc, ring=128) == pisa.PISA_E_ARG and b"ring" in L.pisa_last_error()
+    assert dfwd(dc, wsb=ws_need - 4) == pisa.PISA_E_WORKSPACE
+    assert dfwd(dc, ws=FAKE + 4) == pisa.PISA_E_ARG
+    ring_ok = _p(causal=True, window=96, topk=0, taylor="none")
+    assert L.pisa_decode_fwd(ctypes.byref(ring_ok), 5, 96, FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                             ws_need, None) == pisa.PISA_E_ARG          # O NULL, after the ring checks pass
+    assert b"O is NULL" in L.pisa_last_error()
+    assert L.pisa_decode_topk(ctypes.byref(dc), 5, FAKE, ctypes.byref(st), None, None) == pisa.PISA_E_ARG
