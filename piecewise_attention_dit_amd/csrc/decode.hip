@@ -12,12 +12,14 @@
 // s <= pos), Taylor terms over the other candidates [0, lo).
 //
 // One query row offers no matrix shape: the work is HBM-bound streaming of
-// key/value rows (and Taylor statistics), done on the VALU.  Split-K: the
-// row's blocks are dealt to NW = 4 S workers (S workgroups of four waves);
-// a worker keeps its own online-softmax state and writes a partial
-// (m, l, A, o[d]) to the workspace, and decode_combine merges the partials
-// of a row in worker order (deterministic), adding the hybrid order's
-// (scale sum alpha) q Hbar once per row.
+// key/value rows (and Taylor statistics), done on the VALU.  The query heads
+// of a kv head are served together, so each key and value row is read once
+// for all of them.  Split-K: the kv head's blocks are dealt to NW = 4 S
+// workers (S workgroups of four waves); a worker keeps each head's
+// online-softmax state and writes its partials (m, l, A, o[d]) to the
+// workspace, and decode_combine merges the partials of a row in worker order
+// (deterministic), adding the hybrid order's (scale sum alpha) q Hbar once
+// per row.
 #include "device_common.h"
 #include "pisa_internal.h"
 
@@ -33,16 +35,8 @@ PISA_DEV float ld(const T *p) {
   else return *p;
 }
 
-PISA_DEV float wsum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-PISA_DEV float wmax(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
+PISA_DEV float wsum(float v) { return wave_sum_xl(v); }
+PISA_DEV float wmax(float v) { return wave_max_xl(v); }
 
 // dot of the fp32 row vector q (LDS) with a length-D row of T
 template <typename T, int D>
@@ -70,7 +64,40 @@ PISA_DEV float dot_row(const float *q, const T *row) {
 }
 
 constexpr int kDecWaves = 4;
-constexpr int kMaxList = 64;
+constexpr int kRM = 8;   // query heads per kv head, at most
+
+// eight consecutive elements of a row as fp32
+template <typename T>
+PISA_DEV void load8(const T *p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo(w[i]);
+      v[2 * i + 1] = bf16hi(w[i]);
+    }
+  } else {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(p), y = *reinterpret_cast<const f32x4_t *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = x[i];
+      v[4 + i] = y[i];
+    }
+  }
+}
+
+// EPL consecutive elements of a row as fp32
+template <typename T, int EPL>
+PISA_DEV void load_e(const T *p, float (&v)[EPL]) {
+  if constexpr (sizeof(T) == 2 && EPL == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+    v[0] = bf16lo(w);
+    v[1] = bf16hi(w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = ld(p + i);
+  }
+}
 
 struct DecArgs {
   PisaDims dm;
@@ -82,162 +109,306 @@ struct DecArgs {
   float *part;   // [rows][workers][4 + d]: m, l, A, pad, o
 };
 
-// Worker state: o holds features EPL * l .. EPL * l + EPL - 1.
-template <int D>
-struct Acc {
-  static constexpr int EPL = D / 64;
-  float m = kNegInfD, l = 0.f, A = 0.f, o[EPL] = {};
-  PISA_DEV void rescale(float m_new) {
-    const float c = m == kNegInfD ? 0.f : exp2f(m - m_new);
-    l *= c;
-    A *= c;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[i] *= c;
-    m = m_new;
-  }
-};
+PISA_DEV float readl(float v, int k) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k));
+}
 
+// A worker (one wave) of the kv head's group: the online-softmax state of
+// each query head r < R of the kv head, lane l holding features
+// EPL l .. EPL l + EPL - 1.  Key and value rows, Taylor statistics and H_j
+// are read once for all R heads; a head only takes the terms of its own
+// kept set (hmask / tmask).
 template <typename T, int D, int BS>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
   constexpr int EPL = D / 64;
-  __shared__ float qs[D];
-  __shared__ uint32_t kept_bits[32];   // blocks of the kept list (n_blk <= 1024)
-  __shared__ int elist[kMaxList + 1024];   // exact blocks of the row
+  __shared__ float qs[kRM][D];
+  __shared__ uint32_t kbits[kRM][32];   // per head: its kept blocks before the window range
+  __shared__ uint32_t ubits[32];
+  __shared__ int elist[1024];            // exact blocks of any head (n_blk <= 1024)
   __shared__ int n_exact;
   const PisaDims &dm = a.dm;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  const int row = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
-  const int b = row / dm.Hq, h = row % dm.Hq, hk = h * dm.Hkv / dm.Hq;
+  const int R = dm.ratio;
+  const int grp = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+  const int b = grp / dm.Hkv, hk = grp % dm.Hkv;
+  const int row0 = b * dm.Hq + hk * R;   // rows row0 .. row0 + R - 1
   const int NWK = a.splits * kDecWaves, wk = split * kDecWaves + w;
   const int pos = a.pos;
   const float sl2 = dm.scale * kLog2eD;
-  const T *Q = static_cast<const T *>(a.q) + (size_t)row * D;
-  for (int c = tid; c < D; c += kDecWaves * 64) qs[c] = ld(Q + c);
+  const T *Q = static_cast<const T *>(a.q) + (size_t)row0 * D;
+  for (int i = tid; i < R * D; i += kDecWaves * 64) qs[i / D][i % D] = ld(Q + i);
   const bool ring = a.ring > 0;
   int own, lo;
   const int nc = ring ? 0 : pisa_row_geometry(dm, pos, &own, &lo);
-  if (tid < 32) kept_bits[tid] = 0u;
+  for (int i = tid; i < kRM * 32; i += kDecWaves * 64) kbits[i / 32][i % 32] = 0u;
+  if (tid < 32) ubits[tid] = 0u;
   __syncthreads();
-  if (tid == 0) {
+  // the heads' kept blocks before the window range, as bitmaps (every thread
+  // one list entry; the range itself is kept anyway, entries past it are not
+  // attended)
+  if (!ring && a.idx)
+    for (int i = tid; i < R * dm.topk; i += kDecWaves * 64) {
+      const int r = i / dm.topk;
+      const int j = a.idx[(size_t)(row0 + r) * dm.topk + i % dm.topk];
+      if (j >= 0 && j < lo) {
+        atomicOr(&kbits[r][j >> 5], 1u << (j & 31));
+        atomicOr(&ubits[j >> 5], 1u << (j & 31));
+      }
+    }
+  __syncthreads();
+  if (tid == 0) {   // exact blocks of any head: the union, then the window range
     int n = 0;
     if (!ring) {
-      const int32_t *list = a.idx ? a.idx + (size_t)row * dm.topk : nullptr;
-      for (int i = 0; i < dm.topk && list && list[i] >= 0; ++i) {
-        const int j = list[i];
-        // kept blocks before the window range, each once (the range itself is
-        // kept anyway; entries past it are not attended)
-        if (j < lo && !((kept_bits[j >> 5] >> (j & 31)) & 1u)) {
-          kept_bits[j >> 5] |= 1u << (j & 31);
-          elist[n++] = j;
-        }
-      }
+      for (int wd = 0; wd < 32; ++wd)
+        for (uint32_t u = ubits[wd]; u; u &= u - 1) elist[n++] = wd * 32 + __builtin_ctz(u);
       for (int j = lo; j <= own; ++j) elist[n++] = j;
     }
     n_exact = n;
   }
   __syncthreads();
-  Acc<D> acc;
+  float m[kRM], L[kRM], A[kRM], o[kRM][EPL];
+#pragma unroll
+  for (int r = 0; r < kRM; ++r) {
+    m[r] = kNegInfD;
+    L[r] = A[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[r][i] = 0.f;
+  }
+  auto rescale = [&](int r, float mn) {
+    const float c = m[r] == kNegInfD ? 0.f : exp2f(m[r] - mn);
+    L[r] *= c;
+    A[r] *= c;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[r][i] *= c;
+    m[r] = mn;
+  };
   const size_t kvrows = ring ? (size_t)a.ring : (size_t)dm.L;
   const T *Kh = static_cast<const T *>(a.K) + (size_t)(b * dm.Hkv + hk) * kvrows * D;
   const T *Vh = static_cast<const T *>(a.V) + (size_t)(b * dm.Hkv + hk) * kvrows * D;
 
-  // exact keys [k0, k0 + 64) (all <= pos), rows at slot(key)
-  auto exact64 = [&](int k0, int kend) {
+  // exact keys [k0, kend) (at most 64, all <= pos) for the heads of hmask
+  auto chunk = [&](int k0, int kend, uint32_t hmask) {
     const int n = k0 + l;
     const bool ok = n < kend;
-    const int slot = ring ? n % a.ring : n;
-    const float x = ok ? dot_row<T, D>(qs, Kh + (size_t)slot * D) * sl2 : kNegInfD;
-    const float mx = wmax(x);
-    if (mx > acc.m) acc.rescale(mx);
-    const float p = ok ? exp2f(x - acc.m) : 0.f;
-    acc.l += wsum(p);
-    const int nk = min(64, kend - k0);
-    for (int kk = 0; kk < nk; ++kk) {
-      const float pk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), kk));
-      const int sl = ring ? (k0 + kk) % a.ring : k0 + kk;
-      const T *vr = Vh + (size_t)sl * D + EPL * l;
+    const int nk = kend - k0;
+    // every value entry of this lane for the chunk, issued before the scores
+    // (rows past the chunk repeat its last row: their weights are zero)
+    float vv[64][EPL];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) acc.o[i] = fmaf(pk, ld(vr + i), acc.o[i]);
+    for (int i = 0; i < 64; ++i) {
+      const int kk = k0 + min(i, nk - 1);
+      load_e<T, EPL>(Vh + (size_t)(ring ? kk % a.ring : kk) * D + EPL * l, vv[i]);
+    }
+    float x[kRM];
+#pragma unroll
+    for (int r = 0; r < kRM; ++r) x[r] = 0.f;
+    if (ok) {
+      const T *kr = Kh + (size_t)(ring ? n % a.ring : n) * D;
+      for (int c = 0; c < D; c += 8) {
+        float kv[8];
+        load8(kr + c, kv);
+#pragma unroll
+        for (int r = 0; r < kRM; ++r) {
+          if (r >= R) break;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[r] = fmaf(qs[r][c + i], kv[i], x[r]);
+        }
+      }
+    }
+    float p[kRM];
+#pragma unroll
+    for (int r = 0; r < kRM; ++r) {
+      p[r] = 0.f;
+      if (r >= R || !((hmask >> r) & 1u)) continue;
+      const float xs = ok ? x[r] * sl2 : kNegInfD;
+      const float mx = wmax(xs);
+      if (mx > m[r]) rescale(r, mx);
+      p[r] = ok ? exp2f(xs - m[r]) : 0.f;
+      L[r] += wsum(p[r]);
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+#pragma unroll
+      for (int r = 0; r < kRM; ++r) {
+        if (r >= R || !((hmask >> r) & 1u)) continue;
+        const float pk = readl(p[r], i);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(pk, vv[i][e], o[r][e]);
+      }
     }
   };
 
   if (ring) {
     // the last ring tokens: max(0, pos - ring + 1) .. pos, 64-key chunks dealt to workers
     const int t0 = max(0, pos - a.ring + 1);
-    for (int k0 = t0 + wk * 64; k0 <= pos; k0 += NWK * 64) exact64(k0, pos + 1);
+    for (int k0 = t0 + wk * 64; k0 <= pos; k0 += NWK * 64) chunk(k0, min(k0 + 64, pos + 1), 0xFFu);
   } else {
-    // exact blocks of the row, dealt to the workers block by block
+    // exact blocks of the kv head's rows, dealt to the workers block by block
     for (int e = wk; e < n_exact; e += NWK) {
       const int j = elist[e];
+      uint32_t hm = 0;
+      for (int r = 0; r < R; ++r)
+        if (j >= lo || ((kbits[r][j >> 5] >> (j & 31)) & 1u)) hm |= 1u << r;
       const int kend = min(min(dm.L, (j + 1) * BS), pos + 1);
-      for (int k0 = j * BS; k0 < kend; k0 += 64) exact64(k0, kend);
+      for (int k0 = j * BS; k0 < kend; k0 += 64) chunk(k0, min(k0 + 64, kend), hm);
     }
-    // Taylor blocks: candidates [0, lo) not kept, lane = block, 64 per batch
+    // Taylor blocks: candidates [0, lo); lane = block, 64 per batch
     if (dm.taylor != 0 && nc > 0) {
       const size_t soff = (size_t)(b * dm.Hkv + hk) * dm.n_blk;
       const float *kb = a.kbar + soff * D, *vs = a.vsum + soff * D;
       const bool order1 = dm.taylor == 2;
       for (int base = 0; base * NWK < nc; base += 64) {
         const int j = wk + (base + l) * NWK;
-        const bool ok = j < nc && !((kept_bits[j >> 5] >> (j & 31)) & 1u);
-        const float x = ok ? dot_row<float, D>(qs, kb + (size_t)j * D) * sl2 : kNegInfD;
-        const float mx = wmax(x);
-        if (mx == kNegInfD) continue;
-        if (mx > acc.m) acc.rescale(mx);
-        const float al = ok ? exp2f(x - acc.m) : 0.f;
-        const float asum = wsum(al);
-        acc.l = fmaf(asum, (float)BS, acc.l);   // candidate blocks lie before the window: complete
-        acc.A += asum;
-        for (int kk = 0; kk < 64; ++kk) {
-          const float ak = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, al), kk));
-          if (ak == 0.f) continue;
-          const int jk = __builtin_amdgcn_readlane(j, kk);
-          const float *vr = vs + (size_t)jk * D + EPL * l;
+        const bool in = j < nc;
+        float x[kRM];
 #pragma unroll
-          for (int i = 0; i < EPL; ++i) acc.o[i] = fmaf(ak, vr[i], acc.o[i]);
-          if (order1) {   // + alpha scale q H_j: features of this lane, rows of H_j^T
-            const T *Hj = static_cast<const T *>(a.HT) + (soff + jk) * D * D;
+        for (int r = 0; r < kRM; ++r) x[r] = 0.f;
+        if (in) {
+          for (int c = 0; c < D; c += 8) {
+            float kv[8];
+            load8(kb + (size_t)j * D + c, kv);
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-              const float u = dot_row<T, D>(qs, Hj + (size_t)(EPL * l + i) * D);
-              acc.o[i] = fmaf(ak * dm.scale, u, acc.o[i]);
+            for (int r = 0; r < kRM; ++r) {
+              if (r >= R) break;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) x[r] = fmaf(qs[r][c + i], kv[i], x[r]);
             }
+          }
+        }
+        float al[kRM];
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < kRM; ++r) {
+          al[r] = 0.f;
+          if (r >= R) continue;
+          const bool t = in && !((kbits[r][j >> 5] >> (j & 31)) & 1u);
+          const float xs = t ? x[r] * sl2 : kNegInfD;
+          const float mx = wmax(xs);
+          if (mx == kNegInfD) continue;
+          if (mx > m[r]) rescale(r, mx);
+          al[r] = t ? exp2f(xs - m[r]) : 0.f;
+          const float s = wsum(al[r]);
+          L[r] = fmaf(s, (float)BS, L[r]);   // candidate blocks lie before the window: complete
+          A[r] += s;
+          any = true;
+        }
+        if (!any) continue;
+        const int nb = min(64, (nc - wk + NWK - 1) / NWK - base);   // blocks of this batch
+        for (int k1 = 0; k1 < nb; k1 += 16) {
+          float vv[16][EPL];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int jk = __builtin_amdgcn_readlane(j, min(k1 + i, 63));
+            if (k1 + i < nb) load_e<float, EPL>(vs + (size_t)jk * D + EPL * l, vv[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (k1 + i >= nb) break;
+            float ak[kRM];
+            bool use = false;
+#pragma unroll
+            for (int r = 0; r < kRM; ++r) {
+              ak[r] = r < R ? readl(al[r], k1 + i) : 0.f;
+              use |= ak[r] != 0.f;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(ak[r], vv[i][e], o[r][e]);
+            }
+            if (!order1 || !use) continue;
+            // + alpha scale q H_j for every head: rows EPL l .. of H_j^T read once
+            const int jk = __builtin_amdgcn_readlane(j, k1 + i);
+            const T *Hj = static_cast<const T *>(a.HT) + (soff + jk) * D * D + (size_t)EPL * l * D;
+            float u[kRM][EPL];
+#pragma unroll
+            for (int r = 0; r < kRM; ++r)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) u[r][e] = 0.f;
+            for (int c = 0; c < D; c += 8) {
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) {
+                float hv[8];
+                load8(Hj + (size_t)e * D + c, hv);
+#pragma unroll
+                for (int r = 0; r < kRM; ++r) {
+                  if (r >= R) break;
+#pragma unroll
+                  for (int t = 0; t < 8; ++t) u[r][e] = fmaf(qs[r][c + t], hv[t], u[r][e]);
+                }
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < kRM; ++r)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(ak[r] * dm.scale, u[r][e], o[r][e]);
           }
         }
       }
     }
   }
-  float *out = a.part + ((size_t)row * NWK + wk) * (4 + D);
-  if (l == 0) {
-    out[0] = acc.m;
-    out[1] = acc.l;
-    out[2] = acc.A;
-  }
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) out[4 + EPL * l + i] = acc.o[i];
+  for (int r = 0; r < kRM; ++r) {
+    if (r >= R) break;
+    float *out = a.part + ((size_t)(row0 + r) * NWK + wk) * (4 + D);
+    if (l == 0) {
+      out[0] = m[r];
+      out[1] = L[r];
+      out[2] = A[r];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[4 + EPL * l + e] = o[r][e];
+  }
 }
 
-// one wave per row: merge the workers' partials in order, add the hybrid
-// term, O = N / D in the dtype, lse
+// one wave per row: merge the workers' partials in worker order (lane i
+// takes partial i for the scalars), add the hybrid term, O = N / D in the
+// dtype, lse
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine(DecArgs a, void *O, float *lse) {
   constexpr int EPL = D / 64;
+  constexpr int PW = 4 + D;
   __shared__ float qs[D];
+  __shared__ float cw[128];   // weight of each partial
   const PisaDims &dm = a.dm;
   const int row = blockIdx.x, l = threadIdx.x;
-  const int NWK = a.splits * kDecWaves;
-  const float *pr = a.part + (size_t)row * NWK * (4 + D);
-  float m = kNegInfD;
-  for (int i = 0; i < NWK; ++i) m = fmaxf(m, pr[(size_t)i * (4 + D)]);
-  float L = 0.f, A = 0.f, o[EPL] = {};
-  for (int i = 0; i < NWK; ++i) {
-    const float *p = pr + (size_t)i * (4 + D);
-    if (p[0] == kNegInfD) continue;
-    const float c = exp2f(p[0] - m);
-    L = fmaf(c, p[1], L);
-    A = fmaf(c, p[2], A);
+  const int NWK = a.splits * kDecWaves;   // <= 128
+  const float *pr = a.part + (size_t)row * NWK * PW;
+  float mi[2] = {kNegInfD, kNegInfD}, li[2] = {0.f, 0.f}, ai[2] = {0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = fmaf(c, p[4 + EPL * l + e], o[e]);
+  for (int u = 0; u < 2; ++u) {
+    const int i = l + 64 * u;
+    if (i < NWK) {
+      mi[u] = pr[(size_t)i * PW];
+      li[u] = pr[(size_t)i * PW + 1];
+      ai[u] = pr[(size_t)i * PW + 2];
+    }
+  }
+  const float m = wmax(fmaxf(mi[0], mi[1]));
+  float Ls = 0.f, As = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = l + 64 * u;
+    const float c = mi[u] == kNegInfD ? 0.f : exp2f(mi[u] - m);
+    if (i < NWK) cw[i] = c;
+    Ls = fmaf(c, li[u], Ls);
+    As = fmaf(c, ai[u], As);
+  }
+  // fixed-order tree sums (the same for every run)
+  const float L = wsum(Ls), A = wsum(As);
+  __syncthreads();
+  float o[EPL] = {};
+  for (int i0 = 0; i0 < NWK; i0 += 8) {
+    float v[8][EPL];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (i0 + t < NWK)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[t][e] = pr[(size_t)(i0 + t) * PW + 4 + EPL * l + e];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (i0 + t >= NWK) break;
+      const float c = cw[i0 + t];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(c, v[t][e], o[e]);
+    }
   }
   if (dm.taylor == 3 && A > 0.f) {   // hybrid: + (scale sum alpha) q Hbar
     const int b = row / dm.Hq, h = row % dm.Hq, hk = h * dm.Hkv / dm.Hq;
@@ -265,7 +436,7 @@ __global__ __launch_bounds__(64) void decode_combine(DecArgs a, void *O, float *
 template <typename T, int D, int BS>
 hipError_t launch_t(const DecArgs &a, void *O, float *lse, hipStream_t st) {
   const int rows = a.dm.B * a.dm.Hq;
-  decode_partial<T, D, BS><<<(unsigned)rows * a.splits, kDecWaves * 64, 0, st>>>(a);
+  decode_partial<T, D, BS><<<(unsigned)a.dm.B * a.dm.Hkv * a.splits, kDecWaves * 64, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_combine<T, D><<<(unsigned)rows, 64, 0, st>>>(a, O, lse);
@@ -275,9 +446,9 @@ hipError_t launch_t(const DecArgs &a, void *O, float *lse, hipStream_t st) {
 }  // namespace
 
 int decode_splits(const PisaDims &dm) {
-  const int rows = dm.B * dm.Hq;
-  int s = (512 + rows - 1) / rows;
-  return s < 1 ? 1 : (s > 16 ? 16 : s);
+  const int groups = dm.B * dm.Hkv;   // one group of workgroups per (batch, kv head)
+  int s = (1024 + groups - 1) / groups;
+  return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
 size_t decode_workspace_bytes(const PisaDims &dm) {

@@ -140,6 +140,27 @@ PISA_DEV float pair_sum_f(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- wave reductions on the cross-lane data path (DPP row operations and
+// the permlane swaps, no LDS); every lane ends with the same value
+template <int Ctrl>
+PISA_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+template <bool MAX>
+PISA_DEV float wave_reduce_xl(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  v = op(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));   // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+PISA_DEV float wave_max_xl(float v) { return wave_reduce_xl<true>(v); }
+PISA_DEV float wave_sum_xl(float v) { return wave_reduce_xl<false>(v); }
+
 // Make this wave's LDS writes (and LDS atomics) visible to its own later LDS
 // reads, without a workgroup barrier: a memory fence plus a code-motion
 // barrier for the wave.

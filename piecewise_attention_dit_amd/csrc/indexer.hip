@@ -463,23 +463,6 @@ struct PivotLayout {
   static_assert((int)sizeof(Shared) <= kPX * SLD * 4, "select_row's Shared fits in S");
 };
 
-// ---- wave reductions on the cross-lane data path (DPP and permlane swaps)
-template <int Ctrl>
-PISA_DEV float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Ctrl, 0xF, 0xF, false));
-}
-// maximum over the wave, the same in every lane
-PISA_DEV float wave_max_xl(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-
 // Largest threshold t with at least `need` keys >= t (keys of invalid slots
 // are 0 and never counted: every probe is >= 1).  Returns true when exactly
 // `need` keys are >= t, i.e. the top set is unique at 32 bits.  Slots
