@@ -445,9 +445,13 @@ hipError_t launch_t(const DecArgs &a, void *O, float *lse, hipStream_t st) {
 
 }  // namespace
 
+#ifndef PISA_DECODE_WORKGROUPS
+#define PISA_DECODE_WORKGROUPS 1024   // target workgroups of decode_partial over the chip
+#endif
+
 int decode_splits(const PisaDims &dm) {
   const int groups = dm.B * dm.Hkv;   // one group of workgroups per (batch, kv head)
-  int s = (1024 + groups - 1) / groups;
+  int s = (PISA_DECODE_WORKGROUPS + groups - 1) / groups;
   return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 

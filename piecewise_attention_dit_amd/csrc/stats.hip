@@ -634,8 +634,56 @@ __global__ __launch_bounds__(kStatsThreads) void q_pool(PisaDims dm, const T *__
   *reinterpret_cast<u32x4_t *>(qsel + (size_t)sr * D + ch * EPC) = out;
 }
 
+// query-block pooling (block rows): one workgroup per (b, head, query block);
+// thread (ts, ch) sums the 16-byte chunk ch of every TS-th row from ts in
+// double-double, and the TS partial sums of an element are merged in order.
+template <typename T, int D>
+__global__ __launch_bounds__(kStatsThreads) void q_pool_block(PisaDims dm, const T *__restrict__ Q,
+                                                             T *__restrict__ qsel) {
+  constexpr int EPC = 16 / sizeof(T);          // elements per chunk
+  constexpr int CPR = D / EPC;                 // chunks per row
+  constexpr int TS = kStatsThreads / CPR;      // row slices
+  __shared__ DD part[TS][D];
+  const int tid = threadIdx.x, ch = tid % CPR, ts = tid / CPR;
+  const int r = blockIdx.x % dm.n_sel;
+  const long long bh = blockIdx.x / dm.n_sel;
+  const int t0 = r * dm.bs, t1 = min(dm.L, t0 + dm.bs);
+  const T *src = Q + ((size_t)bh * dm.L) * D + ch * EPC;
+  DD acc[EPC];
+#pragma unroll
+  for (int i = 0; i < EPC; ++i) acc[i] = DD{0.0, 0.0};
+  for (int t = t0 + ts; t < t1; t += TS) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(src + (size_t)t * D);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        dd_add(acc[2 * i], (double)bf16lo(w[i]));
+        dd_add(acc[2 * i + 1], (double)bf16hi(w[i]));
+      } else {
+        dd_add(acc[i], (double)__uint_as_float(w[i]));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPC; ++i) part[ts][ch * EPC + i] = acc[i];
+  __syncthreads();
+  if (tid < D) {
+    DD s = part[0][tid];
+    for (int k = 1; k < TS; ++k) dd_merge(s, part[k][tid]);
+    const double mean = dd_value(s) / (double)(t1 - t0);
+    T *dst = qsel + ((size_t)bh * dm.n_sel + r) * D + tid;
+    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)f64_to_bf16_bits(mean);
+    else *dst = (float)round_to_format(mean, 24);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_q_pool(const PisaDims &dm, const void *Q, void *qsel, hipStream_t st) {
+  if (dm.group == 0) {   // query blocks of 64 or 128 rows
+    q_pool_block<T, D><<<(unsigned)dm.B * dm.Hq * dm.n_sel, kStatsThreads, 0, st>>>(
+        dm, static_cast<const T *>(Q), static_cast<T *>(qsel));
+    return hipGetLastError();
+  }
   constexpr int CPR = D / (16 / sizeof(T));
   const long long total = (long long)dm.B * dm.Hq * dm.n_sel * CPR;
   const unsigned grid = (unsigned)((total + kStatsThreads - 1) / kStatsThreads);
