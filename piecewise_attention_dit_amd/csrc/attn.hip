@@ -333,21 +333,30 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
         }
       }
       const int kbase = j * BS + kh * kStage;
+      // keys past the last token or (causal) past a row's own token: only the
+      // stages that reach them need an element mask
+      const bool edge = kbase + kStage > dm.L || (causal && kbase + kStage - 1 > tw);
       u32x4_t pb[NQ][2][2];
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
+        if (edge && mem[n]) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbase + q * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+              if (key >= dm.L || (causal && key > t[n])) s[n][q][r] = kNegInf;
+            }
+        }
+        // the row's maximum of the raw scores (rows that do not keep the
+        // block take no weight from it: their exponent offset is -inf)
         float mloc = kNegInf;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + q * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool ok = mem[n] && key < dm.L && (!causal || key <= t[n]);
-            const float x = ok ? s[n][q][r] * sl2 : kNegInf;
-            s[n][q][r] = x;
-            mloc = fmaxf(mloc, x);
-          }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+          for (int r = 0; r < 16; r += 2) mloc = fmaxf(fmaxf(mloc, s[n][q][r]), s[n][q][r + 1]);
+        mloc = mem[n] ? mloc * sl2 : kNegInf;
+        mloc = pair_max_f(mloc);
         const bool grow = mloc > m_run[n] + kRescale;   // includes the first visible block
         if (ballot64(grow)) {
           const float corr = grow ? fast_exp2(m_run[n] - mloc) : 1.f;
@@ -356,22 +365,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
           for (int et = 0; et < NE; ++et) oacc[n][et] *= corr;
           m_run[n] = grow ? mloc : m_run[n];
         }
-        const float mref = m_run[n] == kNegInf ? 0.f : m_run[n];
+        const float mneg = mem[n] ? -(m_run[n] == kNegInf ? 0.f : m_run[n]) : kNegInf;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[n][q][r] = fast_exp2(fmaf(s[n][q][r], sl2, mneg));
+        // the row sum of the bf16 weights that P V uses (N and D agree)
         float psum = 0.f;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(s[n][q][r] - mref);
-            s[n][q][r] = p;
-            psum += p;
+          for (int hf = 0; hf < 2; ++hf) {
+            pb[n][q][hf] = pack8(s[n][q], 8 * hf);
+            psum = sum_bf16x8_f(pb[n][q][hf], psum);
           }
-        psum += __shfl_xor(psum, 32);
-        d_run[n] += psum;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) pb[n][q][hf] = pack8(s[n][q], 8 * hf);
+        d_run[n] += pair_sum_f(psum);
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q)

@@ -161,6 +161,24 @@ PISA_DEV float wave_reduce_xl(float v) {
 PISA_DEV float wave_max_xl(float v) { return wave_reduce_xl<true>(v); }
 PISA_DEV float wave_sum_xl(float v) { return wave_reduce_xl<false>(v); }
 
+// max of x and the value of lane l ^ 32 (permlane32 swap, as pair_sum_f)
+PISA_DEV float pair_max_f(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum of eight packed bf16 (a u32x4), accumulated in fp32 with v_dot2c_f32_bf16
+PISA_DEV float sum_bf16x8_f(const u32x4_t &p, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t x = {b[2 * i], b[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+  }
+  return acc;
+}
+
 // Make this wave's LDS writes (and LDS atomics) visible to its own later LDS
 // reads, without a workgroup barrier: a memory fence plus a code-motion
 // barrier for the wave.
