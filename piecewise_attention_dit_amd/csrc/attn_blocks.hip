@@ -357,8 +357,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(sc[q][r], sl2, mneg));
         pc[q][0] = pack8(e, 0);
         pc[q][1] = pack8(e, 8);
-        psum = sum_bf16x8(pc[q][0], psum);
-        psum = sum_bf16x8(pc[q][1], psum);
+        psum = sum_bf16x8_f(pc[q][0], psum);
+        psum = sum_bf16x8_f(pc[q][1], psum);
       }
       return psum;
     };
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       asm volatile("" : "+v"(psum), "+v"(mx));
       // the max moved by more than 2^8 (or the row's first visible step):
       // rescale and recompute this step's weights
-      mx = pair_max(mx);
+      mx = pair_max_f(mx);
       const float ms = cur.mem ? mx * sl2 : kNegInf;
       const bool grow = ms > mold + kRescale;
       if (ballot64(grow)) {
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         for (int et = 0; et < NE; ++et) oacc[et] *= corr;
         psum = weights(sc, cur.mem ? -(m_run == kNegInf ? 0.f : m_run) : kNegInf, pc);
       }
-      d_run += pair_sum(psum);
+      d_run += pair_sum_f(psum);
 #pragma unroll
       for (int q = 0; q < NQT; ++q) {
         pprev[q][0] = pc[q][0];
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
             at[r] = x;
             mx = fmaxf(mx, x);
           }
-          mx = pair_max(mx);
+          mx = pair_max_f(mx);
           const bool grow = mx > m_run + kRescale;
           if (ballot64(grow)) {
             const float corr = grow ? fast_exp2(m_run - mx) : 1.f;
@@ -636,9 +636,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
             apart += al;
             if (order1) alp[en * 32 + lq] = al * dm.scale;
           }
-          dpart = pair_sum(dpart);
+          dpart = pair_sum_f(dpart);
           d_run += dpart;
-          if (hybrid) a_run += pair_sum(apart);
+          if (hybrid) a_run += pair_sum_f(apart);
           u32x4_t ph, pl;
           pack8_split(at, 0, ph, pl);
           // zero order: O^T += Sigma^T alpha^T  (hi*hi + lo*hi + hi*lo)

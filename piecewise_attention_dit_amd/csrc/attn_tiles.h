@@ -110,31 +110,4 @@ PISA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // visits them in the order perm16 (an involution on 0..15).
 PISA_DEV int perm16(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// sum of eight packed bf16, accumulated in fp32 (v_dot2c_f32_bf16 with
-// (1, 1)).  The pairs are taken from a bf16x8 view of the whole vector: a
-// bit_cast of one u32 element inside an unrolled loop was compiled to read
-// element 0 every time.
-PISA_DEV float sum_bf16x8(const u32x4_t &p, float acc) {
-  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2_t x = {b[2 * i], b[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
-  }
-  return acc;
-}
-
-// x combined with the value of lane l ^ 32 (v_permlane32_swap_b32 swaps
-// the upper half of one register with the lower half of another; with both
-// operands x, the two results hold x and its partner on every lane)
-PISA_DEV float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-PISA_DEV float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 }  // namespace pisa_attn

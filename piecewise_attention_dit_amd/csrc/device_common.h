@@ -167,7 +167,10 @@ PISA_DEV float pair_max_f(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// sum of eight packed bf16 (a u32x4), accumulated in fp32 with v_dot2c_f32_bf16
+// sum of eight packed bf16 (a u32x4), accumulated in fp32 (v_dot2c_f32_bf16
+// with (1, 1)).  The pairs are taken from a bf16x8 view of the whole vector:
+// a bit_cast of one u32 element inside an unrolled loop was compiled to read
+// element 0 every time.
 PISA_DEV float sum_bf16x8_f(const u32x4_t &p, float acc) {
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
   const bf16x8_t b = __builtin_bit_cast(bf16x8_t, p);

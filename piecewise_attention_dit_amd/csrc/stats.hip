@@ -21,11 +21,62 @@ namespace {
 constexpr int kStatsThreads = 256;
 
 // ---------------------------------------------------------------------------
-// bf16 K/V statistics with the moment GEMM on MFMA.
-//
-// LDS holds K and V transposed (feature rows, token columns, padded pitch) so
-// that every MFMA operand lane reads 8 consecutive tokens of one feature:
-//   HT[e][c] = sum_n VT[e][n] * KcT[c][n]   (A = VT, B = KcT^T, k = tokens)
+// Exact float64 sums of bf16 values, cheap path.  A bf16 value is an integer
+// of at most 8 bits times 2^(max(E, 1) - 134), E its exponent field, so n
+// values are integer multiples of the smallest nonzero one's quantum and every
+// running sum of them stays below n * 2^(span + 8) of those quanta, span being
+// the spread of max(E, 1) over the nonzero values.  Below 2^53 quanta a plain
+// float64 sum is exact.  The packed u16 max of |bits| and min of |bits| - 1
+// (zeros wrap to 0xFFFF and drop out) give the spread of each half of a word.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+struct SpanCert {
+  u16x2_t amax = {0, 0}, amin = {0xFFFF, 0xFFFF};
+  PISA_DEV void add(uint32_t w) {
+    const u16x2_t a = __builtin_bit_cast(u16x2_t, w & 0x7FFF7FFFu);
+    amax = __builtin_elementwise_max(amax, a);
+    amin = __builtin_elementwise_min(amin, a - u16x2_t{1, 1});
+  }
+  // every partial sum of the half h (0: low bf16) is exact for n <= 2^lg addends
+  PISA_DEV bool exact(int h, int lg) const {
+    const int mx = h ? amax[1] : amax[0], mn = h ? amin[1] : amin[0];
+    if (mn == 0xFFFF) return true;   // all zero
+    const int emax = mx >> 7, emin = max((mn + 1) >> 7, 1);
+    return emax - emin <= 45 - lg;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// bf16 K/V statistics, one workgroup per key block:
+//   * K and V tiles move global -> LDS by DMA, row-major, 16-byte chunks
+//     permuted by vswz (tokens past the sequence end read as zeros);
+//   * lane (feature pair, token class p) sums the tokens t = p (mod PARTS) of
+//     its two features, exactly (certified float64, double-double when the
+//     certificate fails), and the PARTS lanes of a pair merge in order with
+//     cross-lane double-double additions;
+//   * first order: the K tile is centred in place (bf16 of k - kbar, so keys
+//     that all equal their mean give exactly zero), then HT = V^T Kc on MFMA
+//     32x32x16 as T = Kc^T V with both operands read transposed from the
+//     tiles (ds_read_b64_tr_b16), rounded once to bf16, staged in LDS and
+//     written with 16-byte stores.
+template <int D, int BS>
+struct KvCfg {
+  static constexpr int TILE = BS * D * 2;                 // bytes of one K (or V) tile
+  static constexpr int CPW = TILE / 1024 / 4;             // DMA kilobytes per wave and tile
+  static constexpr int NPAIR = D / 2;                     // feature pairs
+  static constexpr int PARTS = kStatsThreads / NPAIR;     // token classes per pair (4 or 8)
+  static constexpr int SEG = BS / PARTS;                  // tokens per lane
+  static constexpr int LG = SEG <= 8 ? 3 : SEG <= 16 ? 4 : 5;
+  static constexpr int NT = D / 32, TPW = NT * NT / 4;    // 32x32 output tiles, per wave
+  static constexpr int OP = D + 4;                        // staging pitch (bf16)
+  static constexpr int STG = D * OP * 2;
+  static constexpr int TILES = 2 * TILE > STG ? 2 * TILE : STG;
+  static constexpr int MEAN = TILES;                      // float [D]: kbar
+  static constexpr int TOTAL = MEAN + D * 4;
+  static_assert(SEG <= 32 && TILE % 4096 == 0, "token split and DMA split");
+  static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
+};
+
 template <int D, int BS>
 __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, const uint16_t *__restrict__ K,
                                                               const uint16_t *__restrict__ V,
@@ -33,158 +84,162 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
                                                               float *__restrict__ kbar,
                                                               float *__restrict__ vsum,
                                                               uint16_t *__restrict__ HT) {
-  constexpr int P = BS + 8;              // LDS pitch in bf16 elements (16-byte pad)
-  constexpr int PARTS = kStatsThreads / D;  // threads per feature in the column sums
-  constexpr int SEG = BS / PARTS;            // tokens per part
-  // kt and vt are carved from one array: the HT output staging (D x (D + 8))
-  // reuses both once the MFMA reads are done.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * D * P];
-  static_assert(2 * P >= D + 8, "output staging must fit in kt + vt");
-  uint16_t *kt = lds;
-  uint16_t *vt = lds + D * P;
-  __shared__ double red[2][PARTS][D][2];
-  __shared__ float kmean32[D];
+  using C = KvCfg<D, BS>;
+  constexpr int PARTS = C::PARTS, SEG = C::SEG, TPW = C::TPW, NT = C::NT, OP = C::OP;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t *kt = lds, *vt = lds + C::TILE;
+  float *kmean = reinterpret_cast<float *>(lds + C::MEAN);
 
-  const int tid = threadIdx.x;
-  const int bid = blockIdx.x;
-  const int j = bid % dm.n_blk;
-  const int bh = bid / dm.n_blk;  // b * Hkv + hk
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, lq = l & 31, hl = l >> 5;
+  const int j = blockIdx.x % dm.n_blk;
+  const int bh = blockIdx.x / dm.n_blk;  // b * Hkv + hk
   const int n = min(BS, dm.L - j * BS);
   const size_t base = ((size_t)bh * dm.L + (size_t)j * BS) * D;
-  const uint16_t *Kb = K + base;
-  const uint16_t *Vb = V + base;
-  const bool taylor = dm.taylor != 0;
+  const bool has_v = dm.taylor != 0, order1 = dm.taylor == 2;
 
-  // ---- load K (and V) transposed into LDS: token pairs x 8-feature chunks.
-  // Lanes run over token pairs fastest so the 4-byte transposed stores of one
-  // instruction spread over distinct banks.
-  constexpr int NPAIR = BS / 2, NCH = D / 8;
-  for (int u = tid; u < NPAIR * NCH; u += kStatsThreads) {
-    const int pr = u % NPAIR, ch = u / NPAIR;
-    const int t0 = 2 * pr;
-    u32x4_t a = {0, 0, 0, 0}, b = {0, 0, 0, 0}, va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-    if (t0 < n) {
-      a = *reinterpret_cast<const u32x4_t *>(Kb + (size_t)t0 * D + ch * 8);
-      if (taylor) va = *reinterpret_cast<const u32x4_t *>(Vb + (size_t)t0 * D + ch * 8);
-    }
-    if (t0 + 1 < n) {
-      b = *reinterpret_cast<const u32x4_t *>(Kb + (size_t)(t0 + 1) * D + ch * 8);
-      if (taylor) vb = *reinterpret_cast<const u32x4_t *>(Vb + (size_t)(t0 + 1) * D + ch * 8);
-    }
+  // ---- 1. tiles: kilobyte c of a tile holds 16-byte chunks 64 c .. 64 c + 63
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int f = ch * 8 + 2 * w;
-      // element f of tokens t0, t0+1 -> one 32-bit word; same for f+1
-      uint32_t k0 = (a[w] & 0xFFFFu) | (b[w] << 16);
-      uint32_t k1 = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-      *reinterpret_cast<uint32_t *>(&kt[f * P + t0]) = k0;
-      *reinterpret_cast<uint32_t *>(&kt[(f + 1) * P + t0]) = k1;
-      if (taylor) {
-        uint32_t v0 = (va[w] & 0xFFFFu) | (vb[w] << 16);
-        uint32_t v1 = (va[w] >> 16) | (vb[w] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t *>(&vt[f * P + t0]) = v0;
-        *reinterpret_cast<uint32_t *>(&vt[(f + 1) * P + t0]) = v1;
-      }
-    }
+  for (int u = 0; u < C::CPW; ++u) {
+    const int c = wave + 4 * u, pos = c * 64 + l;
+    const int row = pos / (D / 8), phys = pos % (D / 8);
+    const int voff = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
+    dma16_buf(K + base, n * D * 2, voff, kt + c * 1024);
+    if (has_v) dma16_buf(V + base, n * D * 2, voff, vt + c * 1024);
   }
+  wait_vmcnt<0>();
   __syncthreads();
 
-  // ---- column sums in float64 (exact cascaded sums), PARTS threads per feature
+  // ---- 2. column sums: lane (pair pr, class p), tokens p, p + PARTS, ...
   {
-    const int f = tid % D, part = tid / D;
-    DD sk = {0.0, 0.0}, sv = {0.0, 0.0};
-    const int t_lo = part * SEG;
-    for (int t = t_lo; t < t_lo + SEG; t += 8) {
-      u32x4_t kw = *reinterpret_cast<const u32x4_t *>(&kt[f * P + t]);
-      u32x4_t vw = taylor ? *reinterpret_cast<const u32x4_t *>(&vt[f * P + t]) : u32x4_t{0, 0, 0, 0};
+    const int pr = wave * (64 / PARTS) + l / PARTS, p = l % PARTS;
+    // the swizzle of row t depends on t & 3 = p & 3 only
+    const int off0 = p * (2 * D) + ((((pr >> 2) ^ vswz<D>(p))) << 4) + (pr & 3) * 4;
+    double sk[2] = {0.0, 0.0}, sv[2] = {0.0, 0.0};
+    SpanCert ck, cv;
+#pragma unroll 8
+    for (int i = 0; i < SEG; ++i) {
+      const int off = off0 + i * PARTS * (2 * D);
+      const uint32_t kw = *reinterpret_cast<const uint32_t *>(kt + off);
+      sk[0] += (double)bf16lo(kw);
+      sk[1] += (double)bf16hi(kw);
+      ck.add(kw);
+      if (has_v) {
+        const uint32_t vw = *reinterpret_cast<const uint32_t *>(vt + off);
+        sv[0] += (double)bf16lo(vw);
+        sv[1] += (double)bf16hi(vw);
+        cv.add(vw);
+      }
+    }
+    DD dk[2], dv[2];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dd_add(sk, (double)bf16lo(kw[w]));
-        dd_add(sk, (double)bf16hi(kw[w]));
-        if (taylor) {
-          dd_add(sv, (double)bf16lo(vw[w]));
-          dd_add(sv, (double)bf16hi(vw[w]));
+    for (int h = 0; h < 2; ++h) {
+      dk[h] = {sk[h], 0.0};
+      dv[h] = {sv[h], 0.0};
+      // a certificate that fails (exponent spread near 45 bits): redo exactly
+      if (!ck.exact(h, C::LG)) {
+        dk[h] = {0.0, 0.0};
+        for (int i = 0; i < SEG; ++i) {
+          const uint32_t kw = *reinterpret_cast<const uint32_t *>(kt + off0 + i * PARTS * (2 * D));
+          dd_add(dk[h], (double)(h ? bf16hi(kw) : bf16lo(kw)));
+        }
+      }
+      if (has_v && !cv.exact(h, C::LG)) {
+        dv[h] = {0.0, 0.0};
+        for (int i = 0; i < SEG; ++i) {
+          const uint32_t vw = *reinterpret_cast<const uint32_t *>(vt + off0 + i * PARTS * (2 * D));
+          dd_add(dv[h], (double)(h ? bf16hi(vw) : bf16lo(vw)));
         }
       }
     }
-    red[0][part][f][0] = sk.hi;
-    red[0][part][f][1] = sk.lo;
-    red[1][part][f][0] = sv.hi;
-    red[1][part][f][1] = sv.lo;
-  }
-  __syncthreads();
-  if (tid < D) {
-    const int f = tid;
-    DD sk = {red[0][0][f][0], red[0][0][f][1]}, sv = {red[1][0][f][0], red[1][0][f][1]};
-    for (int part = 1; part < PARTS; ++part) {
-      DD o = {red[0][part][f][0], red[0][part][f][1]};
-      dd_merge(sk, o);
-      DD ov = {red[1][part][f][0], red[1][part][f][1]};
-      dd_merge(sv, ov);
+    // merge the PARTS classes of a pair (lanes l ^ m), exactly
+#pragma unroll
+    for (int m = 1; m < PARTS; m <<= 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const DD ok = {__shfl_xor(dk[h].hi, m), __shfl_xor(dk[h].lo, m)};
+        dd_merge(dk[h], ok);
+        if (has_v) {
+          const DD ov = {__shfl_xor(dv[h].hi, m), __shfl_xor(dv[h].lo, m)};
+          dd_merge(dv[h], ov);
+        }
+      }
     }
-    const double mean = dd_value(sk) / (double)n;
-    const size_t so = ((size_t)bh * dm.n_blk + j) * D + f;
-    ksel[so] = (uint16_t)f64_to_bf16_bits(mean);
-    const float m32 = (float)mean;
-    kmean32[f] = m32;
-    if (taylor) {
-      kbar[so] = m32;
-      vsum[so] = (float)dd_value(sv);
+    if (p == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int f = 2 * pr + h;
+        const double mean = dd_value(dk[h]) / (double)n;
+        const size_t so = ((size_t)bh * dm.n_blk + j) * D + f;
+        ksel[so] = (uint16_t)f64_to_bf16_bits(mean);
+        const float m32 = (float)mean;
+        kmean[f] = m32;
+        if (has_v) {
+          const float s32 = (float)dd_value(dv[h]);
+          kbar[so] = m32;
+          vsum[so] = s32;
+        }
+      }
     }
   }
-  if (dm.taylor != 2) return;
+  if (!order1) return;
+  __syncthreads();   // the column sums have read the tiles; kbar is in LDS
+
+  // ---- 3. centre the keys in place: bf16(k - kbar), tokens past n stay zero
+  for (int wi = tid; wi < C::TILE / 4; wi += kStatsThreads) {
+    const int byte = wi * 4, row = byte / (2 * D), inrow = byte % (2 * D);
+    const int f = (((inrow >> 4) ^ vswz<D>(row)) << 3) + ((inrow & 15) >> 2) * 2;
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(kt + byte);
+    const float c0 = row < n ? bf16lo(w) - kmean[f] : 0.f;
+    const float c1 = row < n ? bf16hi(w) - kmean[f + 1] : 0.f;
+    *reinterpret_cast<uint32_t *>(kt + byte) = pack_bf16x2(c0, c1);
+  }
   __syncthreads();
 
-  // ---- centre the keys in place (bf16 of k - kbar, padded tokens stay zero)
-  for (int u = tid; u < D * (BS / 2); u += kStatsThreads) {
-    const int f = u / (BS / 2), t0 = 2 * (u % (BS / 2));
-    uint32_t w = *reinterpret_cast<const uint32_t *>(&kt[f * P + t0]);
-    const float m = kmean32[f];
-    float c0 = t0 < n ? bf16lo(w) - m : 0.f;
-    float c1 = t0 + 1 < n ? bf16hi(w) - m : 0.f;
-    *reinterpret_cast<uint32_t *>(&kt[f * P + t0]) = pack_bf16x2(c0, c1);
-  }
-  __syncthreads();
-
-  // ---- HT = VT * KcT^T on MFMA 32x32x16 (k = 16 tokens per step)
-  constexpr int NT = D / 32;                 // output tiles per dimension
-  constexpr int TILES = NT * NT;
-  constexpr int TPW = TILES / (kStatsThreads / 64);  // tiles per wave (4 or 1)
-  const int wave = tid >> 6, l = tid & 63;
+  // ---- 4. first-order moment T = Kc^T V (rows c, columns e) on MFMA
   f32x16_t acc[TPW];
+  const int te = TPW == NT ? wave : wave / NT;   // e tile of this wave
+  {
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = f32x16_t{};
-  const int te = (TPW == NT) ? wave : wave / NT;     // e tile of this wave
+    for (int i = 0; i < TPW; ++i) acc[i] = f32x16_t{};
+    const int srow = (l & 15) >> 2, ecol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
 #pragma unroll
-  for (int ks = 0; ks < BS / 16; ++ks) {
-    const int tok = ks * 16 + (l >> 5) * 8;
-    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&vt[(te * 32 + (l & 31)) * P + tok]);
+    for (int ks = 0; ks < BS / 16; ++ks) {
+      const int rr = ks * 16 + 4 * hl + srow;
+      const u32x4_t b = frag_vt<D>(vt, rr, te * 32 + ecol);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int tc = TPW == NT ? i : wave % NT;
+        acc[i] = mfma32(frag_vt<D>(kt, rr, tc * 32 + ecol), b, acc[i]);
+      }
+    }
+  }
+
+  __syncthreads();   // the MFMA reads of the tiles are done: reuse them for staging
+
+  // ---- 5. HT[e][c] = T[c][e] -> bf16, staged [e][c]
+  uint16_t *ot = reinterpret_cast<uint16_t *>(lds);
+  {
+    const int e = te * 32 + lq;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int tc = (TPW == NT) ? i : wave % NT;
-      const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&kt[(tc * 32 + (l & 31)) * P + tok]);
-      acc[i] = mfma32(a, b, acc[i]);
-    }
-  }
-  __syncthreads();  // kt/vt are reused as the output staging buffer
-  // stage HT rows (e) with c contiguous: lane holds column c = tc*32 + l%32 and
-  // rows e = te*32 + 8*(r/4) + 4*(l/32) + r%4
-  constexpr int OP = D + 8;
-  uint16_t *ot = lds;
+      const int tc = TPW == NT ? i : wave % NT;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tc = (TPW == NT) ? i : wave % NT;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = te * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      ot[e * OP + tc * 32 + (l & 31)] = (uint16_t)f32_to_bf16(acc[i][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = tc * 32 + 8 * g + 4 * hl;
+        u32x2_t o;
+        o[0] = pack_bf16x2(acc[i][4 * g], acc[i][4 * g + 1]);
+        o[1] = pack_bf16x2(acc[i][4 * g + 2], acc[i][4 * g + 3]);
+        *reinterpret_cast<u32x2_t *>(ot + e * OP + c0) = o;
+      }
     }
   }
   __syncthreads();
   uint16_t *Hb = HT + ((size_t)bh * dm.n_blk + j) * D * D;
   for (int u = tid; u < D * D / 8; u += kStatsThreads) {
     const int e = u / (D / 8), c8 = (u % (D / 8)) * 8;
-    *reinterpret_cast<u32x4_t *>(Hb + (size_t)e * D + c8) = *reinterpret_cast<const u32x4_t *>(&ot[e * OP + c8]);
+    const u32x2_t lo2 = *reinterpret_cast<const u32x2_t *>(ot + e * OP + c8);
+    const u32x2_t hi2 = *reinterpret_cast<const u32x2_t *>(ot + e * OP + c8 + 4);
+    *reinterpret_cast<u32x4_t *>(Hb + (size_t)e * D + c8) = u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
   }
 }
 
@@ -694,8 +749,16 @@ hipError_t launch_q_pool(const PisaDims &dm, const void *Q, void *qsel, hipStrea
 template <int D, int BS>
 hipError_t launch_kv_bf16(const PisaDims &dm, const void *K, const void *V, void *ksel, float *kbar,
                           float *vsum, void *HT, hipStream_t st) {
+  using C = KvCfg<D, BS>;
   const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk;
-  kv_stats_bf16<D, BS><<<grid, kStatsThreads, 0, st>>>(
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kv_stats_bf16<D, BS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kv_stats_bf16<D, BS><<<grid, kStatsThreads, C::TOTAL, st>>>(
       dm, static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V), static_cast<uint16_t *>(ksel),
       kbar, vsum, static_cast<uint16_t *>(HT));
   return hipGetLastError();
