@@ -47,43 +47,49 @@ struct SpanCert {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 K/V statistics, one workgroup per key block:
+// bf16 K/V statistics, one workgroup of eight waves per key block (two
+// workgroups fit a CU, so one block's loads overlap another's arithmetic):
 //   * K and V tiles move global -> LDS by DMA, row-major, 16-byte chunks
 //     permuted by vswz (tokens past the sequence end read as zeros);
 //   * lane (feature pair, token class p) sums the tokens t = p (mod PARTS) of
-//     its two features, exactly (certified float64, double-double when the
-//     certificate fails), and the PARTS lanes of a pair merge in order with
-//     cross-lane double-double additions;
-//   * first order: the K tile is centred in place (bf16 of k - kbar, so keys
-//     that all equal their mean give exactly zero), then HT = V^T Kc on MFMA
-//     32x32x16 as T = Kc^T V with both operands read transposed from the
-//     tiles (ds_read_b64_tr_b16), rounded once to bf16, staged in LDS and
-//     written with 16-byte stores.
+//     its two features; key sums exactly (certified float64, double-double
+//     when the certificate fails) and merged across the PARTS lanes of the
+//     pair with exact double-double additions; value sums in float64;
+//   * first order: the K tile is centred in place, 16 bytes at a time (bf16
+//     of k - kbar, so keys that all equal their mean give exactly zero), then
+//     HT = V^T Kc on MFMA 32x32x16 as T = Kc^T V with both operands read
+//     transposed from the tiles (ds_read_b64_tr_b16), rounded once to bf16,
+//     staged in LDS and written with 16-byte stores.
+constexpr int kKvWaves = 8, kKvThreads = 64 * kKvWaves;
+
 template <int D, int BS>
 struct KvCfg {
   static constexpr int TILE = BS * D * 2;                 // bytes of one K (or V) tile
-  static constexpr int CPW = TILE / 1024 / 4;             // DMA kilobytes per wave and tile
+  static constexpr int CPW = TILE / 1024 / kKvWaves;      // DMA kilobytes per wave and tile
   static constexpr int NPAIR = D / 2;                     // feature pairs
-  static constexpr int PARTS = kStatsThreads / NPAIR;     // token classes per pair (4 or 8)
+  static constexpr int PARTS = kKvThreads / NPAIR;        // token classes per pair (8 or 16)
   static constexpr int SEG = BS / PARTS;                  // tokens per lane
-  static constexpr int LG = SEG <= 8 ? 3 : SEG <= 16 ? 4 : 5;
-  static constexpr int NT = D / 32, TPW = NT * NT / 4;    // 32x32 output tiles, per wave
+  static constexpr int LG = SEG <= 4 ? 2 : SEG <= 8 ? 3 : 4;
+  static constexpr int NT = D / 32;                       // 32x32 output tiles per dimension
+  static constexpr int MW = NT * NT < kKvWaves ? NT * NT : kKvWaves;   // waves with MFMA tiles
+  static constexpr int TPW = NT * NT / MW;                // tiles per such wave (same e tile)
   static constexpr int OP = D + 4;                        // staging pitch (bf16)
   static constexpr int STG = D * OP * 2;
   static constexpr int TILES = 2 * TILE > STG ? 2 * TILE : STG;
   static constexpr int MEAN = TILES;                      // float [D]: kbar
   static constexpr int TOTAL = MEAN + D * 4;
-  static_assert(SEG <= 32 && TILE % 4096 == 0, "token split and DMA split");
+  static_assert(SEG >= 4 && SEG <= 16 && TILE % (1024 * kKvWaves) == 0, "token split and DMA split");
+  static_assert(NT % TPW == 0, "a wave's tiles share one e tile");
   static_assert(TOTAL <= 80 * 1024, "two workgroups per CU");
 };
 
 template <int D, int BS>
-__global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, const uint16_t *__restrict__ K,
-                                                              const uint16_t *__restrict__ V,
-                                                              uint16_t *__restrict__ ksel,
-                                                              float *__restrict__ kbar,
-                                                              float *__restrict__ vsum,
-                                                              uint16_t *__restrict__ HT) {
+__global__ __launch_bounds__(kKvThreads) void kv_stats_bf16(PisaDims dm, const uint16_t *__restrict__ K,
+                                                           const uint16_t *__restrict__ V,
+                                                           uint16_t *__restrict__ ksel,
+                                                           float *__restrict__ kbar,
+                                                           float *__restrict__ vsum,
+                                                           uint16_t *__restrict__ HT) {
   using C = KvCfg<D, BS>;
   constexpr int PARTS = C::PARTS, SEG = C::SEG, TPW = C::TPW, NT = C::NT, OP = C::OP;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -97,10 +103,10 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
   const size_t base = ((size_t)bh * dm.L + (size_t)j * BS) * D;
   const bool has_v = dm.taylor != 0, order1 = dm.taylor == 2;
 
-  // ---- 1. tiles: kilobyte c of a tile holds 16-byte chunks 64 c .. 64 c + 63
+  // ---- tiles: kilobyte c of a tile holds 16-byte chunks 64 c .. 64 c + 63
 #pragma unroll
   for (int u = 0; u < C::CPW; ++u) {
-    const int c = wave + 4 * u, pos = c * 64 + l;
+    const int c = wave + kKvWaves * u, pos = c * 64 + l;
     const int row = pos / (D / 8), phys = pos % (D / 8);
     const int voff = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
     dma16_buf(K + base, n * D * 2, voff, kt + c * 1024);
@@ -109,14 +115,14 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
   wait_vmcnt<0>();
   __syncthreads();
 
-  // ---- 2. column sums: lane (pair pr, class p), tokens p, p + PARTS, ...
+  // ---- column sums: lane (pair pr, class p), tokens p, p + PARTS, ...
   {
     const int pr = wave * (64 / PARTS) + l / PARTS, p = l % PARTS;
     // the swizzle of row t depends on t & 3 = p & 3 only
-    const int off0 = p * (2 * D) + ((((pr >> 2) ^ vswz<D>(p))) << 4) + (pr & 3) * 4;
+    const int off0 = p * (2 * D) + (((pr >> 2) ^ vswz<D>(p)) << 4) + (pr & 3) * 4;
     double sk[2] = {0.0, 0.0}, sv[2] = {0.0, 0.0};
-    SpanCert ck, cv;
-#pragma unroll 8
+    SpanCert ck;
+#pragma unroll
     for (int i = 0; i < SEG; ++i) {
       const int off = off0 + i * PARTS * (2 * D);
       const uint32_t kw = *reinterpret_cast<const uint32_t *>(kt + off);
@@ -127,14 +133,12 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
         const uint32_t vw = *reinterpret_cast<const uint32_t *>(vt + off);
         sv[0] += (double)bf16lo(vw);
         sv[1] += (double)bf16hi(vw);
-        cv.add(vw);
       }
     }
-    DD dk[2], dv[2];
+    DD dk[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       dk[h] = {sk[h], 0.0};
-      dv[h] = {sv[h], 0.0};
       // a certificate that fails (exponent spread near 45 bits): redo exactly
       if (!ck.exact(h, C::LG)) {
         dk[h] = {0.0, 0.0};
@@ -143,25 +147,15 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
           dd_add(dk[h], (double)(h ? bf16hi(kw) : bf16lo(kw)));
         }
       }
-      if (has_v && !cv.exact(h, C::LG)) {
-        dv[h] = {0.0, 0.0};
-        for (int i = 0; i < SEG; ++i) {
-          const uint32_t vw = *reinterpret_cast<const uint32_t *>(vt + off0 + i * PARTS * (2 * D));
-          dd_add(dv[h], (double)(h ? bf16hi(vw) : bf16lo(vw)));
-        }
-      }
     }
-    // merge the PARTS classes of a pair (lanes l ^ m), exactly
+    // merge the PARTS classes of a pair (lanes l ^ m)
 #pragma unroll
     for (int m = 1; m < PARTS; m <<= 1) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const DD ok = {__shfl_xor(dk[h].hi, m), __shfl_xor(dk[h].lo, m)};
         dd_merge(dk[h], ok);
-        if (has_v) {
-          const DD ov = {__shfl_xor(dv[h].hi, m), __shfl_xor(dv[h].lo, m)};
-          dd_merge(dv[h], ov);
-        }
+        if (has_v) sv[h] += __shfl_xor(sv[h], m);
       }
     }
     if (p == 0) {
@@ -174,9 +168,8 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
         const float m32 = (float)mean;
         kmean[f] = m32;
         if (has_v) {
-          const float s32 = (float)dd_value(dv[h]);
           kbar[so] = m32;
-          vsum[so] = s32;
+          vsum[so] = (float)sv[h];
         }
       }
     }
@@ -184,21 +177,32 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
   if (!order1) return;
   __syncthreads();   // the column sums have read the tiles; kbar is in LDS
 
-  // ---- 3. centre the keys in place: bf16(k - kbar), tokens past n stay zero
-  for (int wi = tid; wi < C::TILE / 4; wi += kStatsThreads) {
-    const int byte = wi * 4, row = byte / (2 * D), inrow = byte % (2 * D);
-    const int f = (((inrow >> 4) ^ vswz<D>(row)) << 3) + ((inrow & 15) >> 2) * 2;
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(kt + byte);
-    const float c0 = row < n ? bf16lo(w) - kmean[f] : 0.f;
-    const float c1 = row < n ? bf16hi(w) - kmean[f + 1] : 0.f;
-    *reinterpret_cast<uint32_t *>(kt + byte) = pack_bf16x2(c0, c1);
+  // ---- centre the keys in place, one 16-byte chunk (8 features of a token)
+  // at a time: bf16(k - kbar), tokens past n stay zero
+  for (int ci = tid; ci < C::TILE / 16; ci += kKvThreads) {
+    const int row = ci / (D / 8), phys = ci % (D / 8);
+    const int f0 = (phys ^ vswz<D>(row)) << 3;
+    u32x4_t *cp = reinterpret_cast<u32x4_t *>(kt + ci * 16);
+    u32x4_t w = *cp;
+    if (row < n) {
+      const f32x4_t m0 = *reinterpret_cast<const f32x4_t *>(kmean + f0);
+      const f32x4_t m1 = *reinterpret_cast<const f32x4_t *>(kmean + f0 + 4);
+      w[0] = pack_bf16x2(bf16lo(w[0]) - m0[0], bf16hi(w[0]) - m0[1]);
+      w[1] = pack_bf16x2(bf16lo(w[1]) - m0[2], bf16hi(w[1]) - m0[3]);
+      w[2] = pack_bf16x2(bf16lo(w[2]) - m1[0], bf16hi(w[2]) - m1[1]);
+      w[3] = pack_bf16x2(bf16lo(w[3]) - m1[2], bf16hi(w[3]) - m1[3]);
+    } else {
+      w = u32x4_t{0, 0, 0, 0};
+    }
+    *cp = w;
   }
   __syncthreads();
 
-  // ---- 4. first-order moment T = Kc^T V (rows c, columns e) on MFMA
+  // ---- T = Kc^T V (rows c, columns e) on MFMA: wave w < MW takes e tile te
+  // and c tiles tc0 .. tc0 + TPW - 1
   f32x16_t acc[TPW];
-  const int te = TPW == NT ? wave : wave / NT;   // e tile of this wave
-  {
+  const int te = wave / (NT / TPW), tc0 = (wave % (NT / TPW)) * TPW;
+  if (wave < C::MW) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) acc[i] = f32x16_t{};
     const int srow = (l & 15) >> 2, ecol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
@@ -207,35 +211,29 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_bf16(PisaDims dm, cons
       const int rr = ks * 16 + 4 * hl + srow;
       const u32x4_t b = frag_vt<D>(vt, rr, te * 32 + ecol);
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int tc = TPW == NT ? i : wave % NT;
-        acc[i] = mfma32(frag_vt<D>(kt, rr, tc * 32 + ecol), b, acc[i]);
-      }
+      for (int i = 0; i < TPW; ++i) acc[i] = mfma32(frag_vt<D>(kt, rr, (tc0 + i) * 32 + ecol), b, acc[i]);
     }
   }
-
   __syncthreads();   // the MFMA reads of the tiles are done: reuse them for staging
 
-  // ---- 5. HT[e][c] = T[c][e] -> bf16, staged [e][c]
+  // ---- HT[e][c] = T[c][e] -> bf16, staged [e][c], then 16-byte stores
   uint16_t *ot = reinterpret_cast<uint16_t *>(lds);
-  {
+  if (wave < C::MW) {
     const int e = te * 32 + lq;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tc = TPW == NT ? i : wave % NT;
+    for (int i = 0; i < TPW; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c0 = tc * 32 + 8 * g + 4 * hl;
+      for (int q = 0; q < 4; ++q) {
+        const int c0 = (tc0 + i) * 32 + 8 * q + 4 * hl;
         u32x2_t o;
-        o[0] = pack_bf16x2(acc[i][4 * g], acc[i][4 * g + 1]);
-        o[1] = pack_bf16x2(acc[i][4 * g + 2], acc[i][4 * g + 3]);
+        o[0] = pack_bf16x2(acc[i][4 * q], acc[i][4 * q + 1]);
+        o[1] = pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3]);
         *reinterpret_cast<u32x2_t *>(ot + e * OP + c0) = o;
       }
-    }
   }
   __syncthreads();
   uint16_t *Hb = HT + ((size_t)bh * dm.n_blk + j) * D * D;
-  for (int u = tid; u < D * D / 8; u += kStatsThreads) {
+  for (int u = tid; u < D * D / 8; u += kKvThreads) {
     const int e = u / (D / 8), c8 = (u % (D / 8)) * 8;
     const u32x2_t lo2 = *reinterpret_cast<const u32x2_t *>(ot + e * OP + c8);
     const u32x2_t hi2 = *reinterpret_cast<const u32x2_t *>(ot + e * OP + c8 + 4);
@@ -692,32 +690,62 @@ __global__ __launch_bounds__(kStatsThreads) void q_pool(PisaDims dm, const T *__
 // query-block pooling (block rows): one workgroup per (b, head, query block);
 // thread (ts, ch) sums the 16-byte chunk ch of every TS-th row from ts in
 // double-double, and the TS partial sums of an element are merged in order.
-template <typename T, int D>
+template <typename T, int D, int BS>
 __global__ __launch_bounds__(kStatsThreads) void q_pool_block(PisaDims dm, const T *__restrict__ Q,
                                                              T *__restrict__ qsel) {
   constexpr int EPC = 16 / sizeof(T);          // elements per chunk
   constexpr int CPR = D / EPC;                 // chunks per row
   constexpr int TS = kStatsThreads / CPR;      // row slices
+  constexpr int RPT = BS / TS;                 // rows per thread
+  static_assert(RPT >= 1 && RPT * TS == BS, "rows split evenly over the row slices");
   __shared__ DD part[TS][D];
   const int tid = threadIdx.x, ch = tid % CPR, ts = tid / CPR;
   const int r = blockIdx.x % dm.n_sel;
   const long long bh = blockIdx.x / dm.n_sel;
   const int t0 = r * dm.bs, t1 = min(dm.L, t0 + dm.bs);
   const T *src = Q + ((size_t)bh * dm.L) * D + ch * EPC;
+  // every row of this thread is loaded before any arithmetic (one memory
+  // latency); rows past the sequence end read as zeros
+  u32x4_t w[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int t = t0 + ts + k * TS;
+    w[k] = t < t1 ? *reinterpret_cast<const u32x4_t *>(src + (size_t)t * D) : u32x4_t{0, 0, 0, 0};
+  }
   DD acc[EPC];
+  if constexpr (sizeof(T) == 2) {
+    // certified float64 sums, double-double where the certificate fails
+    constexpr int LG = RPT <= 4 ? 2 : RPT <= 8 ? 3 : 4;
+    double sm[EPC];
+    SpanCert cert[4];
 #pragma unroll
-  for (int i = 0; i < EPC; ++i) acc[i] = DD{0.0, 0.0};
-  for (int t = t0 + ts; t < t1; t += TS) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(src + (size_t)t * D);
+    for (int i = 0; i < EPC; ++i) sm[i] = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (sizeof(T) == 2) {
-        dd_add(acc[2 * i], (double)bf16lo(w[i]));
-        dd_add(acc[2 * i + 1], (double)bf16hi(w[i]));
-      } else {
-        dd_add(acc[i], (double)__uint_as_float(w[i]));
+    for (int k = 0; k < RPT; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm[2 * i] += (double)bf16lo(w[k][i]);
+        sm[2 * i + 1] += (double)bf16hi(w[k][i]);
+        cert[i].add(w[k][i]);
       }
-    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[2 * i + h] = DD{sm[2 * i + h], 0.0};
+        if (!cert[i].exact(h, LG)) {
+          acc[2 * i + h] = DD{0.0, 0.0};
+#pragma unroll
+          for (int k = 0; k < RPT; ++k) dd_add(acc[2 * i + h], (double)(h ? bf16hi(w[k][i]) : bf16lo(w[k][i])));
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) acc[i] = DD{0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dd_add(acc[i], (double)__uint_as_float(w[k][i]));
   }
 #pragma unroll
   for (int i = 0; i < EPC; ++i) part[ts][ch * EPC + i] = acc[i];
@@ -735,8 +763,11 @@ __global__ __launch_bounds__(kStatsThreads) void q_pool_block(PisaDims dm, const
 template <typename T, int D>
 hipError_t launch_q_pool(const PisaDims &dm, const void *Q, void *qsel, hipStream_t st) {
   if (dm.group == 0) {   // query blocks of 64 or 128 rows
-    q_pool_block<T, D><<<(unsigned)dm.B * dm.Hq * dm.n_sel, kStatsThreads, 0, st>>>(
-        dm, static_cast<const T *>(Q), static_cast<T *>(qsel));
+    const unsigned grid = (unsigned)dm.B * dm.Hq * dm.n_sel;
+    if (dm.bs == 64) q_pool_block<T, D, 64><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q),
+                                                                           static_cast<T *>(qsel));
+    else q_pool_block<T, D, 128><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q),
+                                                                 static_cast<T *>(qsel));
     return hipGetLastError();
   }
   constexpr int CPR = D / (16 / sizeof(T));
@@ -753,12 +784,12 @@ hipError_t launch_kv_bf16(const PisaDims &dm, const void *K, const void *V, void
   const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kv_stats_bf16<D, BS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&kv_stats_bf16<D, BS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  kv_stats_bf16<D, BS><<<grid, kStatsThreads, C::TOTAL, st>>>(
+  kv_stats_bf16<D, BS><<<grid, kKvThreads, C::TOTAL, st>>>(
       dm, static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V), static_cast<uint16_t *>(ksel),
       kbar, vsum, static_cast<uint16_t *>(HT));
   return hipGetLastError();
