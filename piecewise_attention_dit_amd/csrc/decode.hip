@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
   __shared__ uint32_t ubits[32];
   __shared__ int elist[1024];            // exact blocks of any head (n_blk <= 1024)
   __shared__ int n_exact;
+  __shared__ float fbuf[sizeof(T) == 2 ? kDecWaves : 1][kRM * D];   // first-order relayout, per wave
   const PisaDims &dm = a.dm;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int R = dm.ratio;
@@ -182,6 +183,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
     for (int i = 0; i < EPL; ++i) o[r][i] *= c;
     m[r] = mn;
   };
+  // bf16 first order on MFMA 16x16x32: A = q (row m = query head m of the kv
+  // head, zero past R), loaded once
+  u32x4_t qa[D / 32];
+  if constexpr (sizeof(T) == 2) {
+    const int mq = l & 15, kg = l >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      qa[ks] = mq < R ? *reinterpret_cast<const u32x4_t *>(Q + (size_t)mq * D + ks * 32 + 8 * kg)
+                      : u32x4_t{0, 0, 0, 0};
+  }
   const size_t kvrows = ring ? (size_t)a.ring : (size_t)dm.L;
   const T *Kh = static_cast<const T *>(a.K) + (size_t)(b * dm.Hkv + hk) * kvrows * D;
   const T *Vh = static_cast<const T *>(a.V) + (size_t)(b * dm.Hkv + hk) * kvrows * D;
@@ -294,6 +305,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
         }
         if (!any) continue;
         const int nb = min(64, (nc - wk + NWK - 1) / NWK - base);   // blocks of this batch
+        // bf16 first order of the batch: F[m][e] += alpha_m scale (q_m H_j)[e]
+        // in the MFMA layout (rows m = 4 (l / 16) + t, columns e = 16 nt + l % 16)
+        f32x4_t F[D / 16];
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) F[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        bool fo = false;
         for (int k1 = 0; k1 < nb; k1 += 16) {
           float vv[16][EPL];
 #pragma unroll
@@ -314,8 +331,36 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
               for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(ak[r], vv[i][e], o[r][e]);
             }
             if (!order1 || !use) continue;
-            // + alpha scale q H_j for every head: rows EPL l .. of H_j^T read once
             const int jk = __builtin_amdgcn_readlane(j, k1 + i);
+            if constexpr (sizeof(T) == 2) {
+              // u = Q H_j^T^T on MFMA, B = rows e of H_j^T straight from memory
+              const uint16_t *Hj = static_cast<const uint16_t *>(a.HT) + (soff + jk) * D * D;
+              float am[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int mrow = 4 * (l >> 4) + t;
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < kRM; ++r)
+                  if (r == mrow) v = ak[r];
+                am[t] = v * dm.scale;
+              }
+#pragma unroll
+              for (int nt = 0; nt < D / 16; ++nt) {
+                f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                  const u32x4_t hb = *reinterpret_cast<const u32x4_t *>(
+                      Hj + (size_t)(nt * 16 + (l & 15)) * D + ks * 32 + 8 * (l >> 4));
+                  u = mfma16(qa[ks], hb, u);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) F[nt][t] = fmaf(am[t], u[t], F[nt][t]);
+              }
+              fo = true;
+              continue;
+            }
+            // + alpha scale q H_j for every head: rows EPL l .. of H_j^T read once
             const T *Hj = static_cast<const T *>(a.HT) + (soff + jk) * D * D + (size_t)EPL * l * D;
             float u[kRM][EPL];
 #pragma unroll
@@ -339,6 +384,26 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
             for (int r = 0; r < kRM; ++r)
 #pragma unroll
               for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(ak[r] * dm.scale, u[r][e], o[r][e]);
+          }
+        }
+        if constexpr (sizeof(T) == 2) {
+          if (fo) {   // F into the heads' accumulators (lane l: features EPL l ..), through LDS
+            float *buf = fbuf[w];
+#pragma unroll
+            for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int mrow = 4 * (l >> 4) + t;
+                if (mrow < kRM) buf[mrow * D + nt * 16 + (l & 15)] = F[nt][t];
+              }
+            wave_lds_sync();
+#pragma unroll
+            for (int r = 0; r < kRM; ++r) {
+              if (r >= R) break;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) o[r][e] += buf[r * D + EPL * l + e];
+            }
+            wave_lds_sync();   // read before the next batch writes
           }
         }
       }

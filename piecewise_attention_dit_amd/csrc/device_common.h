@@ -200,6 +200,12 @@ PISA_DEV f32x16_t mfma32(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) 
                                                   c, 0, 0, 0);
 }
 PISA_DEV bf16x8_t as_bf16x8(const u32x4_t &v) { return __builtin_bit_cast(bf16x8_t, v); }
+// 16x16x32: lane l holds A row l % 16 and B column l % 16, k = 8 (l / 16) .. + 7;
+// the result column l % 16, rows 4 (l / 16) .. + 3
+PISA_DEV f32x4_t mfma16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  c, 0, 0, 0);
+}
 
 // Logical block id -> id such that consecutive logical ids run on the same XCD
 // (workgroups are dispatched round-robin over the 8 XCDs of an MI355X).
