@@ -292,17 +292,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
     bool active = false;
 #pragma unroll
     for (int n = 0; n < NQ; ++n) mem[n] = false;
+    // One barrier per pair of stages.  At stage it (even): this wave's DMA of
+    // stages it, it + 1 (issued after the previous barrier) has landed; after
+    // the barrier so has every wave's, and every wave has finished stages
+    // it - 2, it - 1, whose ring slots then take the DMA of stages it + 2 and
+    // it + 3.  Waves drift by up to two stages between barriers.
     for (int it = 0; it < n_st; ++it) {
       const int j = exl[it / SPB], kh = it % SPB;
-      if (it + 2 < n_st) {
-        issue(it + 2);
-        wait_vmcnt<2 * PER_STAGE>();
-      } else if (it + 1 < n_st) {
-        wait_vmcnt<PER_STAGE>();
-      } else {
+      if ((it & 1) == 0) {
         wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < n_st) issue(it + 2);
+        if (it + 3 < n_st) issue(it + 3);
       }
-      __syncthreads();
       if (kh == 0) {
         bool any = false;
 #pragma unroll
