@@ -126,3 +126,44 @@ def test_deterministic_bitwise():
     for key, t in a["stats"].items():
         if t is not None:
             assert torch.equal(t, b["stats"][key]), key
+
+
+def _wide_spread(d, bs, L, dtype=torch.bfloat16):
+    """Q and K with one feature column per block that a plain float64 sum gets
+    wrong: tokens 0, 16 and 32 of the block hold 2^60, 1 and -2^60 (its other
+    tokens 0), so the correctly rounded sum is 1 and the mean 1 / block, while
+    summing them in that order in float64 loses the 1 and gives 0.  One lane
+    sums those tokens in the key kernel (and, for d = 128, in the query
+    kernel), so its exponent-spread certificate fails (60 bits) and the exact
+    fallback decides the result."""
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(1, 2, L, d, generator=g)
+    k = torch.randn(1, 2, L, d, generator=g)
+    v = torch.randn(1, 2, L, d, generator=g)
+    for x in (q, k):
+        for j in range(L // bs):
+            f = 5 + j % 3
+            x[:, :, j * bs:(j + 1) * bs, f] = 0.0
+            x[:, :, j * bs + 0, f] = 2.0 ** 60
+            x[:, :, j * bs + 16, f] = 1.0
+            x[:, :, j * bs + 32, f] = -(2.0 ** 60)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+@pytest.mark.parametrize("d,bs", [(128, 64), (128, 128), (64, 64), (64, 128)])
+def test_pooling_exact_beyond_float64(d, bs):
+    from piecewise_attention_dit_amd import pisa
+    L = 4 * bs
+    q, k, v = _wide_spread(d, bs, L)
+    knobs = dict(B=1, Hq=2, Hkv=2, L=L, d=d, dtype="bf16", block=bs, topk=1, window=0, group=0,
+                 n_cand=0, causal=False, taylor="order1")
+    P = problem(knobs)
+    print(f"[parity] wide exponent spread d={d} block={bs}", flush=True)
+    ref = po.block_stats(*(x.double().numpy() for x in (q, k, v)), P)
+    # the case is sensitive: the pooled value is 1 / block, not the 0 of a plain sum
+    assert ref["ksel"][0, 0, 0, 5] == 1.0 / bs and ref["qsel"][0, 0, 0, 5] == 1.0 / bs
+    p = pisa.make_params(**knobs)
+    st = pisa.block_stats(p, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    g = dict(stats={key: (t.cpu() if t is not None else None) for key, t in st.items()})
+    compare_stats(g, ref, P)
