@@ -410,9 +410,9 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
 //   3. each member's top-k of its proxy's list: MFMA of the gathered list
 //      rows against up to 8 member queries, then the same selection.
 // Selection of one row by one wave, in three tiers:
-//   fast    keys ord(fp32 score); the n-th largest key found by bisection
-//           over its 32 bits, each step one compare per slot and a ballot
-//           count; the set is accepted when it is certified: every kept
+//   fast    keys ord(fp32 score); the n-th largest key found by radix
+//           select over 7-bit digits in a per-wave LDS histogram (radix32);
+//           the set is accepted when it is certified: every kept
 //           lower bound s - e exceeds every dropped upper bound s + e, with
 //           e = D 2^-22 |p| |k| + 2^-110 (see pivot_bound below);
 //   re-score  (rare, a function of its own) candidates whose intervals
@@ -463,40 +463,90 @@ struct PivotLayout {
   static_assert((int)sizeof(Shared) <= kPX * SLD * 4, "select_row's Shared fits in S");
 };
 
-// Largest threshold t with at least `need` keys >= t (keys of invalid slots
-// are 0 and never counted: every probe is >= 1).  Returns true when exactly
-// `need` keys are >= t, i.e. the top set is unique at 32 bits.  Slots
-// s >= nsl (uniform) hold no candidate.
+// wave max / min of unsigned 32-bit values on the cross-lane data path
+// (DPP row operations and the permlane swaps); every lane gets the result
+template <bool MAX>
+PISA_DEV uint32_t wave_ureduce_xl(uint32_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+  v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+  v = op(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  v = op(v, dpp(v, std::integral_constant<int, 0x140>{}));   // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+
+// Largest threshold t with at least `need` keys >= t, by radix select: 7-bit
+// digits counted in a 128-bin LDS histogram of this wave (hist), starting
+// below the bits every candidate key shares, and stopping as soon as the bin
+// that holds the boundary holds exactly the keys still to take.  Keys of 0
+// (invalid slots) are no candidates; slots s >= nsl (uniform) hold none.
+// Returns true with t such that exactly `need` keys are >= t (the top set is
+// unique at 32 bits), false when keys tie across the boundary at 32 bits or
+// fewer than `need` candidates exist.
 template <int NS>
-PISA_DEV bool bisect32(const uint32_t (&key)[NS], int nsl, int need, uint32_t &t) {
-  uint32_t lo = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = lo | (1u << bit);
-    int cnt = 0;
+PISA_DEV bool radix32(const uint32_t (&key)[NS], int nsl, int need, uint32_t &t, uint32_t *hist) {
+  const int l = lane_id();
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nsl && key[s] != 0u) {
+      kmax = key[s] > kmax ? key[s] : kmax;
+      kmin = key[s] < kmin ? key[s] : kmin;
+    }
+  kmax = wave_ureduce_xl<true>(kmax);
+  kmin = wave_ureduce_xl<false>(kmin);
+  const uint32_t diff = kmax ^ kmin;
+  int hi = diff ? 32 - __builtin_clz(diff) : 1;   // bits >= hi are shared by every key
+  uint32_t prefix = hi >= 32 ? 0u : (kmax >> hi) << hi;
+  for (;;) {
+    const int width = hi < 7 ? hi : 7, lo = hi - width;
+    hist[2 * l] = 0u;
+    hist[2 * l + 1] = 0u;
+    wave_lds_sync();
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      if (s < nsl) cnt += __builtin_popcountll(ballot64(key[s] >= c));
-    if (cnt >= need) {
-      lo = c;
-      if (cnt == need) {
-        t = lo;
-        return true;
-      }
+      if (s < nsl && key[s] != 0u && (hi >= 32 || (key[s] >> hi) == (prefix >> hi)))
+        atomicAdd(&hist[(key[s] >> lo) & ((1u << width) - 1u)], 1u);
+    wave_lds_sync();
+    // bins from the top: lane l holds bins 127 - 2 l and 126 - 2 l
+    const int h0 = (int)hist[127 - 2 * l], h1 = (int)hist[126 - 2 * l];
+    const int incl = wave_incl_scan(h0 + h1);
+    const int excl = incl - h0 - h1;
+    const uint64_t bal = ballot64(excl < need && need <= incl);
+    if (!bal) return false;   // fewer candidates than need
+    const int owner = __builtin_amdgcn_readfirstlane(__builtin_ffsll((long long)bal) - 1);
+    const bool first = excl + h0 >= need;
+    const int bin = __builtin_amdgcn_readlane(first ? 127 - 2 * l : 126 - 2 * l, owner);
+    const int above = __builtin_amdgcn_readlane(first ? excl : excl + h0, owner);
+    const int hb = __builtin_amdgcn_readlane(first ? h0 : h1, owner);
+    wave_lds_sync();   // every lane has read the bins before the next round clears them
+    need -= above;
+    prefix |= (uint32_t)bin << lo;
+    if (hb == need) {   // this bin's keys all in, every lower key out
+      t = prefix;
+      return true;
     }
+    if (lo == 0) return false;   // keys equal to prefix straddle the boundary
+    hi = lo;
   }
-  t = lo;
-  return false;
 }
 
 // Fast tier: select the `need` best of fp32 scores sc (bounds dl) and certify.
+// hist: 128 words of LDS of this wave, free while the tier runs.
 template <int NS>
 PISA_DEV bool fast_select(const float (&sc)[NS], const float (&dl)[NS], const bool (&valid)[NS], int nsl,
-                          int need, bool (&sel)[NS]) {
+                          int need, bool (&sel)[NS], uint32_t *hist) {
   uint32_t key[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) key[s] = valid[s] ? ord32(sc[s]) : 0u;
   uint32_t t;
-  if (!bisect32<NS>(key, nsl, need, t)) return false;
+  if (!radix32<NS>(key, nsl, need, t, hist)) return false;
   float t_out = -__builtin_huge_valf();
   bool bad = false;
 #pragma unroll
@@ -843,7 +893,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
           dl[s] = fmaf(0x1p-22f, fabsf(sc[s]), dl[s]);
         }
       }
-      if (fast_select<NS>(sc, dl, valid, nsl, C, sel)) {
+      if (fast_select<NS>(sc, dl, valid, nsl, C, sel, reinterpret_cast<uint32_t *>(PVw))) {
         write_sorted_lds<NS>(sel, cid, lout, gout, dm.n_cand);
       } else {
         const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
@@ -965,7 +1015,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         }
         int ct;
         int32_t *out = member_row(qrow0, t, ct);
-        if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel)) {
+        if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel, reinterpret_cast<uint32_t *>(PVw))) {
           write_sorted_lds<NS>(sel, cj, nullptr, out, dm.klist - ct);
         } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, 0, C, n_take, cb, SKN, route ? MC : nullptr, lam,
                                           Q + (qrow0 + t) * D, PVw, kbase, nullptr, out, dm.klist - ct, diag) &&
