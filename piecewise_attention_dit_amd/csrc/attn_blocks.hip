@@ -536,61 +536,72 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], lds + C::TY_H + (w + NDW * u) * 1024);
     }
     const float *stg = reinterpret_cast<const float *>(lds + C::TY_STG);
+    // Taylor tables of the batch that starts at entry b0, from its staged
+    // kbar / vsum rows: kbar as bf16 hi + lo rows (swizzled like K tiles),
+    // Sigma^T as bf16 hi and lo in the perm16 layout, and n_j.  Built by the
+    // waves that issue no DMA first (thread (tid + NT / 2) % NT).
+    auto build = [&](int b0) {
+      const int nb = min(kNB, n_ty - b0);
+      const int bt = (tid + NT / 2) % NT;
+      if (bt < kNB * (D / 8)) {
+        const int en = bt / (D / 8), ch = bt % (D / 8);
+        u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
+        float sv[8];
+        if (en < nb) {
+          const int j = tyl[b0 + en];
+          const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8);
+          const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8 + 4);
+          const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8);
+          const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8 + 4);
+          const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t pk = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+            hi[i] = pk;
+            lo4[i] = pack_bf16x2(x[2 * i] - bf16lo(pk), x[2 * i + 1] - bf16hi(pk));
+          }
+          sv[0] = v0[0]; sv[1] = v0[1]; sv[2] = v0[2]; sv[3] = v0[3];
+          sv[4] = v1[0]; sv[5] = v1[1]; sv[6] = v1[2]; sv[7] = v1[3];
+          if (ch == 0) nj[en] = (float)min(dm.bs, dm.L - j * dm.bs);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sv[i] = 0.f;
+          if (ch == 0) nj[en] = 0.f;
+        }
+        const int sw = (ch ^ kswz<D>(en)) << 4;
+        *reinterpret_cast<u32x4_t *>(kbh + en * (2 * D) + sw) = hi;
+        *reinterpret_cast<u32x4_t *>(kbl + en * (2 * D) + sw) = lo4;
+        // Sigma^T [feature][16 entries]: entry en at K position perm16(en),
+        // the two 16-byte halves of a row swapped on odd groups of 8 rows
+        const int pos = perm16(en);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = ch * 8 + i;
+          const uint32_t shi = f32_to_bf16(sv[i]);
+          const uint32_t slo = f32_to_bf16(sv[i] - bf16_to_f32(shi));
+          const int off = f * (2 * kNB) + (((pos >> 3) ^ ((f >> 3) & 1)) << 4) + ((pos & 7) << 1);
+          *reinterpret_cast<uint16_t *>(sth + off) = (uint16_t)shi;
+          *reinterpret_cast<uint16_t *>(stl + off) = (uint16_t)slo;
+        }
+      }
+    };
     uint32_t tmask = 0;
     for (int eg = 0; eg < n_ty; ++eg) {
       const int e = eg % kNB;
       if (e == 0) {
         const int nb = min(kNB, n_ty - eg);
-        // this batch's staged rows have landed (H waits of the previous
-        // steps cover them in order; the first batch waits here)
-        if (!order1) wait_vmcnt<0>();
-        else if (eg == 0) {
-          if (n_ty > 1) wait_vmcnt<2 * PH>();
+        // first order: the tables of every batch after the first were built
+        // half a batch earlier, between per-entry barriers; the first batch,
+        // and the orders without per-entry barriers, build them here once
+        // the staged rows have landed
+        if (!order1 || eg == 0) {
+          if (!order1) wait_vmcnt<0>();
+          else if (n_ty > 1) wait_vmcnt<2 * PH>();
           else wait_vmcnt<PH>();
+          __syncthreads();   // the previous batch's tables are consumed; staging landed
+          build(eg);
+          __syncthreads();
         }
-        __syncthreads();   // the previous batch's tables are consumed; staging landed
-        if (tid < kNB * (D / 8)) {
-          const int en = tid / (D / 8), ch = tid % (D / 8);
-          u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
-          float sv[8];
-          if (en < nb) {
-            const int j = tyl[eg + en];
-            const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8);
-            const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8 + 4);
-            const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8);
-            const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8 + 4);
-            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t pk = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-              hi[i] = pk;
-              lo4[i] = pack_bf16x2(x[2 * i] - bf16lo(pk), x[2 * i + 1] - bf16hi(pk));
-            }
-            sv[0] = v0[0]; sv[1] = v0[1]; sv[2] = v0[2]; sv[3] = v0[3];
-            sv[4] = v1[0]; sv[5] = v1[1]; sv[6] = v1[2]; sv[7] = v1[3];
-            if (ch == 0) nj[en] = (float)min(dm.bs, dm.L - j * dm.bs);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sv[i] = 0.f;
-            if (ch == 0) nj[en] = 0.f;
-          }
-          const int sw = (ch ^ kswz<D>(en)) << 4;
-          *reinterpret_cast<u32x4_t *>(kbh + en * (2 * D) + sw) = hi;
-          *reinterpret_cast<u32x4_t *>(kbl + en * (2 * D) + sw) = lo4;
-          // Sigma^T [feature][16 entries]: entry en at K position perm16(en),
-          // the two 16-byte halves of a row swapped on odd groups of 8 rows
-          const int pos = perm16(en);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int f = ch * 8 + i;
-            const uint32_t shi = f32_to_bf16(sv[i]);
-            const uint32_t slo = f32_to_bf16(sv[i] - bf16_to_f32(shi));
-            const int off = f * (2 * kNB) + (((pos >> 3) ^ ((f >> 3) & 1)) << 4) + ((pos & 7) << 1);
-            *reinterpret_cast<uint16_t *>(sth + off) = (uint16_t)shi;
-            *reinterpret_cast<uint16_t *>(stl + off) = (uint16_t)slo;
-          }
-        }
-        __syncthreads();
         {   // lane en < nb decides entry en for this wave's part
           bool mine = false;
           if (pvalid && l < nb) {
@@ -600,12 +611,14 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           tmask = (uint32_t)ballot64(mine);
         }
         if (tmask) {
+          // A rows 0..15 are the entries' kbar hi parts, rows 16..31 their lo
+          // parts: entry en's logit is the sum of result rows en and en + 16
           f32x16_t at = f32x16_t{};
+          const uint8_t *kbs = lq < 16 ? kbh : kbl;
 #pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            at = mfma32(frag_a<D>(kbh, lq & 15, 2 * ks + hl), qf[ks], at);
-            at = mfma32(frag_a<D>(kbl, lq & 15, 2 * ks + hl), qf[ks], at);
-          }
+          for (int ks = 0; ks < D / 16; ++ks) at = mfma32(frag_a<D>(kbs, lq & 15, 2 * ks + hl), qf[ks], at);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) at[r] += at[r + 8];
           // entries 0..15 sit in registers 0..7: entry 8 (r / 4) + 4 hl + r % 4
           float mx = kNegInf;
 #pragma unroll
@@ -695,6 +708,12 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
 #pragma unroll
         for (int c = NMT - KS - 1; c < NMT; ++c) fchunk(u, c);
       }
+      // the next batch's tables: its staged rows landed before this entry's
+      // barrier (they were issued ahead of H_{eg+1}), this batch's tables were
+      // read before entry eg - e + 1's barrier, and the barriers of the
+      // entries up to the batch's end publish them
+      static_assert(kNB / 2 + 2 < kNB, "a per-entry barrier follows the early build");
+      if (e == kNB / 2 + 1 && eg - e + kNB < n_ty) build(eg - e + kNB);
     }
     if (hybrid) {   // O^T += (scale sum alpha) Hbar^T Q^T, once per row
       wait_vmcnt<0>();
