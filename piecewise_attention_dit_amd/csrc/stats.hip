@@ -687,87 +687,105 @@ __global__ __launch_bounds__(kStatsThreads) void q_pool(PisaDims dm, const T *__
   *reinterpret_cast<u32x4_t *>(qsel + (size_t)sr * D + ch * EPC) = out;
 }
 
-// query-block pooling (block rows): one workgroup per (b, head, query block);
-// thread (ts, ch) sums the 16-byte chunk ch of every TS-th row from ts in
-// double-double, and the TS partial sums of an element are merged in order.
+// One wave per query block, four blocks per workgroup: lane (chunk ch, slice
+// ts) loads rows ts, ts + SPW, ... of its block up front and sums them
+// (certified float64 for bf16, double-double where the certificate fails or
+// for fp32); the SPW slices of a chunk then merge by lane shuffles with
+// exact double-double additions, and the first slice writes the means.
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(kStatsThreads) void q_pool_block(PisaDims dm, const T *__restrict__ Q,
-                                                             T *__restrict__ qsel) {
+__global__ __launch_bounds__(kStatsThreads) void q_pool_wave(PisaDims dm, const T *__restrict__ Q,
+                                                            T *__restrict__ qsel) {
   constexpr int EPC = 16 / sizeof(T);          // elements per chunk
   constexpr int CPR = D / EPC;                 // chunks per row
-  constexpr int TS = kStatsThreads / CPR;      // row slices
-  constexpr int RPT = BS / TS;                 // rows per thread
-  static_assert(RPT >= 1 && RPT * TS == BS, "rows split evenly over the row slices");
-  __shared__ DD part[TS][D];
-  const int tid = threadIdx.x, ch = tid % CPR, ts = tid / CPR;
-  const int r = blockIdx.x % dm.n_sel;
-  const long long bh = blockIdx.x / dm.n_sel;
+  constexpr int SPW = 64 / CPR;                // row slices per wave
+  constexpr int RPS = BS / SPW;                // rows per slice
+  static_assert(SPW * CPR == 64 && RPS * SPW == BS, "one block per wave");
+  const int l = threadIdx.x & 63, ch = l % CPR, ts = l / CPR;
+  const long long blk = (long long)blockIdx.x * (kStatsThreads / 64) + (threadIdx.x >> 6);
+  if (blk >= (long long)dm.B * dm.Hq * dm.n_sel) return;   // whole waves
+  const int r = (int)(blk % dm.n_sel);
+  const long long bh = blk / dm.n_sel;
   const int t0 = r * dm.bs, t1 = min(dm.L, t0 + dm.bs);
   const T *src = Q + ((size_t)bh * dm.L) * D + ch * EPC;
-  // every row of this thread is loaded before any arithmetic (one memory
-  // latency); rows past the sequence end read as zeros
-  u32x4_t w[RPT];
-#pragma unroll
-  for (int k = 0; k < RPT; ++k) {
-    const int t = t0 + ts + k * TS;
-    w[k] = t < t1 ? *reinterpret_cast<const u32x4_t *>(src + (size_t)t * D) : u32x4_t{0, 0, 0, 0};
-  }
+  // rows in batches of RB per lane, each batch loaded up front
+  constexpr int RB = RPS < 16 / (int)sizeof(T) * 2 ? RPS : 16 / (int)sizeof(T) * 2;   // 16 bf16, 8 fp32
   DD acc[EPC];
-  if constexpr (sizeof(T) == 2) {
-    // certified float64 sums, double-double where the certificate fails
-    constexpr int LG = RPT <= 4 ? 2 : RPT <= 8 ? 3 : 4;
-    double sm[EPC];
-    SpanCert cert[4];
 #pragma unroll
-    for (int i = 0; i < EPC; ++i) sm[i] = 0.0;
+  for (int i = 0; i < EPC; ++i) acc[i] = DD{0.0, 0.0};
+  for (int k0 = 0; k0 < RPS; k0 += RB) {
+    u32x4_t w[RB];
 #pragma unroll
-    for (int k = 0; k < RPT; ++k)
+    for (int k = 0; k < RB; ++k) {
+      const int t = t0 + ts + (k0 + k) * SPW;
+      w[k] = t < t1 ? *reinterpret_cast<const u32x4_t *>(src + (size_t)t * D) : u32x4_t{0, 0, 0, 0};
+    }
+    if constexpr (sizeof(T) == 2) {
+      // the batch's sums in float64, exact when certified; double-double
+      // additions otherwise
+      constexpr int LG = RB <= 4 ? 2 : RB <= 8 ? 3 : 4;
+      double sm[EPC];
+      SpanCert cert[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sm[2 * i] += (double)bf16lo(w[k][i]);
-        sm[2 * i + 1] += (double)bf16hi(w[k][i]);
-        cert[i].add(w[k][i]);
-      }
+      for (int i = 0; i < EPC; ++i) sm[i] = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int k = 0; k < RB; ++k)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        acc[2 * i + h] = DD{sm[2 * i + h], 0.0};
-        if (!cert[i].exact(h, LG)) {
-          acc[2 * i + h] = DD{0.0, 0.0};
-#pragma unroll
-          for (int k = 0; k < RPT; ++k) dd_add(acc[2 * i + h], (double)(h ? bf16hi(w[k][i]) : bf16lo(w[k][i])));
+        for (int i = 0; i < 4; ++i) {
+          sm[2 * i] += (double)bf16lo(w[k][i]);
+          sm[2 * i + 1] += (double)bf16hi(w[k][i]);
+          cert[i].add(w[k][i]);
         }
-      }
-  } else {
 #pragma unroll
-    for (int i = 0; i < EPC; ++i) acc[i] = DD{0.0, 0.0};
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int k = 0; k < RPT; ++k)
+        for (int h = 0; h < 2; ++h) {
+          if (cert[i].exact(h, LG)) {
+            dd_add(acc[2 * i + h], sm[2 * i + h]);
+          } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dd_add(acc[i], (double)__uint_as_float(w[k][i]));
+            for (int k = 0; k < RB; ++k) dd_add(acc[2 * i + h], (double)(h ? bf16hi(w[k][i]) : bf16lo(w[k][i])));
+          }
+        }
+    } else {
+#pragma unroll
+      for (int k = 0; k < RB; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dd_add(acc[i], (double)__uint_as_float(w[k][i]));
+    }
   }
 #pragma unroll
-  for (int i = 0; i < EPC; ++i) part[ts][ch * EPC + i] = acc[i];
-  __syncthreads();
-  if (tid < D) {
-    DD s = part[0][tid];
-    for (int k = 1; k < TS; ++k) dd_merge(s, part[k][tid]);
-    const double mean = dd_value(s) / (double)(t1 - t0);
-    T *dst = qsel + ((size_t)bh * dm.n_sel + r) * D + tid;
-    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t *>(dst) = (uint16_t)f64_to_bf16_bits(mean);
-    else *dst = (float)round_to_format(mean, 24);
+  for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) {
+      const DD x = {__shfl_xor(acc[i].hi, o), __shfl_xor(acc[i].lo, o)};
+      dd_merge(acc[i], x);
+    }
+  if (ts == 0) {
+    const double inv_n = (double)(t1 - t0);
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t lo = f64_to_bf16_bits(dd_value(acc[2 * i]) / inv_n);
+        const uint32_t hi = f64_to_bf16_bits(dd_value(acc[2 * i + 1]) / inv_n);
+        o[i] = lo | (hi << 16);
+      } else {
+        o[i] = __float_as_uint((float)round_to_format(dd_value(acc[i]) / inv_n, 24));
+      }
+    }
+    *reinterpret_cast<u32x4_t *>(qsel + ((size_t)bh * dm.n_sel + r) * D + ch * EPC) = o;
   }
 }
 
 template <typename T, int D>
 hipError_t launch_q_pool(const PisaDims &dm, const void *Q, void *qsel, hipStream_t st) {
-  if (dm.group == 0) {   // query blocks of 64 or 128 rows
-    const unsigned grid = (unsigned)dm.B * dm.Hq * dm.n_sel;
-    if (dm.bs == 64) q_pool_block<T, D, 64><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q),
-                                                                           static_cast<T *>(qsel));
-    else q_pool_block<T, D, 128><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q),
-                                                                 static_cast<T *>(qsel));
+  if (dm.group == 0) {   // query blocks of 64 or 128 rows, one per wave
+    const long long nblk = (long long)dm.B * dm.Hq * dm.n_sel;
+    const unsigned grid = (unsigned)((nblk + kStatsThreads / 64 - 1) / (kStatsThreads / 64));
+    if (dm.bs == 64) q_pool_wave<T, D, 64><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q),
+                                                                          static_cast<T *>(qsel));
+    else q_pool_wave<T, D, 128><<<grid, kStatsThreads, 0, st>>>(dm, static_cast<const T *>(Q),
+                                                                static_cast<T *>(qsel));
     return hipGetLastError();
   }
   constexpr int CPR = D / (16 / sizeof(T));
