@@ -345,17 +345,26 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
                   if (r == mrow) v = ak[r];
                 am[t] = v * dm.scale;
               }
+              // the fragments of NG output tiles are loaded together (one
+              // memory latency per group, not one per fragment)
+              constexpr int NG = 4;
 #pragma unroll
-              for (int nt = 0; nt < D / 16; ++nt) {
-                f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+              for (int n0 = 0; n0 < D / 16; n0 += NG) {
+                u32x4_t hb[NG][D / 32];
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                  const u32x4_t hb = *reinterpret_cast<const u32x4_t *>(
-                      Hj + (size_t)(nt * 16 + (l & 15)) * D + ks * 32 + 8 * (l >> 4));
-                  u = mfma16(qa[ks], hb, u);
+                for (int g = 0; g < NG; ++g)
+#pragma unroll
+                  for (int ks = 0; ks < D / 32; ++ks)
+                    hb[g][ks] = *reinterpret_cast<const u32x4_t *>(Hj + (size_t)((n0 + g) * 16 + (l & 15)) * D +
+                                                                   ks * 32 + 8 * (l >> 4));
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                  f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int ks = 0; ks < D / 32; ++ks) u = mfma16(qa[ks], hb[g][ks], u);
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) F[n0 + g][t] = fmaf(am[t], u[t], F[n0 + g][t]);
                 }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) F[nt][t] = fmaf(am[t], u[t], F[nt][t]);
               }
               fo = true;
               continue;
