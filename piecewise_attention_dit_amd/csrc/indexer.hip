@@ -111,7 +111,10 @@ struct Shared {
 // row and mark the n_take best in sel[].  NS slots per lane (candidate
 // c = s*64+lane).  Routing (mb non-null): a candidate's score gains
 // lam * mb[cand].
-template <typename T, int D, int NS>
+// ROWWISE: score slot by slot, a candidate row's chunks loaded in groups of
+// eight (few memory latencies, more registers); otherwise chunk by chunk over
+// all slots.  Both sum every score in feature order (identical results).
+template <typename T, int D, int NS, bool ROWWISE = true>
 PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int base, int nc, int n_take,
                          const float *mb, float lam, bool (&sel)[NS], int (&cj)[NS], int32_t *diag) {
   const int l = lane_id();
@@ -137,22 +140,54 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int ba
     sc[s] = 0.0;
     k2[s] = 0.f;
   }
-  constexpr int EPC = 16 / sizeof(T);
-  for (int c0 = 0; c0 < D; c0 += EPC) {
-    double pc[EPC];
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) pc[i] = sh.p[c0 + i];
+  if constexpr (ROWWISE) {
+    // slot by slot: the 16-byte chunks of a lane's candidate row are loaded
+    // eight at a time (one memory latency per group, not per chunk), then
+    // summed in feature order
+    constexpr int EPC = 16 / sizeof(T), CPR = D / EPC, CPG = CPR < 8 ? CPR : 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (!valid[s]) continue;
-      const u32x4_t w = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)cj[s] * D + c0);
+      if (s * 64 >= nc) break;
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) {
-        float kv;
-        if constexpr (sizeof(T) == 2) kv = (i & 1) ? bf16hi(w[i >> 1]) : bf16lo(w[i >> 1]);
-        else kv = __uint_as_float(w[i]);
-        sc[s] = fma(pc[i], (double)kv, sc[s]);
-        k2[s] = fmaf(kv, kv, k2[s]);
+      for (int c0 = 0; c0 < CPR; c0 += CPG) {
+        __builtin_amdgcn_sched_barrier(0);   // one group of loads in registers at a time
+        u32x4_t w[CPG];
+#pragma unroll
+        for (int c = 0; c < CPG; ++c)
+          w[c] = valid[s] ? *reinterpret_cast<const u32x4_t *>(kbase + (size_t)cj[s] * D + (c0 + c) * EPC)
+                          : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < CPG; ++c)
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) {
+            float kv;
+            if constexpr (sizeof(T) == 2) kv = (i & 1) ? bf16hi(w[c][i >> 1]) : bf16lo(w[c][i >> 1]);
+            else kv = __uint_as_float(w[c][i]);
+            sc[s] = fma(sh.p[(c0 + c) * EPC + i], (double)kv, sc[s]);
+            k2[s] = fmaf(kv, kv, k2[s]);
+          }
+      }
+    }
+  } else {
+    // chunk by chunk over every slot (fewer registers; one memory latency
+    // per chunk)
+    constexpr int EPC = 16 / sizeof(T);
+    for (int c0 = 0; c0 < D; c0 += EPC) {
+      double pc[EPC];
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) pc[i] = sh.p[c0 + i];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (!valid[s]) continue;
+        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)cj[s] * D + c0);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) {
+          float kv;
+          if constexpr (sizeof(T) == 2) kv = (i & 1) ? bf16hi(w[i >> 1]) : bf16lo(w[i >> 1]);
+          else kv = __uint_as_float(w[i]);
+          sc[s] = fma(pc[i], (double)kv, sc[s]);
+          k2[s] = fmaf(kv, kv, k2[s]);
+        }
       }
     }
   }
@@ -371,7 +406,7 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
   {
     bool sel[kMaxSlots];
     int cj[kMaxSlots];
-    select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C, mb, dm.route_lambda, sel, cj, diag);
+    select_row<T, D, kMaxSlots, false>(sh, kbase, nullptr, c0, nc - c0, C, mb, dm.route_lambda, sel, cj, diag);
     write_sorted<kMaxSlots>(sel, cj, sh.clist, C);
     if (cand) {
       __syncthreads();
@@ -388,7 +423,7 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
     load_p<T, D>(sh, Q + ((size_t)bh * dm.L + t) * D);
     bool sel[4];
     int cj[4];
-    select_row<T, D, 4>(sh, kbase, sh.clist, 0, C, n_take, mb, dm.route_lambda, sel, cj, diag);
+    select_row<T, D, 4, false>(sh, kbase, sh.clist, 0, C, n_take, mb, dm.route_lambda, sel, cj, diag);
     const int ct = min(dm.sink, pisa_row_geometry(dm, t, &own, &lo));
     int32_t *out = idx + ((size_t)bh * dm.n_rows + t) * dm.klist;
     for (int c = lane_id(); c < ct; c += 64) out[c] = c;
@@ -756,7 +791,7 @@ __device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_
   wave_lds_sync();
   bool sel[NS];
   int cj[NS];
-  select_row<uint16_t, D, NS>(sh, kbase, list ? sh.clist : nullptr, base, nc, n_take, mb, lam, sel, cj, diag);
+  select_row<uint16_t, D, NS, false>(sh, kbase, list ? sh.clist : nullptr, base, nc, n_take, mb, lam, sel, cj, diag);
   write_sorted_lds<NS>(sel, cj, lout, gout, len);
   if (diag && l == 0) atomicAdd(&diag[2], 1);
   wave_lds_sync();
@@ -986,6 +1021,9 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           ka[ks] = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)j * D + 16 * ks + 8 * hl);
+        // keep the gathered row's loads together (otherwise they are issued
+        // one at a time, each waited for before its MFMA)
+        __builtin_amdgcn_sched_barrier(0);
         f32x16_t acc = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], mq[ks], acc);
