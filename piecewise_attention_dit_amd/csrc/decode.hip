@@ -445,16 +445,21 @@ __global__ __launch_bounds__(64) void decode_combine(DecArgs a, void *O, float *
   const int row = blockIdx.x, l = threadIdx.x;
   const int NWK = a.splits * kDecWaves;   // <= 128
   const float *pr = a.part + (size_t)row * NWK * PW;
-  float mi[2] = {kNegInfD, kNegInfD}, li[2] = {0.f, 0.f}, ai[2] = {0.f, 0.f};
+  float mi[2], li[2], ai[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = l + 64 * u;
-    if (i < NWK) {
-      mi[u] = pr[(size_t)i * PW];
-      li[u] = pr[(size_t)i * PW + 1];
-      ai[u] = pr[(size_t)i * PW + 2];
-    }
+  for (int u = 0; u < 2; ++u) {   // both loads issued before either is used
+    const int i = l + 64 * u, ic = i < NWK ? i : NWK - 1;
+    mi[u] = pr[(size_t)ic * PW];
+    li[u] = pr[(size_t)ic * PW + 1];
+    ai[u] = pr[(size_t)ic * PW + 2];
   }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (l + 64 * u >= NWK) {
+      mi[u] = kNegInfD;
+      li[u] = 0.f;
+      ai[u] = 0.f;
+    }
   const float m = wmax(fmaxf(mi[0], mi[1]));
   float Ls = 0.f, As = 0.f;
 #pragma unroll
@@ -469,17 +474,22 @@ __global__ __launch_bounds__(64) void decode_combine(DecArgs a, void *O, float *
   const float L = wsum(Ls), A = wsum(As);
   __syncthreads();
   float o[EPL] = {};
-  for (int i0 = 0; i0 < NWK; i0 += 8) {
-    float v[8][EPL];
+  // partials in groups of 32, each group's loads issued together (four
+  // memory latencies for 128 partials), summed in worker order; rows past
+  // the last partial are a valid row weighted by zero (adds exactly nothing)
+  constexpr int PG = 32;
+  for (int i0 = 0; i0 < NWK; i0 += PG) {
+    float v[PG][EPL];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      if (i0 + t < NWK)
+    for (int t = 0; t < PG; ++t) {
+      const int i = i0 + t < NWK ? i0 + t : NWK - 1;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) v[t][e] = pr[(size_t)(i0 + t) * PW + 4 + EPL * l + e];
+      for (int e = 0; e < EPL; ++e) v[t][e] = pr[(size_t)i * PW + 4 + EPL * l + e];
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (i0 + t >= NWK) break;
-      const float c = cw[i0 + t];
+    for (int t = 0; t < PG; ++t) {
+      const float c = i0 + t < NWK ? cw[i0 + t] : 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = fmaf(c, v[t][e], o[e]);
     }
