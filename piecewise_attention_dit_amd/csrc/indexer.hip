@@ -107,16 +107,47 @@ struct Shared {
   int64_t kul[kLimbs * 64];
 };
 
+// float64 score p . k and |k|^2 (fp32) of one candidate row per lane: the
+// row's 16-byte chunks loaded eight at a time (one memory latency per group,
+// not per chunk), summed in feature order.  A lane with ok false scores 0.
+template <typename T, int D>
+PISA_DEV void score_slot(const Shared &sh, const T *row, bool ok, double &sc, float &k2) {
+  constexpr int EPC = 16 / sizeof(T), CPR = D / EPC, CPG = CPR < 8 ? CPR : 8;
+  sc = 0.0;
+  k2 = 0.f;
+#pragma unroll
+  for (int c0 = 0; c0 < CPR; c0 += CPG) {
+    __builtin_amdgcn_sched_barrier(0);   // one group of loads in registers at a time
+    u32x4_t w[CPG];
+#pragma unroll
+    for (int c = 0; c < CPG; ++c)
+      w[c] = ok ? *reinterpret_cast<const u32x4_t *>(row + (c0 + c) * EPC) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < CPG; ++c)
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) {
+        float kv;
+        if constexpr (sizeof(T) == 2) kv = (i & 1) ? bf16hi(w[c][i >> 1]) : bf16lo(w[c][i >> 1]);
+        else kv = __uint_as_float(w[c][i]);
+        sc = fma(sh.p[(c0 + c) * EPC + i], (double)kv, sc);
+        k2 = fmaf(kv, kv, k2);
+      }
+  }
+}
+
 // Rank the candidates cand(c) = (list ? list[c] : base + c), c < nc, of one
 // row and mark the n_take best in sel[].  NS slots per lane (candidate
 // c = s*64+lane).  Routing (mb non-null): a candidate's score gains
 // lam * mb[cand].
-// ROWWISE: score slot by slot, a candidate row's chunks loaded in groups of
-// eight (few memory latencies, more registers); otherwise chunk by chunk over
-// all slots.  Both sum every score in feature order (identical results).
-template <typename T, int D, int NS, bool ROWWISE = true>
+// ROWWISE: score slot by slot (score_slot: few memory latencies, more
+// registers); otherwise chunk by chunk over all slots.  PRE: the scores and
+// squared norms were computed by score_slot beforehand and stand in LDS
+// (psc, pk2: [NS][64], slot-major).  All three sum every score in feature
+// order (identical results).
+template <typename T, int D, int NS, bool ROWWISE = true, bool PRE = false>
 PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int base, int nc, int n_take,
-                         const float *mb, float lam, bool (&sel)[NS], int (&cj)[NS], int32_t *diag) {
+                         const float *mb, float lam, bool (&sel)[NS], int (&cj)[NS], int32_t *diag,
+                         const double *psc = nullptr, const float *pk2 = nullptr) {
   const int l = lane_id();
   bool valid[NS];
 #pragma unroll
@@ -140,33 +171,18 @@ PISA_DEV void select_row(Shared &sh, const T *kbase, const int32_t *list, int ba
     sc[s] = 0.0;
     k2[s] = 0.f;
   }
-  if constexpr (ROWWISE) {
-    // slot by slot: the 16-byte chunks of a lane's candidate row are loaded
-    // eight at a time (one memory latency per group, not per chunk), then
-    // summed in feature order
-    constexpr int EPC = 16 / sizeof(T), CPR = D / EPC, CPG = CPR < 8 ? CPR : 8;
+  if constexpr (PRE) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s * 64 >= nc) break;
+      sc[s] = psc[s * 64 + l];
+      k2[s] = pk2[s * 64 + l];
+    }
+  } else if constexpr (ROWWISE) {
 #pragma unroll
-      for (int c0 = 0; c0 < CPR; c0 += CPG) {
-        __builtin_amdgcn_sched_barrier(0);   // one group of loads in registers at a time
-        u32x4_t w[CPG];
-#pragma unroll
-        for (int c = 0; c < CPG; ++c)
-          w[c] = valid[s] ? *reinterpret_cast<const u32x4_t *>(kbase + (size_t)cj[s] * D + (c0 + c) * EPC)
-                          : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < CPG; ++c)
-#pragma unroll
-          for (int i = 0; i < EPC; ++i) {
-            float kv;
-            if constexpr (sizeof(T) == 2) kv = (i & 1) ? bf16hi(w[c][i >> 1]) : bf16lo(w[c][i >> 1]);
-            else kv = __uint_as_float(w[c][i]);
-            sc[s] = fma(sh.p[(c0 + c) * EPC + i], (double)kv, sc[s]);
-            k2[s] = fmaf(kv, kv, k2[s]);
-          }
-      }
+    for (int s = 0; s < NS; ++s) {
+      if (s * 64 >= nc) break;
+      score_slot<T, D>(sh, kbase + (size_t)cj[s] * D, valid[s], sc[s], k2[s]);
     }
   } else {
     // chunk by chunk over every slot (fewer registers; one memory latency
@@ -1085,24 +1101,56 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
 // Decode: the kept list of one new token (q [B, Hq, d]) at position pos, a
 // causal token row: sinks, then the top-k of candidates [c0, lo) by q . ksel_j
 // (+ lam mcov_j), as select_row decides it.
+// Decode: one workgroup of kDecIdxWaves waves per (b, head).  The waves
+// score the candidate slots s = w, w + kDecIdxWaves, ... (score_slot, into
+// LDS), then wave 0 selects over all of them (select_row with the scores
+// given).  A decode row has a single wave's worth of selection work but up
+// to 16 slots of candidate rows to load; sharing the loads cuts the chain of
+// memory latencies the row waits for.
+constexpr int kDecIdxWaves = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void indexer_decode(PisaDims dm, int pos, const T *__restrict__ q,
-                                                     const T *__restrict__ ksel, const float *__restrict__ mcov,
-                                                     int32_t *__restrict__ idx, int32_t *diag) {
+__global__ __launch_bounds__(kDecIdxWaves * 64) void indexer_decode(PisaDims dm, int pos, const T *__restrict__ q,
+                                                                    const T *__restrict__ ksel,
+                                                                    const float *__restrict__ mcov,
+                                                                    int32_t *__restrict__ idx, int32_t *diag) {
   __shared__ Shared sh;
+  __shared__ double psc[kMaxSlots * 64];
+  __shared__ float pk2[kMaxSlots * 64];
   const int row = blockIdx.x;   // b * Hq + h
   const int b = row / dm.Hq, h = row % dm.Hq;
   const int hk = h * dm.Hkv / dm.Hq;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const T *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
   int own, lo;
   const int nc = pisa_row_geometry(dm, pos, &own, &lo);
   const int c0 = min(dm.sink, nc);
   const int n_take = min(dm.topk, nc - c0);
-  load_p<T, D>(sh, q + (size_t)row * D);
+  const int ncand = nc - c0;
+  for (int c = threadIdx.x; c < D; c += kDecIdxWaves * 64) {
+    const float v = load_elem(q + (size_t)row * D, c);
+    sh.pf[c] = v;
+    sh.p[c] = (double)v;
+  }
+  __syncthreads();
+  if (n_take > 0 && n_take < ncand) {
+    for (int sl = w; sl * 64 < ncand; sl += kDecIdxWaves) {
+      const int c = sl * 64 + l;
+      const bool ok = c < ncand;
+      double scv;
+      float k2v;
+      score_slot<T, D>(sh, kbase + (size_t)(ok ? c0 + c : 0) * D, ok, scv, k2v);
+      psc[sl * 64 + l] = scv;
+      pk2[sl * 64 + l] = k2v;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
   bool sel[kMaxSlots];
   int cj[kMaxSlots];
   const float *mb = mcov ? mcov + ((size_t)b * dm.Hkv + hk) * dm.n_blk : nullptr;
-  select_row<T, D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, n_take, mb, dm.route_lambda, sel, cj, diag);
+  select_row<T, D, kMaxSlots, true, true>(sh, kbase, nullptr, c0, ncand, n_take, mb, dm.route_lambda, sel, cj,
+                                          diag, psc, pk2);
   int32_t *out = idx + (size_t)row * dm.klist;
   for (int c = lane_id(); c < c0; c += 64) out[c] = c;
   write_sorted<kMaxSlots>(sel, cj, out + c0, dm.klist - c0);
@@ -1155,17 +1203,17 @@ hipError_t launch_decode_topk(const PisaDims &dm, int pos, const void *q, const 
   const unsigned grid = (unsigned)dm.B * dm.Hq;
   if (dm.dtype == 0) {
     if (dm.d == 64)
-      indexer_decode<uint16_t, 64><<<grid, 64, 0, st>>>(dm, pos, static_cast<const uint16_t *>(q),
+      indexer_decode<uint16_t, 64><<<grid, kDecIdxWaves * 64, 0, st>>>(dm, pos, static_cast<const uint16_t *>(q),
                                                         static_cast<const uint16_t *>(ksel), mcov, idx, diag);
     else
-      indexer_decode<uint16_t, 128><<<grid, 64, 0, st>>>(dm, pos, static_cast<const uint16_t *>(q),
+      indexer_decode<uint16_t, 128><<<grid, kDecIdxWaves * 64, 0, st>>>(dm, pos, static_cast<const uint16_t *>(q),
                                                          static_cast<const uint16_t *>(ksel), mcov, idx, diag);
   } else {
     if (dm.d == 64)
-      indexer_decode<float, 64><<<grid, 64, 0, st>>>(dm, pos, static_cast<const float *>(q),
+      indexer_decode<float, 64><<<grid, kDecIdxWaves * 64, 0, st>>>(dm, pos, static_cast<const float *>(q),
                                                      static_cast<const float *>(ksel), mcov, idx, diag);
     else
-      indexer_decode<float, 128><<<grid, 64, 0, st>>>(dm, pos, static_cast<const float *>(q),
+      indexer_decode<float, 128><<<grid, kDecIdxWaves * 64, 0, st>>>(dm, pos, static_cast<const float *>(q),
                                                       static_cast<const float *>(ksel), mcov, idx, diag);
   }
   return hipGetLastError();
