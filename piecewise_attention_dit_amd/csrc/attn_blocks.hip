@@ -43,7 +43,6 @@ constexpr int NW = 8;              // waves per workgroup
 constexpr int NT = NW * 64;
 constexpr int ROWS = NW * 32;      // query rows per workgroup
 constexpr int kNB = 16;            // Taylor entries per logits batch
-constexpr int kRingH = 3;
 constexpr float kRescale = 8.f;    // lazy max threshold (log2 units)
 constexpr int kMaxK = 64;          // kept-list capacity per part
 
@@ -61,8 +60,17 @@ struct Cfg {
   static constexpr int EX_K = 0, EX_V = 2 * SLOT, EX_END = 4 * SLOT;
   static constexpr int HT = D * D * 2;
   static constexpr int HCH = HT / 1024;
+  // first-order entries per barrier: a d = 64 entry is 8 MFMAs per wave, too
+  // short to carry a barrier of its own, so four share one; the H ring holds
+  // three groups (the one in use and two ahead)
+  static constexpr int GE = D == 64 ? 4 : 1;
+  static constexpr int RINGH = 3 * GE;
+  // the next batch's rows are staged at group SG, its tables built in group
+  // SG + 1 and published by the barrier of group SG + 2, inside the batch
+  static constexpr int SG = (kNB / 2) / GE < kNB / GE - 3 ? (kNB / 2) / GE : kNB / GE - 3;
+  static_assert(kNB % GE == 0 && SG >= 1 && SG + 2 < kNB / GE, "batch too short for the table pipeline");
   static constexpr int TY_H = 0;
-  static constexpr int TY_KBH = TY_H + kRingH * HT;
+  static constexpr int TY_KBH = TY_H + RINGH * HT;
   static constexpr int TY_KBL = TY_KBH + kNB * D * 2;
   static constexpr int TY_STH = TY_KBL + kNB * D * 2;
   static constexpr int TY_STL = TY_STH + D * kNB * 2;
@@ -505,7 +513,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     auto dma_h = [&](int eg) {
       if (!issuer) return;
       const uint16_t *src = HTh + (size_t)__builtin_amdgcn_readfirstlane(tyl[eg]) * D * D;
-      uint8_t *dst = lds + C::TY_H + (eg % kRingH) * C::HT;
+      uint8_t *dst = lds + C::TY_H + (eg % C::RINGH) * C::HT;
 #pragma unroll
       for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], dst + (w + NDW * u) * 1024);
     };
@@ -527,10 +535,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       }
     };
     stage(0);
-    if (order1) {
-      dma_h(0);
-      if (n_ty > 1) dma_h(1);
-    } else if (hybrid && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
+    if (order1)
+      for (int i = 0; i < 2 * C::GE && i < n_ty; ++i) dma_h(i); else if (hybrid && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
       const uint16_t *src = static_cast<const uint16_t *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
 #pragma unroll
       for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], lds + C::TY_H + (w + NDW * u) * 1024);
@@ -595,9 +601,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         // and the orders without per-entry barriers, build them here once
         // the staged rows have landed
         if (!order1 || eg == 0) {
-          if (!order1) wait_vmcnt<0>();
-          else if (n_ty > 1) wait_vmcnt<2 * PH>();
-          else wait_vmcnt<PH>();
+          // the staged rows were issued before the first two groups' H tiles
+          if (order1 && n_ty >= 2 * C::GE) wait_vmcnt<2 * C::GE * PH>();
+          else wait_vmcnt<0>();
           __syncthreads();   // the previous batch's tables are consumed; staging landed
           build(eg);
           __syncthreads();
@@ -667,21 +673,32 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           }
         }
       }
-      // the next batch's kbar / vsum rows, half a batch ahead (this batch's
-      // tables were built before the batch-start barrier)
-      if (e == kNB / 2 && eg - e + kNB < n_ty) stage(eg - e + kNB);
+      // the next batch's kbar / vsum rows, about half a batch ahead (this
+      // batch's tables were built before the batch-start barrier)
+      const bool staging = e == C::SG * C::GE && eg - e + kNB < n_ty;
+      if (staging) stage(eg - e + kNB);
       if (!order1) continue;
-      // first order for entry eg: H ring (3 deep, two ahead)
-      if (eg + 1 < n_ty) wait_vmcnt<PH>();
-      else wait_vmcnt<0>();
-      __syncthreads();   // H_eg landed for all waves; slot (eg + 2) % 3 is free
-      if (eg + 2 < n_ty) dma_h(eg + 2);
+      // first order for entry eg: H ring of three groups of GE entries, the
+      // group in use and two ahead; one barrier per group
+      if (e % C::GE == 0) {
+        // wait for this group's tiles: the next group's (issued after them)
+        // and the rows just staged may stay in flight; a short next group
+        // (the phase's end) is waited for too
+        if (eg + 2 * C::GE <= n_ty) {
+          if (staging) wait_vmcnt<C::GE * PH + PS>();
+          else wait_vmcnt<C::GE * PH>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        __syncthreads();   // the group's H tiles landed for all waves; the previous group's slots are free
+        for (int i = 0; i < C::GE && eg + 2 * C::GE + i < n_ty; ++i) dma_h(eg + 2 * C::GE + i);
+      }
       if ((tmask >> e) & 1u) {
         // u = H_j^T Q^T tile by tile (MFMA k: output tile k / KS, K-step
         // k % KS), scheduled by hand: the LDS read of the fragment four MFMAs
         // ahead, and chunk c of O += (alpha scale) u, 16 / KS values of tile
         // c / KS, two MFMAs after that tile's last MFMA.
-        const uint8_t *hp = lds + C::TY_H + (eg % kRingH) * C::HT;
+        const uint8_t *hp = lds + C::TY_H + (eg % C::RINGH) * C::HT;
         const float al = alp[e * 32 + lq];
         constexpr int KS = D / 16, NMT = NE * KS, FPC = 16 / KS;
         auto hfrag = [&](int k) { return frag_a<D>(hp, (k / KS) * 32 + lq, 2 * (k % KS) + hl); };
@@ -708,12 +725,11 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
 #pragma unroll
         for (int c = NMT - KS - 1; c < NMT; ++c) fchunk(u, c);
       }
-      // the next batch's tables: its staged rows landed before this entry's
-      // barrier (they were issued ahead of H_{eg+1}), this batch's tables were
-      // read before entry eg - e + 1's barrier, and the barriers of the
-      // entries up to the batch's end publish them
-      static_assert(kNB / 2 + 2 < kNB, "a per-entry barrier follows the early build");
-      if (e == kNB / 2 + 1 && eg - e + kNB < n_ty) build(eg - e + kNB);
+      // the next batch's tables, at the end of group SG + 1: its staged rows
+      // landed before this group's barrier (they were issued ahead of the
+      // following group's H tiles), this batch's tables were read before the
+      // batch's first barrier, and the barrier of group SG + 2 publishes them
+      if (e == (C::SG + 1) * C::GE + C::GE - 1 && eg - e + kNB < n_ty) build(eg - e + kNB);
     }
     if (hybrid) {   // O^T += (scale sum alpha) Hbar^T Q^T, once per row
       wait_vmcnt<0>();
