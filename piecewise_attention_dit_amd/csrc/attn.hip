@@ -585,7 +585,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
       } else {
         wait_vmcnt<0>();
       }
-      __syncthreads();
+      lds_barrier();   // H_eg landed for all waves; H_{eg+1} stays in flight
       uint32_t bit = 0;
 #pragma unroll
       for (int n = 0; n < NQ; ++n) bit |= (tmask[n] >> e) & 1u;

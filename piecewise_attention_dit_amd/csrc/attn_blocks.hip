@@ -604,9 +604,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           // the staged rows were issued before the first two groups' H tiles
           if (order1 && n_ty >= 2 * C::GE) wait_vmcnt<2 * C::GE * PH>();
           else wait_vmcnt<0>();
-          __syncthreads();   // the previous batch's tables are consumed; staging landed
+          lds_barrier();   // the previous batch's tables are consumed; staging landed
           build(eg);
-          __syncthreads();
+          lds_barrier();
         }
         {   // lane en < nb decides entry en for this wave's part
           bool mine = false;
@@ -690,7 +690,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         } else {
           wait_vmcnt<0>();
         }
-        __syncthreads();   // the group's H tiles landed for all waves; the previous group's slots are free
+        // the group's H tiles landed for all waves; the previous group's slots
+        // are free (the next group's tiles stay in flight)
+        lds_barrier();
         for (int i = 0; i < C::GE && eg + 2 * C::GE + i < n_ty; ++i) dma_h(eg + 2 * C::GE + i);
       }
       if ((tmask >> e) & 1u) {
