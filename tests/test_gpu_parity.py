@@ -68,6 +68,11 @@ def test_parity_cases(name):
     dict(L=500, block=64, topk=2, d=64, group=4, n_cand=5, dtype="f32", causal=True,
          taylor="order0", route_lambda=0.01),                    # routing, fp32 PIVOT
     dict(L=777, block=128, topk=1, d=64, taylor="order1", route_lambda=0.02),
+    # d 64 first order takes four Taylor entries per barrier: two batches of
+    # entries, the last group short
+    dict(L=1500, block=64, topk=2, d=64, taylor="order1"),
+    dict(L=1700, block=64, topk=2, d=64, taylor="order1", causal=True, window=200),
+    dict(L=2900, block=128, topk=2, d=64, taylor="order1"),
 ])
 def test_edge_cases(kw):
     base = dict(B=1, Hq=2, Hkv=2, L=256, d=128, dtype="bf16", block=64, topk=2, window=0, group=0,
