@@ -29,7 +29,9 @@
 //   * the Taylor phase walks the union of the parts' Taylor blocks, 16 per
 //     logits batch (a^T = Kbar Q^T, zero order Sigma^T alpha^T with bf16
 //     hi/lo splits), and per block the first order u = H_j^T Q^T, added as
-//     O^T += (alpha scale) u in fp32; H tiles in a 3-deep ring, two ahead
+//     O^T += (alpha scale) u in fp32; H tiles in a ring of three groups
+//     of blocks (one block for d = 128, four for d = 64), two groups ahead,
+//     one barrier per group
 //     (hybrid order: the zero order only, plus one u = Hbar^T Q^T per row
 //     scaled by the row's summed Taylor weights);
 //   * row maxima move only when a logit exceeds them by more than 2^8.
@@ -597,8 +599,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       if (e == 0) {
         const int nb = min(kNB, n_ty - eg);
         // first order: the tables of every batch after the first were built
-        // half a batch earlier, between per-entry barriers; the first batch,
-        // and the orders without per-entry barriers, build them here once
+        // about half a batch earlier, between per-group barriers; the first
+        // batch, and the orders without those barriers, build them here once
         // the staged rows have landed
         if (!order1 || eg == 0) {
           // the staged rows were issued before the first two groups' H tiles
