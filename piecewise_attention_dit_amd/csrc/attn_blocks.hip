@@ -29,9 +29,9 @@
 //   * the Taylor phase walks the union of the parts' Taylor blocks, 16 per
 //     logits batch (a^T = Kbar Q^T, zero order Sigma^T alpha^T with bf16
 //     hi/lo splits), and per block the first order u = H_j^T Q^T, added as
-//     O^T += (alpha scale) u in fp32; H tiles in a ring of three groups
-//     of blocks (one block for d = 128, four for d = 64), two groups ahead,
-//     one barrier per group
+//     O^T += (alpha scale) u in fp32; H tiles stream through an LDS ring in
+//     groups of blocks (two for d = 128, one group ahead; four for d = 64,
+//     two groups ahead), one barrier per group
 //     (hybrid order: the zero order only, plus one u = Hbar^T Q^T per row
 //     scaled by the row's summed Taylor weights);
 //   * row maxima move only when a logit exceeds them by more than 2^8.
@@ -62,11 +62,14 @@ struct Cfg {
   static constexpr int EX_K = 0, EX_V = 2 * SLOT, EX_END = 4 * SLOT;
   static constexpr int HT = D * D * 2;
   static constexpr int HCH = HT / 1024;
-  // first-order entries per barrier: a d = 64 entry is 8 MFMAs per wave, too
-  // short to carry a barrier of its own, so four share one; the H ring holds
-  // three groups (the one in use and two ahead)
-  static constexpr int GE = D == 64 ? 4 : 1;
-  static constexpr int RINGH = 3 * GE;
+  // first-order entries per barrier (a group) and the H ring.  d = 64: an
+  // entry is 8 MFMAs per wave, so four share a barrier, in a ring of three
+  // groups (the one in use and two ahead).  d = 128: two entries per barrier
+  // in a ring of two groups (the one in use and the next), which is what
+  // fits in LDS beside the batch tables.
+  static constexpr int GE = D == 64 ? 4 : 2;
+  static constexpr int RINGH = D == 64 ? 12 : 4;
+  static constexpr int AHEAD = RINGH / GE - 1;                // groups in flight ahead
   // the next batch's rows are staged at group SG, its tables built in group
   // SG + 1 and published by the barrier of group SG + 2, inside the batch
   static constexpr int SG = (kNB / 2) / GE < kNB / GE - 3 ? (kNB / 2) / GE : kNB / GE - 3;
@@ -76,10 +79,15 @@ struct Cfg {
   static constexpr int TY_KBL = TY_KBH + kNB * D * 2;
   static constexpr int TY_STH = TY_KBL + kNB * D * 2;
   static constexpr int TY_STL = TY_STH + D * kNB * 2;
-  static constexpr int TY_AL = TY_STL + D * kNB * 2;          // fp32 [wave][entry][32 rows]
-  static constexpr int TY_NJ = TY_AL + NW * kNB * 32 * 4;
-  static constexpr int TY_STG = TY_NJ + kNB * 4;              // fp32 [2][kNB][D]: next batch's kbar, vsum rows
-  static constexpr int TY_END = TY_STG + 2 * kNB * D * 4;
+  static constexpr int TY_AL = TY_STL + D * kNB * 2;          // bf16 [wave][entry][32 rows]
+  static constexpr int TY_NJ = TY_AL + NW * kNB * 32 * 2;
+  static constexpr int TY_END = TY_NJ + kNB * 4;
+  // staging of the next batch's kbar, vsum rows (fp32 [2][kNB][D]): at first
+  // order over the batch tables (dead between a batch's start and the next
+  // build), otherwise in ring slot 1 (unused without first order)
+  static constexpr int STG_BYTES = 2 * kNB * D * 4;
+  static_assert(STG_BYTES == TY_AL - TY_KBH, "the staging area overlays the four batch tables");
+  static_assert(STG_BYTES <= HT, "the staging area fits a ring slot");
   static constexpr int MAIN = EX_END > TY_END ? EX_END : TY_END;
   static constexpr int LST = MAIN;                            // uint16 [P][kMaxK] kept lists
   static constexpr int PRV = LST + P * kMaxK * 2;             // uint16 [P][kMaxK] private parts
@@ -90,7 +98,7 @@ struct Cfg {
   static constexpr int CNT = TYL + 1024 * 2;                  // int [16]
   static constexpr int TOTAL = CNT + 64;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  static constexpr int STGCH = 2 * kNB * D * 4 / 1024;          // staging kilobytes per batch
+  static constexpr int STGCH = STG_BYTES / 1024;               // staging kilobytes per batch
   static_assert(CPS % (NW / 2) == 0 && HCH % (NW / 2) == 0 && STGCH % (NW / 2) == 0,
                 "DMA must split evenly over the issuing waves");
   static_assert(kNB * (D / 8) <= NT, "one table unit per thread");
@@ -495,7 +503,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     const uint16_t *HTh = static_cast<const uint16_t *>(a.HT) + soff * D * D;
     uint8_t *kbh = lds + C::TY_KBH, *kbl = lds + C::TY_KBL;
     uint8_t *sth = lds + C::TY_STH, *stl = lds + C::TY_STL;
-    float *alp = reinterpret_cast<float *>(lds + C::TY_AL) + w * kNB * 32;
+    uint16_t *alp = reinterpret_cast<uint16_t *>(lds + C::TY_AL) + w * kNB * 32;
     float *nj = reinterpret_cast<float *>(lds + C::TY_NJ);
     const uint32_t *kb_me = kbm + part * 32;
     const bool order1 = taylor == 2, hybrid = taylor == 3;
@@ -522,6 +530,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     // staging kilobyte c holds rows c * RPC .. of [kbar entries | vsum entries]
     constexpr int RPC = 1024 / (D * 4), LPR = 64 / RPC;   // rows per kilobyte, lanes per row
     const int tbl_bytes = dm.n_blk * D * 4;
+    uint8_t *stgb = lds + (order1 ? C::TY_KBH : C::TY_H + C::HT);
     auto stage = [&](int b0) {
       if (!issuer) return;
       const int nb = min(kNB, n_ty - b0);
@@ -533,29 +542,34 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         const int j = tyl[b0 + min(en, nb - 1)];
         const int voff = en < nb ? j * D * 4 + (l % LPR) * 16 : tbl_bytes;   // past the end: zeros
         dma16_buf(row < kNB ? (const void *)kbar : (const void *)vsum, tbl_bytes, voff,
-                  lds + C::TY_STG + c * 1024);
+                  stgb + c * 1024);
       }
     };
     stage(0);
-    if (order1)
-      for (int i = 0; i < 2 * C::GE && i < n_ty; ++i) dma_h(i); else if (hybrid && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
+    if (order1) {
+      for (int i = 0; i < C::AHEAD * C::GE && i < n_ty; ++i) dma_h(i);
+    } else if (hybrid && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
       const uint16_t *src = static_cast<const uint16_t *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
 #pragma unroll
       for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], lds + C::TY_H + (w + NDW * u) * 1024);
     }
-    const float *stg = reinterpret_cast<const float *>(lds + C::TY_STG);
+    const float *stg = reinterpret_cast<const float *>(stgb);
     // Taylor tables of the batch that starts at entry b0, from its staged
     // kbar / vsum rows: kbar as bf16 hi + lo rows (swizzled like K tiles),
     // Sigma^T as bf16 hi and lo in the perm16 layout, and n_j.  Built by the
-    // waves that issue no DMA first (thread (tid + NT / 2) % NT).
+    // waves that issue no DMA first (thread (tid + NT / 2) % NT).  Every
+    // thread calls it: at first order the staged rows overlay the tables, so
+    // all of them are read before the workgroup meets and any is written.
     auto build = [&](int b0) {
       const int nb = min(kNB, n_ty - b0);
       const int bt = (tid + NT / 2) % NT;
-      if (bt < kNB * (D / 8)) {
-        const int en = bt / (D / 8), ch = bt % (D / 8);
-        u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
-        float sv[8];
-        if (en < nb) {
+      const bool act = bt < kNB * (D / 8);
+      const int en = bt / (D / 8), ch = bt % (D / 8);
+      u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
+      float sv[8];
+      float njv = 0.f;
+      {
+        if (act && en < nb) {
           const int j = tyl[b0 + en];
           const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8);
           const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8 + 4);
@@ -570,12 +584,15 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           }
           sv[0] = v0[0]; sv[1] = v0[1]; sv[2] = v0[2]; sv[3] = v0[3];
           sv[4] = v1[0]; sv[5] = v1[1]; sv[6] = v1[2]; sv[7] = v1[3];
-          if (ch == 0) nj[en] = (float)min(dm.bs, dm.L - j * dm.bs);
+          njv = (float)min(dm.bs, dm.L - j * dm.bs);
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) sv[i] = 0.f;
-          if (ch == 0) nj[en] = 0.f;
         }
+      }
+      if (order1) lds_barrier();
+      if (act) {
+        if (ch == 0) nj[en] = njv;
         const int sw = (ch ^ kswz<D>(en)) << 4;
         *reinterpret_cast<u32x4_t *>(kbh + en * (2 * D) + sw) = hi;
         *reinterpret_cast<u32x4_t *>(kbl + en * (2 * D) + sw) = lo4;
@@ -604,7 +621,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         // the staged rows have landed
         if (!order1 || eg == 0) {
           // the staged rows were issued before the first two groups' H tiles
-          if (order1 && n_ty >= 2 * C::GE) wait_vmcnt<2 * C::GE * PH>();
+          if (order1 && n_ty >= C::AHEAD * C::GE) wait_vmcnt<C::AHEAD * C::GE * PH>();
           else wait_vmcnt<0>();
           lds_barrier();   // the previous batch's tables are consumed; staging landed
           build(eg);
@@ -655,7 +672,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
             at[r] = al;
             dpart += al * nj[en];
             apart += al;
-            if (order1) alp[en * 32 + lq] = al * dm.scale;
+            if (order1) alp[en * 32 + lq] = (uint16_t)f32_to_bf16(al * dm.scale);
           }
           dpart = pair_sum_f(dpart);
           d_run += dpart;
@@ -680,22 +697,22 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       const bool staging = e == C::SG * C::GE && eg - e + kNB < n_ty;
       if (staging) stage(eg - e + kNB);
       if (!order1) continue;
-      // first order for entry eg: H ring of three groups of GE entries, the
-      // group in use and two ahead; one barrier per group
+      // first order for entry eg: H ring of groups of GE entries, the group
+      // in use and AHEAD groups in flight; one barrier per group
       if (e % C::GE == 0) {
-        // wait for this group's tiles: the next group's (issued after them)
+        // wait for this group's tiles: later groups' tiles (issued after them)
         // and the rows just staged may stay in flight; a short next group
         // (the phase's end) is waited for too
-        if (eg + 2 * C::GE <= n_ty) {
-          if (staging) wait_vmcnt<C::GE * PH + PS>();
-          else wait_vmcnt<C::GE * PH>();
+        if (eg + C::AHEAD * C::GE <= n_ty) {
+          if (staging) wait_vmcnt<(C::AHEAD - 1) * C::GE * PH + PS>();
+          else wait_vmcnt<(C::AHEAD - 1) * C::GE * PH>();
         } else {
           wait_vmcnt<0>();
         }
         // the group's H tiles landed for all waves; the previous group's slots
         // are free (the next group's tiles stay in flight)
         lds_barrier();
-        for (int i = 0; i < C::GE && eg + 2 * C::GE + i < n_ty; ++i) dma_h(eg + 2 * C::GE + i);
+        for (int i = 0; i < C::GE && eg + C::AHEAD * C::GE + i < n_ty; ++i) dma_h(eg + C::AHEAD * C::GE + i);
       }
       if ((tmask >> e) & 1u) {
         // u = H_j^T Q^T tile by tile (MFMA k: output tile k / KS, K-step
@@ -703,7 +720,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         // ahead, and chunk c of O += (alpha scale) u, 16 / KS values of tile
         // c / KS, two MFMAs after that tile's last MFMA.
         const uint8_t *hp = lds + C::TY_H + (eg % C::RINGH) * C::HT;
-        const float al = alp[e * 32 + lq];
+        const float al = bf16_to_f32(alp[e * 32 + lq]);
         constexpr int KS = D / 16, NMT = NE * KS, FPC = 16 / KS;
         auto hfrag = [&](int k) { return frag_a<D>(hp, (k / KS) * 32 + lq, 2 * (k % KS) + hl); };
         auto fchunk = [&](const f32x16_t (&uu)[NE], int c) {
