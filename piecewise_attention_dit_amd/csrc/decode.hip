@@ -530,7 +530,7 @@ hipError_t launch_t(const DecArgs &a, void *O, float *lse, hipStream_t st) {
 }  // namespace
 
 #ifndef PISA_DECODE_WORKGROUPS
-#define PISA_DECODE_WORKGROUPS 1024   // target workgroups of decode_partial over the chip
+#define PISA_DECODE_WORKGROUPS 512   // target workgroups of decode_partial over the chip
 #endif
 
 int decode_splits(const PisaDims &dm) {
