@@ -33,8 +33,10 @@
  *            [j*bs, min(L, (j+1)*bs)) and n_j of them.
  *   Memory   The caller allocates and owns every buffer (inputs, statistics,
  *            index lists, outputs, workspace).  The library allocates no
- *            device memory, keeps no global state other than a thread-local
- *            error text, and is re-entrant.
+ *            device memory and keeps no global state other than a
+ *            thread-local error text and the fixed decode scratch of
+ *            pisa_decode_fwd_noalloc (a static device array); every other
+ *            call is re-entrant.
  *   Errors   Every precondition is checked on the host before anything is
  *            launched.  On failure a call returns a non-zero status, writes
  *            nothing and launches nothing; pisa_last_error() gives the
@@ -242,6 +244,24 @@ pisa_status pisa_decode_fwd(const pisa_params *p, int32_t pos, int32_t ring, con
                             const void *K, const void *V, const pisa_stats *stats,
                             const int32_t *idx, void *O, float *lse, void *ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/* ---- decode without a workspace -------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, arguments, results and error behaviour as pisa_decode_fwd, with
+ * the split-K partials in a fixed scratch array of the library instead of a
+ * caller workspace.  The array holds PISA_DECODE_SCRATCH_BYTES; a problem
+ * whose pisa_workspace_size(p, 3) exceeds it returns PISA_E_WORKSPACE before
+ * anything is launched.  Each device the library runs on holds its own copy
+ * until the process ends.  Nothing is allocated: no hipMalloc / hipFree and no
+ * allocating library call.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (other streams, other threads)
+ * race; calls in stream order do not.  Stale contents from an earlier call do
+ * not matter: every partial is written before it is read. */
+#define PISA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+pisa_status pisa_decode_fwd_noalloc(const pisa_params *p, int32_t pos, int32_t ring, const void *q,
+                                    const void *K, const void *V, const pisa_stats *stats,
+                                    const int32_t *idx, void *O, float *lse, hipStream_t stream);
 
 /* ---- errors and version -------------------------------------------------- */
 const char *pisa_status_string(pisa_status s);

@@ -20,6 +20,8 @@
 // workspace, and decode_combine merges the partials of a row in worker order
 // (deterministic), adding the hybrid order's (scale sum alpha) q Hbar once
 // per row.
+#include <mutex>
+
 #include "device_common.h"
 #include "pisa_internal.h"
 
@@ -560,4 +562,38 @@ hipError_t launch_decode(const PisaDims &dm, int pos, int ring, const void *q, c
   }
   if (bf) return dm.bs == 64 ? launch_t<uint16_t, 128, 64>(a, O, lse, st) : launch_t<uint16_t, 128, 128>(a, O, lse, st);
   return dm.bs == 64 ? launch_t<float, 128, 64>(a, O, lse, st) : launch_t<float, 128, 128>(a, O, lse, st);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for pisa_decode_fwd_noalloc: the split-K partials live in a
+// device array of the library instead of a caller workspace, for callers
+// that cannot allocate.  Each device holds its own copy of the array for the
+// life of the process.  Its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current; host code never passes
+// the array's own name (a host-side stand-in, not a device address).
+// decode_partial writes every partial before decode_combine reads it, so no
+// part of the array needs clearing between calls.  Calls that overlap on one
+// device share the array and race.
+namespace {
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void **ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }

@@ -260,9 +260,15 @@ pisa_status pisa_decode_topk(const pisa_params *p, int32_t pos, const void *q, c
                   "decode_topk");
 }
 
-pisa_status pisa_decode_fwd(const pisa_params *p, int32_t pos, int32_t ring, const void *q, const void *K,
-                            const void *V, const pisa_stats *stats, const int32_t *idx, void *O, float *lse,
-                            void *ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode_fwd entry points (everything but the
+// workspace); on success dm holds the geometry with topk = the list width.
+pisa_status decode_fwd_check(const pisa_params *p, int32_t pos, int32_t ring, const void *q, const void *K,
+                             const void *V, const pisa_stats *stats, const int32_t *idx, void *O, float *lse,
+                             PisaDims *dm_out) {
   PisaDims dm;
   PISA_TRY(make_dims(p, &dm));
   if (!dm.causal) return fail(PISA_E_ARG, "decode needs causal attention");
@@ -283,13 +289,48 @@ pisa_status pisa_decode_fwd(const pisa_params *p, int32_t pos, int32_t ring, con
     PISA_TRY(check_ptr(stats->vsum, "stats.vsum", true));
     PISA_TRY(check_ptr(stats->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
   }
-  const size_t need = decode_workspace_bytes(dm);
-  PISA_TRY(check_ws(ws, ws_bytes, need));
-  if (!aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
+  *dm_out = dm;
+  return PISA_OK;
+}
+
+pisa_status decode_fwd_launch(PisaDims dm, int32_t pos, int32_t ring, const void *q, const void *K, const void *V,
+                              const pisa_stats *stats, const int32_t *idx, void *O, float *lse, void *ws,
+                              hipStream_t stream, const char *what) {
+  const bool ty = dm.taylor != PISA_TAYLOR_NONE;
   dm.topk = dm.klist;   // the kernels take topk as the width of a kept list
   return launched(launch_decode(dm, pos, ring, q, K, V, ty ? stats->kbar : nullptr, ty ? stats->vsum : nullptr,
                                 ty ? stats->HT : nullptr, ring == 0 ? idx : nullptr, O, lse, ws, stream),
-                  "decode_fwd");
+                  what);
+}
+
+}  // namespace
+
+extern "C" {
+
+pisa_status pisa_decode_fwd(const pisa_params *p, int32_t pos, int32_t ring, const void *q, const void *K,
+                            const void *V, const pisa_stats *stats, const int32_t *idx, void *O, float *lse,
+                            void *ws, size_t ws_bytes, hipStream_t stream) {
+  PisaDims dm;
+  PISA_TRY(decode_fwd_check(p, pos, ring, q, K, V, stats, idx, O, lse, &dm));
+  const size_t need = decode_workspace_bytes(dm);
+  PISA_TRY(check_ws(ws, ws_bytes, need));
+  if (!aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
+  return decode_fwd_launch(dm, pos, ring, q, K, V, stats, idx, O, lse, ws, stream, "decode_fwd");
+}
+
+pisa_status pisa_decode_fwd_noalloc(const pisa_params *p, int32_t pos, int32_t ring, const void *q, const void *K,
+                                    const void *V, const pisa_stats *stats, const int32_t *idx, void *O,
+                                    float *lse, hipStream_t stream) {
+  PisaDims dm;
+  PISA_TRY(decode_fwd_check(p, pos, ring, q, K, V, stats, idx, O, lse, &dm));
+  const size_t need = decode_workspace_bytes(dm);
+  if (need > kDecodeScratchBytes)
+    return fail(PISA_E_WORKSPACE, "decode needs %zu bytes of scratch, the library's fixed scratch holds %zu",
+                need, kDecodeScratchBytes);
+  void *ws = nullptr;
+  const hipError_t e = decode_scratch(&ws);
+  if (e != hipSuccess) return fail(PISA_E_HIP, "decode scratch address: %s", hipGetErrorString(e));
+  return decode_fwd_launch(dm, pos, ring, q, K, V, stats, idx, O, lse, ws, stream, "decode_fwd_noalloc");
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/pisa.h"
+
 // Problem geometry derived from pisa_params on the host, passed by value to
 // every kernel.
 struct PisaDims {
@@ -74,6 +76,10 @@ hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, c
                           const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);
 // decode (one new token per row): split-K partials in a workspace, then a merge
 size_t decode_workspace_bytes(const PisaDims &dm);
+// the library's own fixed decode scratch (pisa_decode_fwd_noalloc): capacity
+// in bytes, and its device address on the current device
+constexpr size_t kDecodeScratchBytes = PISA_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(void **ptr);
 hipError_t launch_decode(const PisaDims &dm, int pos, int ring, const void *q, const void *K, const void *V,
                          const float *kbar, const float *vsum, const void *HT, const int32_t *idx, void *O,
                          float *lse, void *ws, hipStream_t st);

@@ -62,9 +62,10 @@ def lib() -> ctypes.CDLL:
         i32 = ctypes.c_int32
         L.pisa_decode_topk.argtypes = [P, i32, vp, S, vp, vp]
         L.pisa_decode_fwd.argtypes = [P, i32, i32, vp, vp, vp, S, vp, vp, vp, vp, sz, vp]
+        L.pisa_decode_fwd_noalloc.argtypes = [P, i32, i32, vp, vp, vp, S, vp, vp, vp, vp]
         for f in ("pisa_validate", "pisa_stats_layout", "pisa_index_layout", "pisa_workspace_size",
                   "pisa_block_stats", "pisa_indexer_topk", "pisa_sparse_attn_fwd", "pisa_decode_topk",
-                  "pisa_decode_fwd"):
+                  "pisa_decode_fwd", "pisa_decode_fwd_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.pisa_status_string.argtypes = [ctypes.c_int]
         L.pisa_status_string.restype = ctypes.c_char_p
@@ -227,6 +228,22 @@ def decode_fwd(p: Params, pos: int, q, k, v, stats=None, idx=None, ring: int = 0
     _check(lib().pisa_decode_fwd(ctypes.byref(p), int(pos), int(ring), _ptr(q), _ptr(k), _ptr(v),
                                  ctypes.byref(cs) if cs is not None else None, _ptr(idx), _ptr(out), _ptr(lse),
                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def decode_fwd_noalloc(p: Params, pos: int, q, k, v, stats=None, idx=None, ring: int = 0, out=None,
+                       lse=None, want_lse=True, stream=None):
+    """decode_fwd with the split-K partials in the library's fixed scratch
+    (no workspace; for callers that cannot allocate).  Allocates out / lse
+    here only when they are not given."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.B, p.Hq), dtype=torch.float32, device=q.device)
+    cs = _cstats(stats) if stats is not None else None
+    _check(lib().pisa_decode_fwd_noalloc(ctypes.byref(p), int(pos), int(ring), _ptr(q), _ptr(k), _ptr(v),
+                                         ctypes.byref(cs) if cs is not None else None, _ptr(idx), _ptr(out),
+                                         _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -162,3 +162,12 @@ def test_launch_calls_reject_before_launch():
                              ws_need, None) == pisa.PISA_E_ARG          # O NULL, after the ring checks pass
     assert b"O is NULL" in L.pisa_last_error()
     assert L.pisa_decode_topk(ctypes.byref(dc), 5, FAKE, ctypes.byref(st), None, None) == pisa.PISA_E_ARG
+    # the no-allocation decode: the same checks, and a problem whose partials
+    # exceed the library's fixed scratch is refused before any GPU call
+    nfwd = lambda pp, pos=5, ring=0: L.pisa_decode_fwd_noalloc(
+        ctypes.byref(pp), pos, ring, FAKE, FAKE, FAKE, ctypes.byref(st), FAKE, FAKE, None, None)
+    assert nfwd(_p(causal=False)) == pisa.PISA_E_ARG and b"causal" in L.pisa_last_error()
+    assert nfwd(dc, pos=1000) == pisa.PISA_E_ARG
+    big = _p(B=64, Hq=128, Hkv=128, L=64, causal=True, topk=0, taylor="none")
+    assert pisa.workspace_size(big, 3) > 16 << 20
+    assert nfwd(big) == pisa.PISA_E_WORKSPACE and b"fixed scratch" in L.pisa_last_error()
