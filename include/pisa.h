@@ -78,7 +78,10 @@ typedef enum {
   PISA_TAYLOR_HYBRID = 3   /* zero order per block, plus one global first-order
                               term q Hbar * sum_j exp(q.kbar_j) in the numerator,
                               Hbar = mean of H_j over all blocks of the (b, kv
-                              head) ([PISA] section 2, hybrid order) */
+                              head) ([PISA] section 2, hybrid order); on a
+                              causal row the mean over the blocks it may see as
+                              Taylor candidates, [0, lo_r), so that no later
+                              token enters the row */
 } pisa_taylor;
 
 /* Problem statement.  Supported today: d in {64, 128}; block in {64, 128};
@@ -105,7 +108,12 @@ typedef struct {
   float route_lambda; /* covariance-aware routing ([PISA] section 2): >= 0;
                        when > 0 every selection score (block rows, PIVOT
                        proxies and members) is the attention score plus
-                       route_lambda * mcov_j.  Needs taylor != NONE. */
+                       route_lambda * mcov_j.  Needs taylor != NONE.  Defined
+                       for non-causal rows only: the page measures the norm
+                       against the mean over all blocks of bidirectional
+                       attention, which on a causal row would carry later
+                       tokens; causal with route_lambda > 0 returns
+                       PISA_E_UNSUPPORTED. */
 } pisa_params;
 
 /* Block statistics ([PISA] precompute; [PIVOT] step 2).  Caller-allocated,
@@ -119,10 +127,12 @@ typedef struct {
  *   vsum  fp32 [B, Hkv, n_blk, d]: sum of the block's value rows
  *   HT    bf16 for bf16 inputs and fp32 for fp32 inputs.  ORDER1:
  *         [B, Hkv, n_blk, d, d], the transposed first-order matrix,
- *         HT[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c).  HYBRID: [B, Hkv, d, d],
- *         the transposed mean of those matrices over the n_blk blocks of the
- *         (b, kv head) (every block, also for causal rows).  Not used by the
- *         other modes.
+ *         HT[e][c] = sum_n v_{n,e} (k_{n,c} - kbar_c).  HYBRID, non-causal:
+ *         [B, Hkv, d, d], the transposed mean of those matrices over the n_blk
+ *         blocks of the (b, kv head).  HYBRID, causal: [B, Hkv, n_blk, d, d],
+ *         entry lo the transposed mean over blocks [0, lo) (entry 0 is zero),
+ *         the matrix of every row whose Taylor candidates are [0, lo).  Not
+ *         used by the other modes.
  *   mcov  fp32 [B, Hkv, n_blk]: ||H_j - Hbar||_F, the covariance norm of block
  *         j against the mean first-order matrix ([PISA] covariance-aware
  *         routing; the pages' norm read as Frobenius), written and read when
@@ -207,8 +217,13 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
  *   O_t = N_t / D_t rounded to nearest-even in dtype;
  *   lse_t = max-shifted ln D_t (fp32 [B, Hq, L]) if lse != NULL.
  * idx may come from pisa_indexer_topk or from the caller (e.g. lists reused
- * from another layer); entries must be ascending, -1 padded, and lie in the
- * row's candidate range. */
+ * from another layer, [HyLRA] section 2.3).  T_r is the set of the row's
+ * entries j with 0 <= j < |cand_r|; every other entry (the -1 padding, a
+ * block of the window range [lo_r, own] or past it, any other value) is
+ * dropped on the device, so no entry reads outside Q, K, V or the statistics.
+ * Block rows (group == 0) accept the entries in any order and repeated.
+ * PIVOT rows (group >= 1) need the kept entries in ascending order (repeats
+ * and dropped entries may sit anywhere); pisa_indexer_topk writes them so. */
 pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void *K,
                                  const void *V, const pisa_stats *stats, const int32_t *idx,
                                  void *O, float *lse, void *ws, size_t ws_bytes,
@@ -225,9 +240,11 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
  *   K, V   dtype [B, Hkv, L, d], the cache (ring == 0), or
  *          dtype [B, Hkv, ring, d], a ring buffer with token i in slot i mod ring
  *   stats  block statistics of the cache (pisa_block_stats over it); only
- *          blocks before the row's window range are read: qsel is not used
- *   idx    int32 [B, Hq, topk + sink] kept lists (ascending not required,
- *          -1 padded); entries at or past the window range are ignored
+ *          statistics of blocks before the row's window range are read (for
+ *          HYBRID the entry lo of HT, the mean over [0, lo)), so cache slots
+ *          after pos may hold anything finite: qsel is not used
+ *   idx    int32 [B, Hq, topk + sink] kept lists (any order, repeats allowed);
+ *          entries outside the candidates [0, lo) are ignored
  *   O      dtype [B, Hq, d];  lse  fp32 [B, Hq] or NULL
  * pisa_decode_topk writes the lists of a sensitive layer: the sinks, then
  * the top-min(k, |cand| - c0) of candidates [c0, lo) by q . ksel_j

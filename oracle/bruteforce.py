@@ -11,12 +11,14 @@ with exact terms over selected blocks and, for non-selected blocks,
 alpha_{t,j} = exp(q_t . kbar_j) times the block value sum plus the first-order
 term, alpha * n_j in the denominator; the hybrid order's global first-order
 correction q_t Hbar sum_j alpha_{t,j} with Hbar the mean of the per-block
-matrices over all blocks); the PIVOT page's steps 1-4 (proxy =
+matrices over all blocks, or, on a causal row, over the blocks it may see as
+Taylor candidates, [0, lo)); the PIVOT page's steps 1-4 (proxy =
 mean of g consecutive queries, candidates re-ranked per member); the Sliding
 Window Attention page's causal mask 0 <= t - s < w, and its attention sinks
 (the first blocks of the sequence kept beside the window; the top-k is chosen
 among the other candidates); covariance-aware routing adds route_lambda times
-the Frobenius norm of H_j - Hbar to every selection score.
+the Frobenius norm of H_j - Hbar to every selection score (non-causal rows
+only: a causal problem with routing is refused).
 """
 from __future__ import annotations
 
@@ -60,6 +62,8 @@ def run(q, k, v, P):
     P: an object with the problem fields (B, Hq, Hkv, L, d, dtype, block, topk,
     window, group, n_cand, causal, taylor, sm_scale).  Returns dict with
     'idx' {(b,h,row): sorted kept list}, 'O' {(b,h,t): [d]}, 'lse' {(b,h,t)}."""
+    if P.causal and getattr(P, "route_lambda", 0.0) > 0:
+        raise ValueError("covariance-aware routing is defined for non-causal rows only")
     bs, L, d = P.block, P.L, P.d
     nb = -(-L // bs)
     blocks = [list(range(j * bs, min(L, (j + 1) * bs))) for j in range(nb)]
@@ -155,8 +159,12 @@ def run(q, k, v, P):
                 N = [sum(math.exp(x - m) * vec[e] for x, _, vec in terms) for e in range(d)]
                 if P.taylor == "hybrid" and U:
                     asum = sum(math.exp(sc * sum(qt[c] * kb[j][c] for c in range(d)) - m) for j in U)
+                    if P.causal:     # the mean over the row's candidates [0, lo)
+                        Hr = [[sum(Hm[j][c][e] for j in range(lo)) / lo for e in range(d)] for c in range(d)]
+                    else:
+                        Hr = Hbar
                     for e in range(d):
-                        N[e] += asum * sc * sum(qt[c] * Hbar[c][e] for c in range(d))
+                        N[e] += asum * sc * sum(qt[c] * Hr[c][e] for c in range(d))
                 res_O[(b, h, t)] = [N[e] / D for e in range(d)]
                 res_lse[(b, h, t)] = m + math.log(D)
     return dict(idx=res_idx, O=res_O, lse=res_lse)

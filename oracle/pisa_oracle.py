@@ -37,10 +37,17 @@ The definition implemented (notation of the PISA page):
     with route_lambda = lam > 0 a block's selection score is the attention
     score plus lam * M_j, M_j = ||H_j - Hbar|| (Frobenius; the rule that
     combines the two and the weight are not given on the pages: the sum with
-    a caller's weight is the reading taken), at every selection stage.
+    a caller's weight is the reading taken), at every selection stage.  The
+    pages define M_j against the global statistic of bidirectional (DiT)
+    attention; on causal rows that statistic would carry later tokens, so
+    routing is defined for non-causal rows only (a causal problem with
+    lam > 0 is refused).
   * Hybrid order ([PISA] section 2, the global first-order correction): zero
     order per non-kept block plus scale q_t Hbar sum_{j in U} alpha_{t,j} in
-    N_t, Hbar = the mean of H_j over all blocks of the (batch, KV head).
+    N_t, Hbar = the mean of H_j over all blocks of the (batch, KV head).  On a
+    causal row, "all blocks" is read as all blocks the row may see as Taylor
+    candidates: Hbar_r = the mean of H_j over its candidates [0, lo_r), so no
+    statistic of a later token enters the row.
 Readings of points the pages leave open are listed in the design notes and
 repeated at the functions that take them.
 """
@@ -75,6 +82,11 @@ class Problem:
     scale: float = 0.0       # <= 0 -> 1/sqrt(d)
     sink: int = 0            # leading key blocks always kept (attention sinks)
     route_lambda: float = 0.0  # covariance-aware routing weight (0: attention score only)
+
+    def __post_init__(self):
+        if self.causal and self.route_lambda > 0:
+            raise ValueError("covariance-aware routing is defined for non-causal rows only: its "
+                             "global statistic Hbar would carry later tokens into a causal row")
 
     @property
     def sm_scale(self) -> float:
@@ -174,7 +186,9 @@ def block_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: Problem) -> dict
     (key channel c, value channel e), and Hbar = mean_j H_j over all n_blk
     blocks ([PISA] section 2, the global statistic of the hybrid order; the
     pages average over all blocks, read here as every block of the sequence,
-    each with weight 1 / n_blk, also when the rows are causal).  Per query selection row: qsel =
+    each with weight 1 / n_blk).  Causal problems also get the prefix table
+    Hpre[lo] = mean of H_j over blocks [0, lo) (Hpre[0] = 0), the statistic a
+    causal row with candidates [0, lo) uses.  Per query selection row: qsel =
     RNE_dtype(mean of the rows of query block i), or in PIVOT mode the proxy
     RNE_dtype(mean of queries g*gamma .. g*gamma+g-1) (a last partial group
     averages its actual members)."""
@@ -201,7 +215,12 @@ def block_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, P: Problem) -> dict
     Hbar = H.mean(axis=2)
     # covariance norm of each block against the mean ([PISA] covariance-aware routing)
     M = np.sqrt(((H - Hbar[:, :, None]) ** 2).sum(axis=(-2, -1)))
-    return dict(n=n, kbar=kbar, ksel=ksel, vsum=vsum, H=H, Hbar=Hbar, M=M, qsel=qsel)
+    out = dict(n=n, kbar=kbar, ksel=ksel, vsum=vsum, H=H, Hbar=Hbar, M=M, qsel=qsel)
+    if P.causal:
+        Hpre = np.zeros_like(H)
+        Hpre[:, :, 1:] = np.cumsum(H, axis=2)[:, :, :-1] / np.arange(1, nb)[:, None, None]
+        out["Hpre"] = Hpre
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -348,7 +367,9 @@ def attend_tokens(q, k, v, st, idx, P: Problem, b: int, h: int, tokens) -> tuple
       N_t = sum_E e^{x-m} v_s + sum_U e^{a-m} (sigma_j + [order1] scale q H_j)
             + [hybrid] scale (q Hbar) sum_U e^{a-m}
       o_t = N_t / D_t,  lse_t = m + ln D_t
-    E_t: tokens of kept blocks (s <= t when causal); U_t: Taylor blocks."""
+    E_t: tokens of kept blocks (s <= t when causal); U_t: Taylor blocks.
+    Hbar: over all blocks (non-causal), or over the row's candidates
+    [0, lo) (causal)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     hk = h * P.Hkv // P.Hq
     sc = P.sm_scale
@@ -360,6 +381,7 @@ def attend_tokens(q, k, v, st, idx, P: Problem, b: int, h: int, tokens) -> tuple
         sel = np.nonzero(rows == r)[0]
         tt = tokens[sel]
         kept, U = row_sets(P, idx[b, h, r], int(r))
+        lo = row_geometry(P, int(r))[1]
         keys = np.concatenate([np.arange(j * bs, j * bs + P.block_len(j)) for j in kept]) \
             if kept else np.zeros(0, dtype=np.int64)
         qt = q[b, h, tt]                                   # [n, d]
@@ -377,7 +399,9 @@ def attend_tokens(q, k, v, st, idx, P: Problem, b: int, h: int, tokens) -> tuple
             qH = np.einsum("nc,jce->nje", qt, st["H"][b, hk, Uj])
             N = N + sc * np.einsum("nj,nje->ne", pa, qH)
         if P.taylor == "hybrid" and len(Uj):
-            N = N + sc * (qt @ st["Hbar"][b, hk]) * pa.sum(axis=1)[:, None]
+            # causal rows: the mean over the row's candidate blocks [0, lo)
+            Hb = st["Hpre"][b, hk, lo] if P.causal else st["Hbar"][b, hk]
+            N = N + sc * (qt @ Hb) * pa.sum(axis=1)[:, None]
         out[sel] = N / D[:, None]
         lse[sel] = m + np.log(D)
     return out, lse
@@ -442,7 +466,8 @@ def decode_attend(q, k, v, st, idx, P: Problem, pos: int) -> tuple:
     layer).  PISA page, section 2: exact terms over the kept blocks and the
     window range [lo, own] (keys s <= pos), Taylor terms for the other
     candidates [0, lo): alpha = e^{scale q . kbar_j} times (sigma_j + [order1]
-    scale q H_j) in N and alpha n_j in D, [hybrid] + scale (q Hbar) sum alpha."""
+    scale q H_j) in N and alpha n_j in D, [hybrid] + scale (q Hbar_lo) sum
+    alpha with Hbar_lo the mean of H_j over the candidates [0, lo)."""
     B, Hq, d = q.shape
     sc, bs = P.sm_scale, P.block
     own, lo, nc = decode_geometry(P, pos)
@@ -468,7 +493,7 @@ def decode_attend(q, k, v, st, idx, P: Problem, pos: int) -> tuple:
                 if P.taylor == "order1":
                     N = N + sc * pa @ np.einsum("c,jce->je", qv, st["H"][b, hk, U])
                 if P.taylor == "hybrid":
-                    N = N + sc * pa.sum() * (qv @ st["Hbar"][b, hk])
+                    N = N + sc * pa.sum() * (qv @ st["Hpre"][b, hk, lo])
             O[b, h] = N / D
             lse[b, h] = m + math.log(D)
     return O, lse

@@ -117,24 +117,38 @@ PISA_DEV u32x4_t frag_st(const uint8_t *base, int e, int ch) {
   return *reinterpret_cast<const u32x4_t *>(base + e * 64 + (phys << 4));
 }
 
-// Kept-list cursor of one PIVOT row (the head is fetched one match ahead).
+// Kept-list cursor of one PIVOT row, for walks that visit blocks in
+// ascending order: the head is the next list entry that is a candidate of
+// the row (0 <= j < nc; other entries are skipped), entries below the block
+// asked for are passed over, and past the end the head is INT_MAX.
 struct Cursor {
   const int32_t *p;
   int left;
+  int nc;
   int head;
 };
-PISA_DEV void cursor_init(Cursor &c, const int32_t *list, int n) {
+PISA_DEV void cursor_next(Cursor &c) {
+  c.head = 0x7FFFFFFF;
+  while (c.left > 0) {
+    const int v = *c.p;
+    ++c.p;
+    --c.left;
+    if (pisa_list_entry_kept(v, c.nc)) {
+      c.head = v;
+      break;
+    }
+  }
+}
+PISA_DEV void cursor_init(Cursor &c, const int32_t *list, int n, int nc) {
   c.p = list;
   c.left = n;
-  const int v = n > 0 ? list[0] : -1;
-  c.head = v < 0 ? 0x7FFFFFFF : v;
+  c.nc = nc;
+  cursor_next(c);
 }
 PISA_DEV bool cursor_match(Cursor &c, int j) {
+  while (c.head < j) cursor_next(c);
   if (c.head != j) return false;
-  ++c.p;
-  --c.left;
-  const int v = c.left > 0 ? *c.p : -1;
-  c.head = v < 0 ? 0x7FFFFFFF : v;
+  cursor_next(c);
   return true;
 }
 
@@ -205,9 +219,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
   for (int n = 0; n < NQ; ++n) {
     const bool leader = valid[n] && (pivot ? hl == 0 : (l == 0 && n == 0));
     if (!leader) continue;
+    // list entries that are not candidates of the row are dropped
     for (int i = 0; i < topk; ++i) {
       const int j = list[n][i];
-      if (j < 0) break;
+      if (!pisa_list_entry_kept(j, nc[n])) continue;
       atomicOr(&exb[j >> 5], 1u << (j & 31));
       if (!pivot) tbits[j >> 5] |= 1u << (j & 31);
     }
@@ -216,11 +231,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
       int ptr = 0;
       for (int wd = 0; wd * 32 < nc[n]; ++wd) {
         uint32_t bits = (nc[n] - wd * 32 >= 32) ? 0xFFFFFFFFu : ((1u << (nc[n] - wd * 32)) - 1u);
-        while (ptr < topk) {
+        for (ptr = 0; ptr < topk; ++ptr) {   // the row's kept candidates in this word
           const int j = list[n][ptr];
-          if (j < 0 || j >= (wd + 1) * 32) break;
-          bits &= ~(1u << (j & 31));
-          ++ptr;
+          if (j >= wd * 32 && j < (wd + 1) * 32 && j < nc[n]) bits &= ~(1u << (j & 31));
         }
         if (bits) atomicOr(&tyb[wd], bits);
       }
@@ -287,7 +300,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
     if (n_st > 1) issue(1);
     Cursor cur[NQ];
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) cursor_init(cur[n], list[n], valid[n] && pivot ? topk : 0);
+    for (int n = 0; n < NQ; ++n) cursor_init(cur[n], list[n], valid[n] && pivot ? topk : 0, nc[n]);
     bool mem[NQ];
     bool active = false;
 #pragma unroll
@@ -423,13 +436,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
     for (int n = 0; n < NQ; ++n) a_run[n] = 0.f;
     Cursor cur[NQ];
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) cursor_init(cur[n], list[n], valid[n] && pivot ? topk : 0);
+    for (int n = 0; n < NQ; ++n) cursor_init(cur[n], list[n], valid[n] && pivot ? topk : 0, nc[n]);
     uint32_t tmask[NQ];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) tmask[n] = 0;
     if (order1) dma_tile<D, D, 0, NW>(HTh + (size_t)tyl[0] * D * D, D, lds + LY::TY_H, w, l);
-    else if (hybrid)   // the mean matrix Hbar^T of this kv head
-      dma_tile<D, D, 0, NW>(static_cast<const uint16_t *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D, D,
+    else if (hybrid && !causal)   // the mean matrix Hbar^T of this kv head
+      dma_tile<D, D, 0, NW>(static_cast<const uint16_t *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, 0), D,
                             lds + LY::TY_H, w, l);
     for (int eg = 0; eg < n_ty; ++eg) {
       const int e = eg & (kTyBatch - 1);
@@ -612,7 +625,35 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
         }
       }
     }
-    if (hybrid) {   // O^T += Hbar^T (scale * sum alpha) q^T, once per row
+    if (hybrid && causal) {
+      // O^T += Hbar(lo)^T (scale * sum alpha) q^T, once per row, Hbar(lo) the
+      // mean over the row's candidates [0, lo): one pass per distinct lo
+      // among the wave's rows (rows of other lo take a zero weight), the
+      // A fragments read straight from memory
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        const float al = a_run[n] * dm.scale;
+        uint64_t pend = ballot64(valid[n] && al != 0.f);
+        while (pend) {
+          const int l0 = __builtin_amdgcn_readlane(lo[n], (int)__builtin_ctzll(pend));
+          const float aln = (valid[n] && lo[n] == l0) ? al : 0.f;
+          const uint16_t *hg = static_cast<const uint16_t *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, l0);
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4_t bq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bq[i] = pack_bf16x2(bf16lo(qf[n][ks][i]) * aln, bf16hi(qf[n][ks][i]) * aln);
+            u32x4_t hf[NE];
+#pragma unroll
+            for (int et = 0; et < NE; ++et)
+              hf[et] = *reinterpret_cast<const u32x4_t *>(hg + (size_t)(et * 32 + lq) * D + (2 * ks + hl) * 8);
+#pragma unroll
+            for (int et = 0; et < NE; ++et) oacc[n][et] = mfma32(hf[et], bq, oacc[n][et]);
+          }
+          pend &= ~ballot64(lo[n] == l0);
+        }
+      }
+    } else if (hybrid) {   // O^T += Hbar^T (scale * sum alpha) q^T, once per row
       wait_vmcnt<0>();
       __syncthreads();
       const uint8_t *hlp = lds + LY::TY_H;

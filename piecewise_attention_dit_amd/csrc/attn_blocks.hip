@@ -70,6 +70,7 @@ struct Cfg {
   static constexpr int GE = D == 64 ? 4 : 2;
   static constexpr int RINGH = D == 64 ? 12 : 4;
   static constexpr int AHEAD = RINGH / GE - 1;                // groups in flight ahead
+  static_assert(RINGH >= P, "causal hybrid rows stage one mean matrix per block row");
   // the next batch's rows are staged at group SG, its tables built in group
   // SG + 1 and published by the barrier of group SG + 2, inside the batch
   static constexpr int SG = (kNB / 2) / GE < kNB / GE - 3 ? (kNB / 2) / GE : kNB / GE - 3;
@@ -173,15 +174,19 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
   for (int i = tid; i < P * 32; i += NT) kbm[i] = 0;
   __syncthreads();
   if (rg == 0 && l == 0) {
+    // the kept set is the set of list entries that are candidates of the
+    // row, 0 <= j < nc: other entries (padding, blocks of the window range or
+    // past it, garbage in a caller's list) are dropped, and the list is
+    // rebuilt ascending from the bitmap, so order and repeats do not matter
     int c = 0;
     if (pvalid && a.idx && dm.topk > 0) {
       const int32_t *row = a.idx + ((size_t)(b * dm.Hq + h) * dm.n_rows + iblk) * dm.topk;
       for (int k = 0; k < dm.topk; ++k) {
         const int j = row[k];
-        if (j < 0) break;
-        lst[part * kMaxK + c++] = (uint16_t)j;
-        kbm[part * 32 + (j >> 5)] |= 1u << (j & 31);
+        if (pisa_list_entry_kept(j, nc)) kbm[part * 32 + (j >> 5)] |= 1u << (j & 31);
       }
+      for (int wd = 0; wd * 32 < nc; ++wd)
+        for (uint32_t m = kbm[part * 32 + wd]; m; m &= m - 1) lst[part * kMaxK + c++] = (uint16_t)(wd * 32 + __ffs(m) - 1);
     }
     cnt[8 + part] = c;
   }
@@ -548,8 +553,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     stage(0);
     if (order1) {
       for (int i = 0; i < C::AHEAD * C::GE && i < n_ty; ++i) dma_h(i);
-    } else if (hybrid && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
-      const uint16_t *src = static_cast<const uint16_t *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
+    } else if (hybrid && !causal && issuer) {   // the mean matrix Hbar^T of this kv head, into ring slot 0
+      const uint16_t *src = static_cast<const uint16_t *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, 0);
 #pragma unroll
       for (int u = 0; u < PH; ++u) dma16_buf(src, D * D * 2, offh[u], lds + C::TY_H + (w + NDW * u) * 1024);
     }
@@ -755,7 +760,24 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     if (hybrid) {   // O^T += (scale sum alpha) Hbar^T Q^T, once per row
       wait_vmcnt<0>();
       __syncthreads();
-      const uint8_t *hp = lds + C::TY_H;
+      if (causal) {
+        // causal rows: the mean over each block row's candidates [0, lo),
+        // the TB block rows' matrices into ring slots 0 .. TB - 1
+        if (issuer) {
+          for (int p = 0; p < TB; ++p) {
+            const int ip = tile * TB + p;
+            int o2, l2 = 0;
+            if (ip < dm.n_blk) pisa_row_geometry(dm, ip * BS, &o2, &l2);
+            const uint16_t *src = static_cast<const uint16_t *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, l2);
+#pragma unroll
+            for (int u = 0; u < PH; ++u)
+              dma16_buf(src, D * D * 2, offh[u], lds + C::TY_H + p * C::HT + (w + NDW * u) * 1024);
+          }
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+      const uint8_t *hp = lds + C::TY_H + (causal ? (part % TB) * C::HT : 0);
       const float al = a_run * dm.scale;
 #pragma unroll
       for (int et = 0; et < NE; ++et) {

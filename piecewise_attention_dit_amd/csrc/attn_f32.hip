@@ -45,12 +45,23 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     float m = kNegInf, dsum = 0.f, asum = 0.f, o[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) o[i] = 0.f;
+    // a list entry counts once, and only if it is a candidate of the row
+    // (0 <= j < nc): padding, blocks of the window range or past it and
+    // repeats are skipped
+    auto kept_entry = [&](int i) -> bool {
+      const int j = list[i];
+      if (!pisa_list_entry_kept(j, nc)) return false;
+      for (int i2 = 0; i2 < i; ++i2)
+        if (list[i2] == j) return false;
+      return true;
+    };
     // exact blocks: the kept list, then the window range [lo, own] (causal)
     int li = 0;
     bool range_done = !causal;
     for (;;) {
       int jlo, jhi;
-      if (li < dm.topk && list[li] >= 0) {
+      while (li < dm.topk && !kept_entry(li)) ++li;
+      if (li < dm.topk) {
         jlo = jhi = list[li++];
       } else if (!range_done) {
         jlo = lo;
@@ -95,10 +106,10 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     }
     // Taylor blocks: candidates [0, nc) not in the kept list
     if (dm.taylor) {
-      int ptr = 0;
       for (int j = 0; j < nc; ++j) {
-        while (ptr < dm.topk && list[ptr] >= 0 && list[ptr] < j) ++ptr;
-        if (ptr < dm.topk && list[ptr] == j) continue;
+        bool kept = false;
+        for (int i = 0; i < dm.topk; ++i) kept |= list[i] == j;
+        if (kept) continue;
         const float *kb = a.kbar + soff + (size_t)j * D;
         float part = 0.f;
         for (int c = l; c < D; c += 64) part = fmaf(qs[w][c], kb[c], part);
@@ -127,7 +138,8 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
         }
       }
       if (dm.taylor == 3 && asum > 0.f) {   // hybrid: + (scale sum alpha) q Hbar
-        const float *Hb = static_cast<const float *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
+        // non-causal: the mean over all blocks; causal: over the row's candidates [0, lo)
+        const float *Hb = static_cast<const float *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, lo);
 #pragma unroll
         for (int i = 0; i < NE; ++i) {
           const int e = l + 64 * i;

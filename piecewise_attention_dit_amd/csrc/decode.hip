@@ -18,8 +18,8 @@
 // workers (S workgroups of four waves); a worker keeps each head's
 // online-softmax state and writes its partials (m, l, A, o[d]) to the
 // workspace, and decode_combine merges the partials of a row in worker order
-// (deterministic), adding the hybrid order's (scale sum alpha) q Hbar once
-// per row.
+// (deterministic), adding the hybrid order's (scale sum alpha) q Hbar(lo)
+// once per row, Hbar(lo) the mean over the candidates [0, lo).
 #include <mutex>
 
 #include "device_common.h"
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial(DecArgs a) {
     for (int i = tid; i < R * dm.topk; i += kDecWaves * 64) {
       const int r = i / dm.topk;
       const int j = a.idx[(size_t)(row0 + r) * dm.topk + i % dm.topk];
-      if (j >= 0 && j < lo) {
+      if (pisa_list_entry_kept(j, lo)) {   // candidates [0, lo) only
         atomicOr(&kbits[r][j >> 5], 1u << (j & 31));
         atomicOr(&ubits[j >> 5], 1u << (j & 31));
       }
@@ -501,7 +501,11 @@ __global__ __launch_bounds__(64) void decode_combine(DecArgs a, void *O, float *
     const T *Q = static_cast<const T *>(a.q) + (size_t)row * D;
     for (int c = l; c < D; c += 64) qs[c] = ld(Q + c);
     __syncthreads();
-    const T *Hb = static_cast<const T *>(a.HT) + (size_t)(b * dm.Hkv + hk) * D * D;
+    // the mean over the token's candidates [0, lo): statistics of complete
+    // blocks before the window range only
+    int own, lo;
+    pisa_row_geometry(dm, a.pos, &own, &lo);
+    const T *Hb = static_cast<const T *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, lo);
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
       o[e] = fmaf(dm.scale * A, dot_row<T, D>(qs, Hb + (size_t)(EPL * l + e) * D), o[e]);

@@ -69,6 +69,10 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
     return fail(PISA_E_ARG, "route_lambda must be finite and >= 0");
   if (p->route_lambda > 0.f && p->taylor == PISA_TAYLOR_NONE)
     return fail(PISA_E_ARG, "covariance routing decides which blocks go to the Taylor term: taylor is NONE");
+  if (p->route_lambda > 0.f && p->causal)
+    return fail(PISA_E_UNSUPPORTED,
+                "covariance routing is defined for non-causal rows only (its mean first-order matrix "
+                "would carry later tokens into a causal row)");
   if (!p->causal && p->topk == 0 && p->sink == 0 && p->taylor == PISA_TAYLOR_NONE)
     return fail(PISA_E_ARG, "non-causal with topk = 0, no sinks and no Taylor term attends to nothing");
   const long long n_blk = (p->L + (long long)p->block - 1) / p->block;
@@ -145,9 +149,10 @@ pisa_status pisa_stats_layout(const pisa_params *p, size_t bytes[6]) {
   bytes[1] = kv * dm.d * es;
   bytes[2] = kv * dm.d * sizeof(float);
   bytes[3] = kv * dm.d * sizeof(float);
-  bytes[4] = dm.taylor == PISA_TAYLOR_ORDER1   ? kv * dm.d * dm.d * es
-             : dm.taylor == PISA_TAYLOR_HYBRID ? (size_t)dm.B * dm.Hkv * dm.d * dm.d * es
-                                               : 0;
+  bytes[4] = dm.taylor == PISA_TAYLOR_ORDER1 ? kv * dm.d * dm.d * es
+             : dm.taylor == PISA_TAYLOR_HYBRID
+                 ? (dm.causal ? kv : (size_t)dm.B * dm.Hkv) * dm.d * dm.d * es   // causal: one per lo
+                 : 0;
   bytes[5] = dm.route_lambda > 0.f ? kv * sizeof(float) : 0;
   return PISA_OK;
 }

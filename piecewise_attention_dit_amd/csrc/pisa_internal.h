@@ -52,10 +52,23 @@ inline int pisa_row_geometry(const PisaDims &dm, int start_token, int *own, int 
   return l;
 }
 
+// Whether entry j of a kept list counts for a selection row with nc
+// candidate blocks (pisa_row_geometry's return value): only candidates of the
+// row, 0 <= j < nc.  The -1 padding, blocks of the row's exact window range
+// [lo, own] or later ones, and any other value a caller's list (reused from
+// another layer) may hold are dropped, so no kernel indexes with them.
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline bool pisa_list_entry_kept(int j, int nc) { return j >= 0 && j < nc; }
+
 // The mean first-order matrix Hbar (hybrid order, covariance routing).  bf16:
 // summed over runs of kHbarRun consecutive blocks into an fp32 workspace
-// [B, Hkv, runs, d, d], then the runs are added in order.  Routing also keeps
-// an fp32 copy of Hbar^T [B, Hkv, d, d] after the run sums.
+// [B, Hkv, runs, d, d], then the runs are added in order.  Causal rows use
+// the prefix means Hbar(lo) over blocks [0, lo) instead, one per lo: the run
+// sums are turned into exclusive prefix sums in place, and a second pass over
+// the runs writes the mean before each of its blocks.  Routing also keeps an
+// fp32 copy of Hbar^T [B, Hkv, d, d] after the run sums.
 constexpr int kHbarRun = 16;
 inline bool needs_hbar(const PisaDims &dm) { return dm.taylor == 3 || dm.route_lambda > 0.f; }
 inline size_t hbar_runs_bytes(const PisaDims &dm) {
@@ -66,6 +79,16 @@ inline size_t hbar_runs_bytes(const PisaDims &dm) {
 inline size_t stats_workspace_bytes(const PisaDims &dm) {
   const size_t hb32 = dm.route_lambda > 0.f ? (size_t)dm.B * dm.Hkv * dm.d * dm.d * sizeof(float) : 0;
   return hbar_runs_bytes(dm) + hb32;
+}
+// Element offset of the Hbar^T matrix a selection row with window start lo
+// uses: the one matrix of the (b, kv head) for non-causal rows, the prefix
+// mean over [0, lo) for causal rows.
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline size_t hbar_offset(const PisaDims &dm, int bk, int lo) {
+  const size_t dd = (size_t)dm.d * dm.d;
+  return dm.causal ? ((size_t)bk * dm.n_blk + (size_t)lo) * dd : (size_t)bk * dd;
 }
 
 // launchers (return the hipError_t of the launch)

@@ -8,7 +8,8 @@
 //   q_pool       one thread per (selection row, 16-byte column chunk):
 //                qsel = RNE_dtype(mean of the row's queries)
 //   hbar_*       hybrid order: HbarT = transposed mean of H_j over all blocks
-//                of a (b, kv head) (the global first-order statistic)
+//                of a (b, kv head) (the global first-order statistic); for
+//                causal rows one mean per lo, over the blocks [0, lo)
 //
 // The means are float64 cascaded sums divided once (IEEE division) and rounded
 // once into the dtype.  HBM-bound: Q, K and V are read exactly once.
@@ -320,6 +321,13 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_f32(PisaDims dm, const
 //               of at most 128 terms) and add H_j^T = R_j^T - sigma_j kbar_j^T
 //               to the run's fp32 sum in the workspace;
 //   hbar_final  one thread per (b, kv head, e, c): the runs in order, / n_blk.
+// Causal rows (the mean over a row's Taylor candidates [0, lo), one matrix
+// per lo):
+//   hbar_run    as above, the run sums;
+//   hbar_scan   one thread per (b, kv head, e, c): the run sums become
+//               exclusive prefix sums over the runs, in place;
+//   hbar_run    PREFIX: each run starts from its prefix sum and writes
+//               sum / j as HbarT(lo = j) before it adds block j (HbarT(0) = 0).
 // The centring follows the exact products, so no rounded centred key enters,
 // and every sum has a fixed order, so the result is deterministic.
 template <int D, int BS>
@@ -332,11 +340,12 @@ struct HbarCfg {
   static_assert(CPW >= 1 && (TILE / 1024) % 4 == 0, "tile must split over four waves");
 };
 
-template <int D, int BS>
+template <int D, int BS, bool PREFIX>
 __global__ __launch_bounds__(256) void hbar_run(PisaDims dm, const uint16_t *__restrict__ K,
                                                 const uint16_t *__restrict__ V,
                                                 const float *__restrict__ kbar,
-                                                const float *__restrict__ vsum, float *__restrict__ ws) {
+                                                const float *__restrict__ vsum, float *__restrict__ ws,
+                                                uint16_t *__restrict__ HbT) {
   using C = HbarCfg<D, BS>;
   constexpr int NE = C::NE, TPW = C::TPW, TILE = C::TILE, CPW = C::CPW;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -378,8 +387,19 @@ __global__ __launch_bounds__(256) void hbar_run(PisaDims dm, const uint16_t *__r
   };
   const int srow = (l & 15) >> 2, ecol = 16 * ((l >> 4) & 1) + 4 * (l & 3);
   f32x16_t tot[TPW];
+  float *runp = ws + ((size_t)bh * nrun + run) * D * D;
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) tot[i] = f32x16_t{};
+  for (int i = 0; i < TPW; ++i) {
+    if (PREFIX) {   // the exclusive prefix sum of the earlier runs
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          tot[i][4 * g + q] = runp[(size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq];
+    } else {
+      tot[i] = f32x16_t{};
+    }
+  }
   float ck[TPW];
   f32x4_t cv[4];
   ldstat(j0, ck, cv);
@@ -392,6 +412,19 @@ __global__ __launch_bounds__(256) void hbar_run(PisaDims dm, const uint16_t *__r
     if (j + 1 < j1) {
       ldstat(j + 1, nk, nv);
       dma(j + 1);
+    }
+    if (PREFIX) {   // HbarT(lo = j): the mean over blocks [0, j)
+      uint16_t *dst = HbT + ((size_t)bh * dm.n_blk + j) * D * D;
+      const float inv = j > 0 ? 1.f / (float)j : 0.f;
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dst[(size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq] =
+                (uint16_t)f32_to_bf16(j > 0 ? tot[i][4 * g + q] * inv : 0.f);
+      if (j + 1 == dm.n_blk) break;   // no row has lo = n_blk
     }
     const uint8_t *kt = lds + ((j - j0) & 1) * 2 * TILE, *vt = kt + TILE;
     f32x16_t r[TPW];
@@ -415,14 +448,29 @@ __global__ __launch_bounds__(256) void hbar_run(PisaDims dm, const uint16_t *__r
 #pragma unroll
     for (int g = 0; g < 4; ++g) cv[g] = nv[g];
   }
-  float *out = ws + ((size_t)bh * nrun + run) * D * D;
+  if (PREFIX) return;
 #pragma unroll
   for (int i = 0; i < TPW; ++i)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        out[(size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq] = tot[i][4 * g + q];
+        runp[(size_t)(et * 32 + 8 * g + 4 * hl + q) * D + (ct0 + i) * 32 + lq] = tot[i][4 * g + q];
+}
+
+// causal rows: the run sums of a (b, kv head) become exclusive prefix sums
+__global__ __launch_bounds__(256) void hbar_scan(PisaDims dm, float *__restrict__ ws) {
+  const int DD = dm.d * dm.d;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)dm.B * dm.Hkv * DD) return;
+  const int nrun = (dm.n_blk + kHbarRun - 1) / kHbarRun;
+  float *p = ws + (size_t)(gid / DD) * nrun * DD + (int)(gid % DD);
+  float s = 0.f;
+  for (int r = 0; r < nrun; ++r) {
+    const float x = p[(size_t)r * DD];
+    p[(size_t)r * DD] = s;
+    s += x;
+  }
 }
 
 // HbT (bf16, hybrid order) and hb32 (fp32 copy, routing): either may be null
@@ -581,12 +629,18 @@ __global__ __launch_bounds__(kStatsThreads) void hbar_f32(PisaDims dm, const flo
   const float *Kb = K + (size_t)bh * dm.L * D, *Vb = V + (size_t)bh * dm.L * D;
   const float *kb = kbar + (size_t)bh * dm.n_blk * D, *vs = vsum + (size_t)bh * dm.n_blk * D;
   float tot = 0.f;
+  const bool prefix = dm.causal != 0;   // one mean per lo, over blocks [0, lo)
   for (int j = 0; j < dm.n_blk; ++j) {
+    if (prefix && HbT) {
+      HbT[((size_t)bh * dm.n_blk + j) * D * D + o] = j > 0 ? tot / (float)j : 0.f;
+      if (j + 1 == dm.n_blk) return;
+    }
     const int t1 = min(dm.L, (j + 1) * BS);
     float r = 0.f;
     for (int t = j * BS; t < t1; ++t) r = fmaf(Vb[(size_t)t * D + e], Kb[(size_t)t * D + c], r);
     tot += r - vs[(size_t)j * D + e] * kb[(size_t)j * D + c];
   }
+  if (prefix) return;
   const float m = tot / (float)dm.n_blk;
   if (HbT) HbT[(size_t)bh * D * D + o] = m;
   if (hb32) hb32[(size_t)bh * D * D + o] = m;
@@ -603,8 +657,11 @@ hipError_t launch_hbar(const PisaDims &dm, const void *K, const void *V, const f
     using C = HbarCfg<D, BS>;
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hbar_run<D, BS>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hbar_run<D, BS, false>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hbar_run<D, BS, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
       if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mcov_bf16<D, BS>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL + 16);
@@ -612,11 +669,21 @@ hipError_t launch_hbar(const PisaDims &dm, const void *K, const void *V, const f
       attr_set = true;
     }
     const int nrun = (dm.n_blk + kHbarRun - 1) / kHbarRun;
-    hbar_run<D, BS><<<(unsigned)dm.B * dm.Hkv * nrun, 256, C::TOTAL, st>>>(
-        dm, static_cast<const uint16_t *>(K), static_cast<const uint16_t *>(V), kbar, vsum,
-        static_cast<float *>(ws));
+    const unsigned rgrid = (unsigned)dm.B * dm.Hkv * nrun;
+    hbar_run<D, BS, false><<<rgrid, 256, C::TOTAL, st>>>(dm, static_cast<const uint16_t *>(K),
+                                                         static_cast<const uint16_t *>(V), kbar, vsum,
+                                                         static_cast<float *>(ws), nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (dm.causal) {   // hybrid order only (routing is non-causal): one mean per lo
+      hbar_scan<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dm, static_cast<float *>(ws));
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hbar_run<D, BS, true><<<rgrid, 256, C::TOTAL, st>>>(dm, static_cast<const uint16_t *>(K),
+                                                          static_cast<const uint16_t *>(V), kbar, vsum,
+                                                          static_cast<float *>(ws), static_cast<uint16_t *>(HT));
+      return hipGetLastError();
+    }
     hbar_final<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dm, static_cast<const float *>(ws),
                                                              hybrid ? static_cast<uint16_t *>(HT) : nullptr, hb32);
     if (route) {

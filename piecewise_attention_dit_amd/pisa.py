@@ -143,8 +143,9 @@ def alloc_stats(p: Params, device="cuda") -> dict:
         st["vsum"] = torch.empty((p.B, p.Hkv, n_blk, p.d), dtype=torch.float32, device=device)
     if p.taylor == TAYLOR["order1"]:
         st["HT"] = torch.empty((p.B, p.Hkv, n_blk, p.d, p.d), dtype=td, device=device)
-    elif p.taylor == TAYLOR["hybrid"]:   # the transposed mean first-order matrix
-        st["HT"] = torch.empty((p.B, p.Hkv, p.d, p.d), dtype=td, device=device)
+    elif p.taylor == TAYLOR["hybrid"]:   # the transposed mean first-order matrix (per lo when causal)
+        shape = (p.B, p.Hkv, n_blk, p.d, p.d) if p.causal else (p.B, p.Hkv, p.d, p.d)
+        st["HT"] = torch.empty(shape, dtype=td, device=device)
     if p.route_lambda > 0:              # covariance norms for routing
         st["mcov"] = torch.empty((p.B, p.Hkv, n_blk), dtype=torch.float32, device=device)
     return st

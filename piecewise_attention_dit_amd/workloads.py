@@ -141,15 +141,24 @@ PARITY_CASES = {
                                                        L=1000, grid=(1, 20, 50), topk=2, sink=1,
                                                        taylor="hybrid"),
     # covariance-aware routing, weights that make both terms of the score count
-    "llm_swa_s_route": WORKLOADS["llm_swa"].replace(name="llm_swa_s_route", B=1, Hq=8, Hkv=2,
-                                                    L=2048 + 24, window=384, topk=4,
-                                                    route_lambda=0.04),
+    # (covariance routing is defined for non-causal rows: the LLM shapes run
+    # bidirectional here)
+    "gqa_s_route": WORKLOADS["llm_swa"].replace(name="gqa_s_route", B=1, Hq=8, Hkv=2,
+                                                L=2048 + 24, window=0, causal=False, topk=4,
+                                                route_lambda=0.04),
     "video_dit_s_route": WORKLOADS["video_dit"].replace(name="video_dit_s_route", Hq=2, Hkv=2,
                                                         L=1000, grid=(1, 20, 50), topk=2,
                                                         taylor="hybrid", route_lambda=0.05),
-    "llm_pivot_s_route": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_route", Hq=8, Hkv=2,
-                                                        L=2048 + 40, topk=6, n_cand=12,
-                                                        taylor="order0", route_lambda=0.016),
+    "pivot_s_route": WORKLOADS["llm_pivot"].replace(name="pivot_s_route", Hq=8, Hkv=2,
+                                                    L=2048 + 40, topk=6, n_cand=12, causal=False,
+                                                    taylor="order0", route_lambda=0.016),
+    # causal hybrid order with a window that spans several blocks per tile
+    "llm_swa_s_hyb_w": WORKLOADS["llm_swa"].replace(name="llm_swa_s_hyb_w", B=1, Hq=8, Hkv=8,
+                                                    L=2048 + 24, window=200, topk=3,
+                                                    taylor="hybrid"),
+    "llm_pivot_s_hyb_w": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_hyb_w", Hq=2, Hkv=2,
+                                                        L=1024 + 40, topk=3, n_cand=6, window=150,
+                                                        taylor="hybrid"),
 }
 
 

@@ -54,12 +54,16 @@ def compare_stats(g: dict, st: dict, P: po.Problem):
         rel = (num / den).max()
         assert rel < TOL[P.dtype]["H"], f"H relative Frobenius error {rel}"
     if P.taylor == "hybrid":
-        Hb = st["Hbar"]                                # [B, Hkv, c, e]
-        HbT = to64(gs["HT"])                           # [B, Hkv, e, c]
+        # non-causal: one mean [B, Hkv, c, e]; causal: one per lo [B, Hkv, n_blk, c, e]
+        Hb = st["Hpre"] if P.causal else st["Hbar"]
+        HbT = to64(gs["HT"])
         num = np.linalg.norm((np.swapaxes(HbT, -1, -2) - Hb).reshape(-1, P.d * P.d), axis=1)
         den = np.linalg.norm(Hb.reshape(-1, P.d * P.d), axis=1) + 1e-30
-        rel = (num / den).max()
+        # the empty prefix (lo = 0) is exactly zero on both sides
+        rel = (num / den)[den > 1e-20].max()
         assert rel < TOL[P.dtype]["H"], f"Hbar relative Frobenius error {rel}"
+        if P.causal:
+            assert not HbT[:, :, 0].any(), "Hbar(lo = 0) must be zero"
     if P.route_lambda > 0:
         err = np.abs(to64(gs["mcov"]) - st["M"])
         tol = MCOV_REL * st["M"].max(axis=-1, keepdims=True) + 1e-30

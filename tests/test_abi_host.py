@@ -61,6 +61,8 @@ def _p(**kw):
     (dict(route_lambda=-1.0), pisa.PISA_E_ARG),
     (dict(route_lambda=float("nan")), pisa.PISA_E_ARG),
     (dict(route_lambda=0.5, taylor="none"), pisa.PISA_E_ARG),
+    (dict(route_lambda=0.5, causal=True), pisa.PISA_E_UNSUPPORTED),      # routing is non-causal only
+    (dict(route_lambda=0.5, causal=True, group=8, n_cand=8), pisa.PISA_E_UNSUPPORTED),
     (dict(topk=40, sink=25), pisa.PISA_E_UNSUPPORTED),
     (dict(topk=-1), pisa.PISA_E_ARG),
     (dict(topk=65), pisa.PISA_E_UNSUPPORTED),
@@ -96,6 +98,10 @@ def test_layouts():
     # the hybrid order, none otherwise
     h = _p(L=1000, group=0, taylor="hybrid")
     assert pisa.stats_layout(h)[4] == 2 * 128 * 128 * 2
+    # causal rows: one mean per lo (the prefix over the row's candidates)
+    hc = _p(L=1000, group=0, taylor="hybrid", causal=True, window=200)
+    assert pisa.stats_layout(hc)[4] == 2 * n_blk * 128 * 128 * 2
+    assert pisa.workspace_size(hc, 0) == pisa.workspace_size(h, 0)
     assert pisa.stats_layout(h)[2:4] == sizes[2:4]
     for mode in ("none", "order0"):
         assert pisa.stats_layout(_p(L=1000, group=0, taylor=mode, topk=2))[4] == 0

@@ -6,7 +6,11 @@ recomputes what it can afford:
 * for sampled (batch, query head) pairs, everything of that head: pooled
   selection vectors, block statistics and every selection row;
 * the outputs of sampled tokens of that head: the first and last tokens, block
-  boundaries, the ragged tail and seeded random tokens.
+  boundaries, the ragged tail and seeded random tokens;
+* the outputs of whole query blocks of that head, every row of them: the
+  first block, the last (ragged where L is not a multiple of the block) and
+  two seeded blocks in between (each row of them takes its Taylor terms in
+  several batches of the kernel), with the mean-abs bar over those rows.
 Bar: selections and pooled vectors bit-exact; outputs within max-abs 2e-2 /
 mean-abs 2e-3 (bf16) or 1e-4 (fp32); lse within 1e-2 / 1e-5.
 """
@@ -27,6 +31,12 @@ def _heads(wl):
     if wl.Hq > 2:
         hs.append((wl.B // 2, wl.Hq // 2 + 1))
     return sorted(set(hs))
+
+
+def _blocks(wl, rng):
+    n_blk = -(-wl.L // wl.block)
+    mid = rng.choice(np.arange(1, n_blk - 1), size=2, replace=False)
+    return sorted({0, n_blk - 1, *(int(x) for x in mid)})
 
 
 def _tokens(wl, rng, n_random=12):
@@ -99,3 +109,16 @@ def test_fullsize(name):
         assert d.max() <= tol["max_abs"], f"max abs error {d.max()}"
         assert d.mean() <= tol["mean_abs"], f"mean abs error {d.mean()}"
         assert np.abs(l_gpu - l_ref).max() <= tol["lse"], f"lse error {np.abs(l_gpu - l_ref).max()}"
+        # whole query blocks, every row
+        for i in _blocks(wl, rng):
+            toks = np.arange(i * wl.block, min(wl.L, (i + 1) * wl.block))
+            o_ref, l_ref = po.attend_tokens(qa, ka, va, ref, r_idx, P1, 0, 0, toks)
+            o_gpu = out[b, h, toks].cpu().double().numpy()
+            l_gpu = lse[b, h, toks].cpu().double().numpy()
+            assert np.isfinite(o_gpu).all()
+            d = np.abs(o_gpu - o_ref)
+            print(f"[fullsize] {name} b={b} h={h} query block {i} ({len(toks)} rows): "
+                  f"max_abs={d.max():.3e} mean_abs={d.mean():.3e}", flush=True)
+            assert d.max() <= tol["max_abs"], f"block {i}: max abs error {d.max()}"
+            assert d.mean() <= tol["mean_abs"], f"block {i}: mean abs error {d.mean()}"
+            assert np.abs(l_gpu - l_ref).max() <= tol["lse"], f"block {i}: lse error"

@@ -143,7 +143,7 @@ def check_hybrid(m):
     output averaged over cyclic relabelings of the blocks' H."""
     B, H, L, d, bs = 1, 2, 70, 8, 10
     q, k, v = _rand((B, H, L, d), 16), _rand((B, H, L, d), 17, scale=2.0) + 1.0, _rand((B, H, L, d), 18)
-    kw = dict(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=bs, topk=2, causal=True, window=15)
+    kw = dict(B=B, Hq=H, Hkv=H, L=L, d=d, dtype="f32", block=bs, topk=2, causal=False)
     Ph, P1 = m.Problem(taylor="hybrid", **kw), m.Problem(taylor="order1", **kw)
     st = m.block_stats(q, k, v, Ph)
     raw = np.einsum("bhsc,bhse->bhce", k, v) - np.einsum("bhjc,bhje->bhce", st["kbar"], st["vsum"])
@@ -196,6 +196,36 @@ def check_routing(m):
     return ok
 
 
+def check_causal(m):
+    """Editing keys and values after position c changes nothing at or before c
+    (outputs, lse, selection rows, decode), in the hybrid and first orders, for
+    block rows and PIVOT rows; a causal problem with routing is refused."""
+    B, Hq, Hkv, L, d, bs = 1, 2, 1, 64, 6, 8
+    q, k, v = _rand((B, Hq, L, d), 26, "bf16"), _rand((B, Hkv, L, d), 27, "bf16"), _rand((B, Hkv, L, d), 28, "bf16")
+    c = 37
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, c + 1:] = _rand(k2[:, :, c + 1:].shape, 29, "bf16", 3.0) + 1.0
+    v2[:, :, c + 1:] = _rand(v2[:, :, c + 1:].shape, 30, "bf16", 3.0) - 1.0
+    ok = True
+    for taylor, extra in (("hybrid", dict(window=12)), ("hybrid", dict(group=2, n_cand=3)),
+                          ("order1", dict(window=12))):
+        P = m.Problem(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=bs, topk=1, causal=True, taylor=taylor, **extra)
+        r, r2 = m.run(q, k, v, P), m.run(q, k2, v2, P)
+        ok &= np.abs(r["O"][:, :, :c + 1] - r2["O"][:, :, :c + 1]).max() < 1e-13
+        ok &= np.abs(r["lse"][:, :, :c + 1] - r2["lse"][:, :, :c + 1]).max() < 1e-13
+        for pos in (c, 20):
+            i1 = m.decode_select(q[:, :, pos], r["stats"], P, pos)
+            o1, _ = m.decode_attend(q[:, :, pos], k, v, r["stats"], i1, P, pos)
+            o2, _ = m.decode_attend(q[:, :, pos], k2, v2, r2["stats"], i1, P, pos)
+            ok &= np.abs(o1 - o2).max() < 1e-13
+    try:
+        m.Problem(B=1, Hq=1, Hkv=1, L=16, d=4, block=4, topk=1, causal=True, route_lambda=0.5)
+        ok = False
+    except ValueError:
+        pass
+    return ok
+
+
 def check_decode(m):
     """The decode step equals the prefill's causal token row at the same position."""
     B, Hq, Hkv, L, d, bs = 1, 2, 1, 40, 6, 8
@@ -213,7 +243,8 @@ def check_decode(m):
 
 
 CHECKS = [check_pivot_mean, check_swa_count, check_dense, check_constant_v, check_orders, check_ties,
-          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks, check_routing, check_decode]
+          check_pivot_reuse, check_pooled_selection, check_hybrid, check_sinks, check_routing, check_decode,
+          check_causal]
 
 MUTATIONS = {
     "H transposed": ('H[:, :, j] = np.einsum("bhnc,bhne->bhce", kc, vj)',
@@ -236,9 +267,14 @@ MUTATIONS = {
     "pivot members ignore proxy list": ("tt = top_n(q[b, h, t], Kb[cl], cl, k, bias[cl])",
                                         "tt = top_n(q[b, h, t], Kb[:nc], np.arange(nc), k, bias[:nc])"),
     "hybrid Hbar is the sum": ("Hbar = H.mean(axis=2)", "Hbar = H.sum(axis=2)"),
-    "hybrid Hbar over the tail only": ('(qt @ st["Hbar"][b, hk])', '(qt @ st["H"][b, hk, Uj].mean(axis=0))'),
-    "hybrid Hbar transposed": ('(qt @ st["Hbar"][b, hk])', '(qt @ st["Hbar"][b, hk].T)'),
-    "hybrid term without scale": ('N = N + sc * (qt @ st["Hbar"]', 'N = N + 1.0 * (qt @ st["Hbar"]'),
+    "hybrid Hbar over the tail only": ('(qt @ Hb)', '(qt @ st["H"][b, hk, Uj].mean(axis=0))'),
+    "hybrid Hbar transposed": ('(qt @ Hb)', '(qt @ Hb.T)'),
+    "hybrid term without scale": ('N = N + sc * (qt @ Hb)', 'N = N + 1.0 * (qt @ Hb)'),
+    "hybrid causal Hbar over all blocks": ('Hb = st["Hpre"][b, hk, lo] if P.causal else st["Hbar"][b, hk]',
+                                           'Hb = st["Hbar"][b, hk]'),
+    "hybrid causal prefix takes block lo": ("Hpre[:, :, 1:] = np.cumsum(H, axis=2)[:, :, :-1] / np.arange(1, nb)[:, None, None]",
+                                            "Hpre[:, :, 1:] = np.cumsum(H, axis=2)[:, :, 1:] / np.arange(2, nb + 1)[:, None, None]"),
+    "routing allowed on causal rows": ("if self.causal and self.route_lambda > 0:", "if False:"),
     "hybrid weights include exact terms": ('* pa.sum(axis=1)[:, None]',
                                            '* (pa.sum(axis=1) + px.sum(axis=1))[:, None]'),
     "sinks take top-k places": ("t = top_n(qsel[b, h, r], Kb[c0:nc], np.arange(c0, nc), k, bias[c0:nc])",
@@ -251,8 +287,10 @@ MUTATIONS = {
     "routing skipped for members": ("tt = top_n(q[b, h, t], Kb[cl], cl, k, bias[cl])",
                                     "tt = top_n(q[b, h, t], Kb[cl], cl, k)"),
     "decode reads keys past the token": ("np.arange(j * bs, min((j + 1) * bs, pos + 1))", "np.arange(j * bs, (j + 1) * bs)"),
-    "decode hybrid term without scale": ("N = N + sc * pa.sum() * (qv @ st[\"Hbar\"][b, hk])",
-                                         "N = N + pa.sum() * (qv @ st[\"Hbar\"][b, hk])"),
+    "decode hybrid term without scale": ('N = N + sc * pa.sum() * (qv @ st["Hpre"][b, hk, lo])',
+                                         'N = N + pa.sum() * (qv @ st["Hpre"][b, hk, lo])'),
+    "decode hybrid Hbar over all blocks": ('N = N + sc * pa.sum() * (qv @ st["Hpre"][b, hk, lo])',
+                                           'N = N + sc * pa.sum() * (qv @ st["Hbar"][b, hk])'),
     "decode window not widened": ("lo = (max(0, pos - P.window + 1) // P.block) if P.window > 0 else own\n    return own, lo, lo",
                                   "lo = (max(0, pos - P.window + 1 + P.block - 1) // P.block) if P.window > 0 else own\n    return own, min(lo, own), min(lo, own)"),
     "scale not applied to exact logits": ("x = sc * (qt @ k[b, hk, keys].T)", "x = (qt @ k[b, hk, keys].T)"),

@@ -327,8 +327,10 @@ BRUTE_CASES = [
          taylor="order0", dtype="bf16"),
     dict(Hq=2, Hkv=1, L=40, block=4, topk=2, causal=False, route_lambda=0.05, taylor="order1",
          dtype="f32"),
-    dict(Hq=2, Hkv=1, L=44, block=4, topk=2, group=2, n_cand=4, causal=True, window=5,
+    dict(Hq=2, Hkv=1, L=44, block=4, topk=2, group=2, n_cand=4, causal=False,
          route_lambda=0.02, taylor="hybrid", dtype="bf16"),
+    dict(Hq=2, Hkv=1, L=52, block=4, topk=1, group=2, n_cand=3, causal=True, window=7,
+         taylor="hybrid", dtype="bf16"),
 ]
 
 
@@ -414,8 +416,11 @@ def test_p11_first_order_algebra():
 # N_t is affine in the per-block matrices H_j and D_t does not depend on them,
 # so replacing every H_j by the mean over the n_blk cyclic shifts H_{(j+s) mod
 # n_blk} (which is Hbar for every j) averages the order-1 outputs of the
-# shifted statistics.  Pins the hybrid term's placement, scale, sign,
-# orientation and the set it averages over (all blocks, not the tail).
+# shifted statistics.  A causal row sees the blocks [0, lo) as Taylor
+# candidates: there the shifts run over those lo blocks only, H_{(j+s) mod lo},
+# and the average is taken over the rows that share lo.  Pins the hybrid
+# term's placement, scale, sign, orientation and the set it averages over
+# (all blocks, not the tail; a causal row's candidates, not later blocks).
 
 @pytest.mark.parametrize("causal,window,group", [(False, 0, 0), (True, 20, 0), (True, 0, 4)])
 def test_p12_hybrid_is_mean_over_relabelled_order1(causal, window, group):
@@ -429,11 +434,21 @@ def test_p12_hybrid_is_mean_over_relabelled_order1(causal, window, group):
     idx, _ = po.select(q, st, Ph)
     oh, lh = po.attention(q, k, v, st, idx, Ph)
     nb = Ph.n_blk
+    rows = np.arange(L) if Ph.pivot else np.arange(L) // bs
+    lo_t = np.array([po.row_geometry(Ph, int(r))[1] if causal else nb for r in rows])
     acc = np.zeros_like(oh)
-    for s in range(nb):
-        o1, l1 = po.attention(q, k, v, dict(st, H=np.roll(st["H"], s, axis=2)), idx, P1)
-        acc += o1 / nb
-        np.testing.assert_allclose(l1, lh, atol=1e-12)     # the denominator ignores H
+    for lo in np.unique(lo_t):
+        toks = np.nonzero(lo_t == lo)[0]
+        if lo == 0:                                          # no Taylor candidates
+            acc[:, :, toks] = oh[:, :, toks]
+            continue
+        for s in range(lo):
+            Hs = st["H"].copy()
+            Hs[:, :, :lo] = np.roll(st["H"][:, :, :lo], s, axis=2)
+            for h in range(Hq):
+                o1, l1 = po.attend_tokens(q, k, v, dict(st, H=Hs), idx, P1, 0, h, toks)
+                acc[0, h, toks] += o1 / lo
+                np.testing.assert_allclose(l1, lh[0, h, toks], atol=1e-12)   # the denominator ignores H
     np.testing.assert_allclose(oh, acc, atol=1e-12)
     o1, _ = po.attention(q, k, v, st, idx, P1)
     assert np.abs(oh - o1).max() > 1e-3                      # the blocks' H_j differ here
@@ -563,7 +578,8 @@ def test_p15_routing_prefers_high_covariance(pivot):
 # ring buffer attends exactly to the last w tokens.
 
 @pytest.mark.parametrize("taylor,window,sink,lam", [("order1", 0, 0, 0.0), ("hybrid", 20, 1, 0.0),
-                                                     ("order0", 9, 0, 0.05), ("none", 13, 2, 0.0)])
+                                                     ("order0", 9, 0, 0.0), ("none", 13, 2, 0.0),
+                                                     ("hybrid", 0, 0, 0.0)])
 def test_p16_decode_is_the_prefill_token_row(taylor, window, sink, lam):
     B, Hq, Hkv, L, d, bs = 1, 4, 2, 70, 8, 8
     q, k, v = _rand((B, Hq, L, d), 161, "bf16"), _rand((B, Hkv, L, d), 162, "bf16"), \
@@ -617,6 +633,71 @@ def test_p16_ring_is_the_sliding_window(w):
         kr[:, :, pos % w], vr[:, :, pos % w] = k[:, :, pos], v[:, :, pos]
         o, _ = po.decode_ring(q[:, :, pos], kr, vr, P, pos, w)
         np.testing.assert_allclose(o, o_ref[:, :, pos], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P17: causality.  A causal row never reads a later token: editing the keys
+# and values after position c leaves every selection row that starts at or
+# before c, and the output and lse of every token t <= c, unchanged, in every
+# Taylor mode, for block rows, PIVOT rows and decode ([SWA]: the causal mask
+# 0 <= t - s < w; the hybrid order's statistic is taken over the row's
+# candidates).  Covariance routing's global statistic would break this, so a
+# causal problem with routing is refused.
+
+def _edit_after(x, c, seed):
+    y = x.copy()
+    y[:, :, c + 1:] = _rand(y[:, :, c + 1:].shape, seed, "bf16", 3.0) + 1.5
+    return y
+
+
+@pytest.mark.parametrize("taylor", ["none", "order0", "order1", "hybrid"])
+@pytest.mark.parametrize("window,group,sink", [(0, 0, 0), (20, 0, 1), (0, 4, 0), (13, 2, 1)])
+def test_p17_causal_rows_ignore_later_tokens(taylor, window, group, sink):
+    B, Hq, Hkv, L, d, bs = 1, 4, 2, 90, 8, 8
+    q, k, v = _rand((B, Hq, L, d), 191, "bf16"), _rand((B, Hkv, L, d), 192, "bf16"), \
+        _rand((B, Hkv, L, d), 193, "bf16")
+    P = po.Problem(B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, block=bs, topk=2, window=window, group=group,
+                   n_cand=4 if group else 0, causal=True, taylor=taylor, sink=sink)
+    r = po.run(q, k, v, P)
+    for c in (11, 40, 63, 77):
+        k2, v2 = _edit_after(k, c, 194 + c), _edit_after(v, c, 195 + c)
+        r2 = po.run(q, k2, v2, P)
+        starts = np.arange(P.n_rows) if P.pivot else np.arange(P.n_rows) * bs
+        rows = starts <= c
+        assert np.array_equal(r["idx"][:, :, rows], r2["idx"][:, :, rows]), c
+        np.testing.assert_allclose(r2["O"][:, :, :c + 1], r["O"][:, :, :c + 1], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(r2["lse"][:, :, :c + 1], r["lse"][:, :, :c + 1], rtol=0, atol=1e-14)
+        assert np.abs(r2["O"][:, :, c + 1:] - r["O"][:, :, c + 1:]).max() > 1e-3   # the edit counts
+        # decode at a position <= c from a cache whose later slots hold other values
+        for pos in (c, max(0, c - 9)):
+            st, st2 = po.block_stats(q, k, v, P), po.block_stats(q, k2, v2, P)
+            i1 = po.decode_select(q[:, :, pos], st, P, pos)
+            assert np.array_equal(i1, po.decode_select(q[:, :, pos], st2, P, pos))
+            o1, l1 = po.decode_attend(q[:, :, pos], k, v, st, i1, P, pos)
+            o2, l2 = po.decode_attend(q[:, :, pos], k2, v2, st2, i1, P, pos)
+            np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-14)
+
+
+def test_p17_causal_routing_is_refused():
+    with pytest.raises(ValueError):
+        po.Problem(B=1, Hq=1, Hkv=1, L=64, d=8, block=8, topk=1, causal=True, route_lambda=0.1)
+    po.Problem(B=1, Hq=1, Hkv=1, L=64, d=8, block=8, topk=1, causal=False, route_lambda=0.1)
+
+
+def test_p17_causal_hbar_is_the_candidate_prefix_mean():
+    """Hpre[lo] is the mean of H_j over [0, lo), by its own sums over blocks."""
+    B, Hkv, L, d, bs = 1, 2, 70, 8, 8
+    q, k, v = _rand((B, Hkv, L, d), 196), _rand((B, Hkv, L, d), 197), _rand((B, Hkv, L, d), 198)
+    P = po.Problem(B=B, Hq=Hkv, Hkv=Hkv, L=L, d=d, dtype="f32", block=bs, topk=1, causal=True,
+                   taylor="hybrid")
+    st = po.block_stats(q, k, v, P)
+    assert np.all(st["Hpre"][:, :, 0] == 0)
+    for lo in range(1, P.n_blk):
+        s_end = lo * bs      # tokens of blocks [0, lo), all complete
+        raw = np.einsum("bhsc,bhse->bhce", k[:, :, :s_end], v[:, :, :s_end])
+        corr = np.einsum("bhjc,bhje->bhce", st["kbar"][:, :, :lo], st["vsum"][:, :, :lo])
+        np.testing.assert_allclose(st["Hpre"][:, :, lo], (raw - corr) / lo, rtol=0, atol=1e-11)
 
 
 # ---------------------------------------------------------------------------
