@@ -65,7 +65,7 @@ PISA_DEV float dot_row(const float *q, const T *row) {
   return acc;
 }
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = kDecodeWaves;
 constexpr int kRM = 8;   // query heads per kv head, at most
 
 // eight consecutive elements of a row as fp32
@@ -534,20 +534,6 @@ hipError_t launch_t(const DecArgs &a, void *O, float *lse, hipStream_t st) {
 }
 
 }  // namespace
-
-#ifndef PISA_DECODE_WORKGROUPS
-#define PISA_DECODE_WORKGROUPS 512   // target workgroups of decode_partial over the chip
-#endif
-
-int decode_splits(const PisaDims &dm) {
-  const int groups = dm.B * dm.Hkv;   // one group of workgroups per (batch, kv head)
-  int s = (PISA_DECODE_WORKGROUPS + groups - 1) / groups;
-  return s < 1 ? 1 : (s > 32 ? 32 : s);
-}
-
-size_t decode_workspace_bytes(const PisaDims &dm) {
-  return (size_t)dm.B * dm.Hq * decode_splits(dm) * kDecWaves * (4 + dm.d) * sizeof(float);
-}
 
 hipError_t launch_decode(const PisaDims &dm, int pos, int ring, const void *q, const void *K, const void *V,
                          const float *kbar, const float *vsum, const void *HT, const int32_t *idx, void *O,

@@ -51,8 +51,8 @@ pisa_status make_dims(const pisa_params *p, PisaDims *dm) {
   if (p->topk < 0) return fail(PISA_E_ARG, "topk must be >= 0");
   if (p->sink < 0) return fail(PISA_E_ARG, "sink must be >= 0");
   if (p->topk > kMaxTopk) return fail(PISA_E_UNSUPPORTED, "topk %d > %d", p->topk, kMaxTopk);
-  if (p->topk + p->sink > kMaxTopk)
-    return fail(PISA_E_UNSUPPORTED, "topk + sink = %d > %d", p->topk + p->sink, kMaxTopk);
+  if ((long long)p->topk + p->sink > kMaxTopk)
+    return fail(PISA_E_UNSUPPORTED, "topk + sink = %lld > %d", (long long)p->topk + p->sink, kMaxTopk);
   if (p->window < 0) return fail(PISA_E_ARG, "window must be >= 0");
   if (p->window > 0 && !p->causal)
     return fail(PISA_E_UNSUPPORTED, "a sliding window needs causal attention");

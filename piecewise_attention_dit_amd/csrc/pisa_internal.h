@@ -97,8 +97,21 @@ hipError_t launch_block_stats(const PisaDims &dm, const void *Q, const void *K, 
                               void *ws, hipStream_t st);
 hipError_t launch_indexer(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
                           const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st);
-// decode (one new token per row): split-K partials in a workspace, then a merge
-size_t decode_workspace_bytes(const PisaDims &dm);
+// decode (one new token per row): split-K partials in a workspace, then a
+// merge.  One group of `splits` workgroups of kDecodeWaves waves per (batch,
+// kv head), about kDecodeWorkgroups workgroups over the chip in all; every
+// wave writes (m, l, A, pad, o[d]) fp32 partials for each query head of its
+// kv head.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWorkgroups = 512;
+inline int decode_splits(const PisaDims &dm) {
+  const int groups = dm.B * dm.Hkv;
+  const int s = (kDecodeWorkgroups + groups - 1) / groups;
+  return s < 1 ? 1 : (s > 32 ? 32 : s);
+}
+inline size_t decode_workspace_bytes(const PisaDims &dm) {
+  return (size_t)dm.B * dm.Hq * decode_splits(dm) * kDecodeWaves * (4 + dm.d) * sizeof(float);
+}
 // the library's own fixed decode scratch (pisa_decode_fwd_noalloc): capacity
 // in bytes, and its device address on the current device
 constexpr size_t kDecodeScratchBytes = PISA_DECODE_SCRATCH_BYTES;
