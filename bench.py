@@ -83,8 +83,8 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
         stats_out += 2 * B * Hkv * n_blk * d * 4
     if taylor == "order1":
         stats_out += B * Hkv * n_blk * d * d * es
-    if taylor == "hybrid":
-        stats_out += B * Hkv * d * d * es
+    if taylor == "hybrid":   # one mean matrix, or one per lo for causal rows
+        stats_out += B * Hkv * (n_blk if causal else 1) * d * d * es
     return {k: int(v) for k, v in dict(flop_exact=flop_exact, flop_taylor0=flop_t0, flop_taylor1=flop_t1,
                                         flop_attn=flop_exact + flop_t0 + flop_t1, flop_dense=dense,
                                         stats_bytes=qkv + stats_out, exact_pairs=exact,
@@ -132,20 +132,21 @@ def cpu_baseline(wl, q, k, v, budget_s: float) -> dict:
 
 def hbm_traffic(kernel_src: str, workload: str):
     """HBM bytes per launch of the attention kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
-    calibration factor), or None if that summary was taken on other source
-    or another workload."""
+    records (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
+    calibration factor), or None unless a record was taken on this very
+    source (sha256) and workload."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)
+            recs = json.load(f).get("records", [])
         with open(kernel_src, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
+    except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for rec in recs:
+        if rec.get("source_sha256") == sha and rec.get("workload") == workload:
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def decode_bench(args):
@@ -236,6 +237,81 @@ def decode_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def _dist(a) -> dict:
+    a = np.asarray(a, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4), "p90": round(float(np.percentile(a, 90)), 4),
+            "n": int(a.size)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_peaks(torch, pisa) -> dict:
+    """On-box roofline denominators (include/pisa_roofline.h): the best of a
+    few runs of the bf16 MFMA loop (1024 workgroups of four waves, four
+    independent 32x32x16 chains per wave) and of a 1 GiB HBM copy and read."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            work = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rate = work / (e0.elapsed_time(e1) * 1e-3)
+            best = rate if best is None else max(best, rate)
+        return best
+
+    wg = 1024
+    sink = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    pisa.probe_mfma_bf16(wg, 2000, sink)
+    mfma = timed(lambda: pisa.probe_mfma_bf16(wg, 60000, sink), 3) / 1e12
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    rsink = torch.zeros(65536, dtype=torch.float32, device="cuda")
+    pisa.probe_hbm_copy(dst, src)
+    copy = timed(lambda: pisa.probe_hbm_copy(dst, src), 5) / 1e9
+    read = timed(lambda: pisa.probe_hbm_read(src, rsink), 5) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_copy_gbs": round(copy, 1), "hbm_read_gbs": round(read, 1),
+            "how": "best of 3 runs of a bf16 MFMA 32x32x16 loop (1024 workgroups x 4 waves x 4 chains) and "
+                   "of 5 runs of a 1 GiB copy (read + write bytes) and read (HIP events)"}
+
+
+def indexer_bytes(knobs: dict, wrote_cand: bool) -> int:
+    """Algorithmic HBM bytes of pisa_indexer_topk: the pooled selection vectors
+    it scores (and, PIVOT, every member query row) read once, the kept lists
+    (and proxy lists if asked for) written once."""
+    B, Hq, Hkv, L, d, bs = (knobs[k] for k in ("B", "Hq", "Hkv", "L", "d", "block"))
+    es = 2 if knobs["dtype"] == "bf16" else 4
+    group = knobs["group"]
+    n_blk = -(-L // bs)
+    klist = knobs["topk"] + knobs.get("sink", 0)
+    n_sel = -(-L // group) if group >= 1 else n_blk
+    n_rows = L if group >= 1 else n_blk
+    total = B * Hq * n_sel * d * es + B * Hkv * n_blk * d * es + B * Hq * n_rows * klist * 4
+    if group >= 1:
+        total += B * Hq * L * d * es
+        if wrote_cand:
+            total += B * Hq * n_sel * knobs["n_cand"] * 4
+    if knobs.get("route_lambda", 0.0) > 0:
+        total += B * Hkv * n_blk * 4
+    return total
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +326,9 @@ def main():
                          "(reported as workload <name>_<mode>)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the warm-up and the timed steps (for traces): no distribution, "
+                         "cold-cache, peak-probe or diagnostic runs")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run three plain device copies of MIB MiB (reads and writes MIB MiB "
                          "each), to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -286,23 +365,29 @@ def main():
     p = pisa.make_params(**knobs)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
     st = pisa.alloc_stats(p)
-    idx, cand = pisa.alloc_index(p)
+    idx, _ = pisa.alloc_index(p)      # the proxy lists (diagnostics) are not asked for
     out = torch.empty_like(dq)
     lse = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device="cuda")
+    ws_need = pisa.workspace_size(p, 0)
+    ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        pisa.block_stats(p, dq, dk, dv, st)
+        pisa.block_stats(p, dq, dk, dv, st, ws=ws)
         if ev:
             ev[1].record(stream)
-        pisa.indexer_topk(p, dq, st, idx, cand)
+        pisa.indexer_topk(p, dq, st, idx, None, want_cand=False)
         if ev:
             ev[2].record(stream)
         pisa.sparse_attn_fwd(p, dq, dk, dv, st, idx, out, lse)
         if ev:
             ev[3].record(stream)
+
+    def per_call(evs):
+        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                         for e in evs])
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -316,9 +401,40 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    per = per_call(evs)
     ms_stats, ms_idx, ms_attn = per.mean(axis=0)
     ms_step = wall * 1e3 / args.steps
+
+    extras = {}
+    if not args.no_extras:
+        # the same step N more times, for the spread of each call
+        n_dist = max(50, args.steps)
+        print(f"[bench] distribution over {n_dist} steps", file=sys.stderr, flush=True)
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_dist)]
+        for i in range(n_dist):
+            step(evd[i])
+        torch.cuda.synchronize()
+        extras["dist"] = per_call(evd)
+        # cold cache: 512 MiB written before every step (more than the 256 MB
+        # last-level cache and the L2s together)
+        print("[bench] cold-cache steps", file=sys.stderr, flush=True)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(12)]
+        for i in range(12):
+            flush.fill_(i & 255)
+            step(evc[i])
+        torch.cuda.synchronize()
+        extras["cold"] = per_call(evc)
+        del flush
+        # selection diagnostics (counters slow the call: untimed)
+        dg = torch.zeros(16, dtype=torch.int32, device="cuda")
+        pisa.indexer_topk(p, dq, st, idx, None, want_cand=False, diag=dg)
+        torch.cuda.synchronize()
+        dgh = dg.cpu().tolist()
+        extras["diag"] = {"rows_selected": dgh[0], "rows_rescored": dgh[1], "rows_or_candidates_exact": dgh[2]}
+        print("[bench] roofline probes", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        extras["peaks"] = measured_peaks(torch, pisa)
 
     work = algorithmic_work(knobs, idx.cpu().numpy())
     # bf16 runs on the matrix cores; the fp32 path is plain fp32 FMA on the
@@ -327,6 +443,9 @@ def main():
     tflops_eff = work["flop_dense"] / (ms_step * 1e-3) / 1e12
     attn_achieved = work["flop_attn"] / (ms_attn * 1e-3) / 1e12
     stats_gbs = work["stats_bytes"] / (ms_stats * 1e-3) / 1e9
+    idx_bytes = indexer_bytes(knobs, wrote_cand=False)
+    idx_gbs = idx_bytes / (ms_idx * 1e-3) / 1e9
+    kept_frac = work["flop_exact"] / (ms_attn * 1e-3) / 1e12 / peak
     line = {
         "metric": "sparse-attn fwd ms & effective TFLOP/s at L=32K; % of bf16 MFMA / HBM roofline",
         "value": round(tflops_eff, 2),
@@ -349,17 +468,33 @@ def main():
                      "frac": round(attn_achieved / peak, 4),
                      "traffic": hbm_traffic(ATTN_SRC[wl.group == 0], wl.name) if wl.dtype == "bf16" else None},
         "kernels": {
-            "block_stats": {"ms": round(ms_stats, 4), "GB/s": round(stats_gbs, 1),
+            "block_stats": {"ms": round(ms_stats, 4), "bytes": work["stats_bytes"], "GB/s": round(stats_gbs, 1),
                             "hbm_frac": round(stats_gbs / PEAK_HBM_GBS, 4)},
-            "indexer_topk": {"ms": round(ms_idx, 4)},
+            "indexer_topk": {"ms": round(ms_idx, 4), "bytes": idx_bytes, "GB/s": round(idx_gbs, 1),
+                             "hbm_frac": round(idx_gbs / PEAK_HBM_GBS, 4)},
             "sparse_attn_fwd": {"ms": round(ms_attn, 4),
-                                "kept_mfma_frac": round(work["flop_exact"] / (ms_attn * 1e-3) / 1e12
-                                                        / peak, 4),
+                                "kept_mfma_frac": round(kept_frac, 4),
                                 "total_mfma_frac": round(attn_achieved / peak, 4),
                                 "flop_exact": work["flop_exact"], "flop_taylor": work["flop_taylor0"]
                                 + work["flop_taylor1"]},
         },
+        "host": {"cpu_model": cpu_model(), "cpus": len(os.sched_getaffinity(0))},
     }
+    names = ("block_stats", "indexer_topk", "sparse_attn_fwd")
+    if extras:
+        for c, nm in enumerate(names):
+            line["kernels"][nm]["dist_ms"] = _dist(extras["dist"][:, c])
+            line["kernels"][nm]["cold_ms"] = _dist(extras["cold"][:, c])
+        line["kernels"]["indexer_topk"].update(extras["diag"])
+        pk = extras["peaks"]
+        line["measured_peaks"] = pk
+        if peak_kind == "mfma":
+            line["roofline"]["peak_measured"] = pk["mfma_bf16_tflops"]
+            line["roofline"]["frac_measured"] = round(attn_achieved / pk["mfma_bf16_tflops"], 4)
+            line["kernels"]["sparse_attn_fwd"]["kept_mfma_frac_measured"] = round(
+                kept_frac * peak / pk["mfma_bf16_tflops"], 4)
+        for nm, gbs in (("block_stats", stats_gbs), ("indexer_topk", idx_gbs)):
+            line["kernels"][nm]["hbm_frac_measured_copy"] = round(gbs / pk["hbm_copy_gbs"], 4)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)

@@ -63,7 +63,11 @@ def lib() -> ctypes.CDLL:
         L.pisa_decode_topk.argtypes = [P, i32, vp, S, vp, vp]
         L.pisa_decode_fwd.argtypes = [P, i32, i32, vp, vp, vp, S, vp, vp, vp, vp, sz, vp]
         L.pisa_decode_fwd_noalloc.argtypes = [P, i32, i32, vp, vp, vp, S, vp, vp, vp, vp]
-        for f in ("pisa_validate", "pisa_stats_layout", "pisa_index_layout", "pisa_workspace_size",
+        L.pisa_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+        L.pisa_probe_hbm_copy.argtypes = [vp, vp, sz, vp]
+        L.pisa_probe_hbm_read.argtypes = [vp, sz, vp, vp]
+        for f in ("pisa_probe_mfma_bf16", "pisa_probe_hbm_copy", "pisa_probe_hbm_read",
+                  "pisa_validate", "pisa_stats_layout", "pisa_index_layout", "pisa_workspace_size",
                   "pisa_block_stats", "pisa_indexer_topk", "pisa_sparse_attn_fwd", "pisa_decode_topk",
                   "pisa_decode_fwd", "pisa_decode_fwd_noalloc"):
             getattr(L, f).restype = ctypes.c_int
@@ -246,6 +250,28 @@ def decode_fwd_noalloc(p: Params, pos: int, q, k, v, stats=None, idx=None, ring:
                                          ctypes.byref(cs) if cs is not None else None, _ptr(idx), _ptr(out),
                                          _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def probe_mfma_bf16(workgroups: int, iters: int, sink, stream=None) -> float:
+    """Roofline probe (include/pisa_roofline.h): enqueue the bf16 MFMA loop;
+    returns the dense bf16 FLOPs it executes."""
+    _check(lib().pisa_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _stream(stream)))
+    return float(workgroups) * 4 * iters * 4 * 32768
+
+
+def probe_hbm_copy(dst, src, stream=None) -> int:
+    """Roofline probe: dst <- src (uint8 tensors of equal size); returns the
+    HBM bytes moved (read + write)."""
+    n = src.numel() * src.element_size()
+    _check(lib().pisa_probe_hbm_copy(_ptr(dst), _ptr(src), n, _stream(stream)))
+    return 2 * n
+
+
+def probe_hbm_read(src, sink, stream=None) -> int:
+    """Roofline probe: read every byte of src; returns the bytes read."""
+    n = src.numel() * src.element_size()
+    _check(lib().pisa_probe_hbm_read(_ptr(src), n, _ptr(sink), _stream(stream)))
+    return n
 
 
 def attention(q, k, v, *, block=64, topk=0, window=0, group=0, n_cand=0, causal=False,
