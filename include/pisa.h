@@ -166,8 +166,12 @@ pisa_status pisa_index_layout(const pisa_params *p, size_t bytes[2]);
  * 2 = sparse_attn_fwd, 3 = decode_fwd).  decode_fwd always needs one
  * (fp32 split-K partials).  block_stats needs one for the HYBRID order with bf16
  * inputs and for routing (fp32 partial sums of the mean first-order matrix and
- * an fp32 copy of it; 16-byte aligned, contents need not be initialised and
- * are garbage afterwards); every other call and mode needs none.  A non-NULL workspace of at least
+ * an fp32 copy of it).  sparse_attn_fwd needs one for PIVOT rows in bf16 with
+ * taylor NONE when the rows' kept sets fit the key-gathered kernel (at most
+ * 1024 blocks, its LDS budget): K and V^T of every 64-key unit in MFMA
+ * fragment order, 4 * B * Hkv * n_blk * block * d bytes; 0 otherwise.  Workspaces are 16-byte aligned;
+ * their contents need not be initialised and are garbage afterwards.  Every
+ * other call and mode needs none.  A non-NULL workspace of at least
  * PISA_DIAG_BYTES passed to pisa_indexer_topk receives diagnostic counters
  * (int32: rows selected, rows whose fast selection was not certified and went
  * to a float64 re-score or an exact comparison, rows or candidates decided by
@@ -223,7 +227,8 @@ pisa_status pisa_indexer_topk(const pisa_params *p, const void *Q, const pisa_st
  * dropped on the device, so no entry reads outside Q, K, V or the statistics.
  * Block rows (group == 0) accept the entries in any order and repeated.
  * PIVOT rows (group >= 1) need the kept entries in ascending order (repeats
- * and dropped entries may sit anywhere); pisa_indexer_topk writes them so. */
+ * and dropped entries may sit anywhere); pisa_indexer_topk writes them so.
+ * ws: at least pisa_workspace_size(p, 2) bytes, else PISA_E_WORKSPACE. */
 pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void *K,
                                  const void *V, const pisa_stats *stats, const int32_t *idx,
                                  void *O, float *lse, void *ws, size_t ws_bytes,

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libpisa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["pisa_host.cpp", "stats.hip", "indexer.hip", "attn.hip", "attn_blocks.hip", "attn_f32.hip",
-           "decode.hip", "roofline.hip"]
+           "decode.hip", "roofline.hip", "attn_pivot.hip"]
 ARCH = "gfx950"
 
 

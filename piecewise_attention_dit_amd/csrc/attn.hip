@@ -729,11 +729,13 @@ hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const void *V, const float *kbar,
-                       const float *vsum, const void *HT, const int32_t *idx, void *O, float *lse,
+                       const float *vsum, const void *HT, const int32_t *idx, void *O, float *lse, void *ws,
                        hipStream_t st) {
   AttnArgs a;
   a.dm = dm;
   a.Q = Q; a.K = K; a.V = V; a.kbar = kbar; a.vsum = vsum; a.HT = HT; a.idx = idx; a.O = O; a.lse = lse;
   a.sl2 = dm.scale * kLog2e;
-  return dm.dtype == 1 ? launch_attn_f32(a, st) : launch_attn_bf16(a, st);
+  if (dm.dtype == 1) return launch_attn_f32(a, st);
+  if (ws && pivot_kg_supported(dm)) return launch_attn_pivot(a, ws, st);
+  return launch_attn_bf16(a, st);
 }

@@ -34,3 +34,5 @@ PISA_DEV void lds_barrier() {
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_blocks(const AttnArgs &a, hipStream_t st);
+// PIVOT rows without a Taylor tail, key-gathered (workspace: V^T per block)
+hipError_t launch_attn_pivot(const AttnArgs &a, void *ws, hipStream_t st);

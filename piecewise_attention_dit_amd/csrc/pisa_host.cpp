@@ -171,7 +171,10 @@ pisa_status pisa_workspace_size(const pisa_params *p, int op, size_t *bytes) {
   PISA_TRY(make_dims(p, &dm));
   if (!bytes) return fail(PISA_E_ARG, "bytes is NULL");
   if (op < 0 || op > 3) return fail(PISA_E_ARG, "unknown op %d", op);
-  *bytes = op == 0 ? stats_workspace_bytes(dm) : op == 3 ? decode_workspace_bytes(dm) : 0;
+  *bytes = op == 0   ? stats_workspace_bytes(dm)
+           : op == 2 ? pivot_kg_workspace_bytes(dm)
+           : op == 3 ? decode_workspace_bytes(dm)
+                     : 0;
   return PISA_OK;
 }
 
@@ -241,10 +244,12 @@ pisa_status pisa_sparse_attn_fwd(const pisa_params *p, const void *Q, const void
     PISA_TRY(check_ptr(stats->vsum, "stats.vsum", true));
     PISA_TRY(check_ptr(stats->HT, "stats.HT", dm.taylor == PISA_TAYLOR_ORDER1 || dm.taylor == PISA_TAYLOR_HYBRID));
   }
-  PISA_TRY(check_ws(ws, ws_bytes, 0));
+  const size_t need = pivot_kg_workspace_bytes(dm);
+  PISA_TRY(check_ws(ws, ws_bytes, need));
+  if (need && !aligned16(ws)) return fail(PISA_E_ARG, "workspace is not 16-byte aligned");
   dm.topk = dm.klist;   // the attention kernels take topk as the width of a kept list
   return launched(launch_attn(dm, Q, K, V, ty ? stats->kbar : nullptr, ty ? stats->vsum : nullptr,
-                              ty ? stats->HT : nullptr, idx, O, lse, stream),
+                              ty ? stats->HT : nullptr, idx, O, lse, need ? ws : nullptr, stream),
                   "sparse_attn_fwd");
 }
 

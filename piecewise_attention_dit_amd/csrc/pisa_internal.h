@@ -123,4 +123,57 @@ hipError_t launch_decode_topk(const PisaDims &dm, int pos, const void *q, const 
                               int32_t *idx, int32_t *diag, hipStream_t st);
 hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const void *V,
                        const float *kbar, const float *vsum, const void *HT, const int32_t *idx,
-                       void *O, float *lse, hipStream_t st);
+                       void *O, float *lse, void *ws, hipStream_t st);
+// PIVOT rows in bf16 with no Taylor tail run key-gathered: a workgroup
+// takes kPivotRows rows (tokens x the query heads of one KV head), inverts
+// their kept sets into per-block row lists and accumulates every row's
+// output in LDS; the workspace holds K and V^T of every 64-key unit in MFMA
+// fragment order, 4 B Hkv n_blk block d bytes.  The LDS layout depends on the problem:
+//   acc    fp32 [kPivotRows][d] output accumulators (the set-up's bitmaps
+//          [32 words][kPivotRows] and four int[1024] block arrays overlay it)
+//   ml     fp32 running maxima, one copy per wave [4][kPivotRows], and the
+//          running sums [kPivotRows]
+//   px     four tile slots: P^T fragments (64 lanes x 32 bytes) and the 16
+//          row maxima
+//   bkt    u8 row ids of the per-block lists, ent_cap entries
+//   til    u32 tiles, tile_cap entries
+//   small  int[4]: list entries, tiles
+constexpr int kPivotRows = 256;
+constexpr int kPivotLdsMax = 160 * 1024;
+struct PivotLds {
+  int acc, ml, px, bkt, til, small, total;
+  int ent_cap, tile_cap;
+};
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline PivotLds pivot_lds(const PisaDims &dm) {
+  PivotLds y;
+  // a row keeps its list entries and, causal, the window range [lo, own]
+  const int win = dm.causal ? (dm.window > 0 ? (dm.window - 1) / dm.bs + 2 : 1) : 0;
+  const long long ent = (long long)kPivotRows * (dm.klist + win);
+  y.ent_cap = ent > (1 << 20) ? (1 << 20) : (int)ent;
+  const int nh = dm.bs / 64;
+  const int used = dm.n_blk < y.ent_cap ? dm.n_blk : y.ent_cap;   // blocks with a non-empty list
+  y.tile_cap = nh * (y.ent_cap / 16 + used);
+  y.acc = 0;
+  y.ml = kPivotRows * dm.d * 4;
+  y.px = y.ml + 5 * kPivotRows * 4;
+  y.bkt = y.px + 4 * (64 * 32 + 16 * 4);
+  y.til = y.bkt + ((y.ent_cap + 15) & ~15);
+  y.small = y.til + y.tile_cap * 4;
+  y.total = y.small + 16;
+  return y;
+}
+inline bool pivot_kg_supported(const PisaDims &dm) {
+  if (dm.dtype != 0 || dm.group < 1 || dm.taylor != 0) return false;
+  if ((dm.d != 64 && dm.d != 128) || (dm.bs != 64 && dm.bs != 128)) return false;
+  // bitmaps of 32 words per row; row ids in a byte; tiles pack the block in
+  // 10 bits and the list offset in 15
+  if (dm.n_blk > 1024 || dm.ratio < 1 || dm.ratio > kPivotRows) return false;
+  const PivotLds y = pivot_lds(dm);
+  return y.ent_cap <= 32768 && y.total <= kPivotLdsMax;
+}
+inline size_t pivot_kg_workspace_bytes(const PisaDims &dm) {
+  return pivot_kg_supported(dm) ? (size_t)dm.B * dm.Hkv * dm.n_blk * dm.d * dm.bs * 4 : 0;
+}

@@ -196,14 +196,20 @@ def indexer_topk(p: Params, q, stats: dict, idx=None, cand=None, want_cand=True,
 
 
 def sparse_attn_fwd(p: Params, q, k, v, stats: dict, idx, out=None, lse=None, want_lse=True,
-                    stream=None):
+                    ws=None, stream=None):
+    """Stage C.  ws: a device byte buffer of at least workspace_size(p, 2)
+    bytes (allocated here when the problem needs one and none is given)."""
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((p.B, p.Hq, p.L), dtype=torch.float32, device=q.device)
+    need = workspace_size(p, 2)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     cs = _cstats(stats)
     _check(lib().pisa_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
-                                      _ptr(idx), _ptr(out), _ptr(lse), None, 0, _stream(stream)))
+                                      _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+                                      ws.numel() if ws is not None else 0, _stream(stream)))
     return out, lse
 
 

@@ -36,7 +36,7 @@ hipError_t launch_decode_topk(const PisaDims &, int, const void *, const void *,
   return hipSuccess;
 }
 hipError_t launch_attn(const PisaDims &, const void *, const void *, const void *, const float *, const float *,
-                       const void *, const int32_t *, void *, float *, hipStream_t) {
+                       const void *, const int32_t *, void *, float *, void *, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }

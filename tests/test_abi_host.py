@@ -120,6 +120,28 @@ def test_layouts():
     assert pisa.workspace_size(_p(L=1000, route_lambda=0.5, dtype="f32"), 0) == 2 * 128 * 128 * 4
 
 
+def test_attention_workspace():
+    """PIVOT rows in bf16 without a Taylor tail run key-gathered and need K and
+    V^T in MFMA fragment order, 4 B Hkv n_blk block d bytes, when their kept
+    sets fit the kernel's LDS (rows x (list + window blocks))."""
+    pv = dict(group=8, n_cand=8, causal=True, taylor="none", topk=4)
+    assert pisa.workspace_size(_p(L=1000, **pv), 2) == 1 * 2 * 16 * 128 * 64 * 4
+    assert pisa.workspace_size(_p(L=1000, block=128, d=64, **pv), 2) == 1 * 2 * 8 * 64 * 128 * 4
+    assert pisa.workspace_size(_p(L=1000, **{**pv, "causal": False}), 2) == 1 * 2 * 16 * 128 * 64 * 4
+    assert pisa.workspace_size(_p(L=1000, **{**pv, "taylor": "order1"}), 2) == 0
+    assert pisa.workspace_size(_p(L=1000, dtype="f32", **pv), 2) == 0
+    assert pisa.workspace_size(_p(L=1000, group=0, topk=4, causal=True, taylor="none"), 2) == 0
+    # the largest problem the library takes, 1024 blocks, fills the set-up's bitmaps
+    assert pisa.workspace_size(_p(L=64 * 1024, **pv), 2) == 1 * 2 * 1024 * 128 * 64 * 4
+    with pytest.raises(pisa.PisaError):
+        pisa.workspace_size(_p(L=64 * 1025, **pv), 2)
+    # a 4096-token window adds 65 blocks per row: past the LDS budget at d 128,
+    # within it at d 64
+    wide = dict(pv, window=4096, topk=32, n_cand=64)
+    assert pisa.workspace_size(_p(L=8192, **wide), 2) == 0
+    assert pisa.workspace_size(_p(L=8192, d=64, **wide), 2) == 1 * 2 * 128 * 64 * 64 * 4
+
+
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 
 

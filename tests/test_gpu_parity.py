@@ -79,6 +79,13 @@ def test_parity_cases(name):
     dict(L=500, block=64, topk=2, d=64, group=4, n_cand=5, dtype="f32", causal=True, taylor="hybrid"),
     dict(L=1300, block=64, topk=2, d=64, causal=True, window=130, taylor="hybrid"),
     dict(L=1500, block=128, topk=1, d=128, causal=True, taylor="hybrid"),
+    # PIVOT rows without a Taylor tail (key-gathered kernel): GQA 8 with a
+    # window, one head per kv head with d 64 and 128-token blocks, non-causal
+    # GQA 2, and rows whose lists repeat the whole proxy list
+    dict(L=900, block=64, topk=3, group=4, n_cand=6, causal=True, window=150, taylor="none", Hq=8, Hkv=1),
+    dict(L=1300, block=128, topk=2, group=8, n_cand=5, causal=True, taylor="none", d=64, Hq=2, Hkv=2),
+    dict(L=700, block=64, topk=3, group=2, n_cand=6, causal=False, taylor="none", Hq=4, Hkv=2),
+    dict(L=1100, block=64, topk=5, group=8, n_cand=5, causal=True, window=64, taylor="none", Hq=4, Hkv=2, sink=1),
     # d 64 first order takes four Taylor entries per barrier: two batches of
     # entries, the last group short
     dict(L=1500, block=64, topk=2, d=64, taylor="order1"),
