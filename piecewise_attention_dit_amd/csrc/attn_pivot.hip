@@ -20,9 +20,11 @@
 //            from memory), its own row maxima, and P^T in bf16 as the MFMA B
 //            operand, into an LDS slot;
 //   phase 2  wave p takes the quarter p of the features for all four tiles:
-//            O^T = V^T P^T, then folds each tile row into the row's fp32
-//            accumulator in LDS (rescale by the running maximum).  Wave 0
-//            also gets the row sums, from an all-ones V^T tile.
+//            O^T = V^T P^T.  During the next round's phase 1 each tile row
+//            folds into the row's fp32 accumulator in LDS (rescale by the
+//            running maximum), so the folds' LDS latency overlaps that
+//            round's softmax.  The row sums of the bf16 weights come from
+//            phase 1; wave 0 folds them.
 // K and V^T come from a copy of every 64-key unit in MFMA fragment order
 // (V^T keys in the order the MFMA takes P^T from the S^T registers): an
 // operand load reads one contiguous kilobyte, where loading a fragment from
@@ -39,6 +41,7 @@ using namespace pisa_attn;
 namespace {
 
 constexpr int kPvRows = kPivotRows;   // rows per workgroup
+constexpr int kPvRowsA = kPvRows + 1; // accumulator rows: the last is a dummy
 constexpr int kPvWaves = 4;
 constexpr int kPvThreads = kPvWaves * 64;
 constexpr int kPvTile = 16;           // rows per tile
@@ -95,10 +98,15 @@ __global__ __launch_bounds__(256) void kv_prep(PisaDims dm, const uint16_t *__re
   KVF[gid] = out;
 }
 
-// max of x over lanes l and l ^ 16 (v_permlane16_swap_b32, as pair_max_f)
+// max and sum of x over lanes l and l ^ 16 (v_permlane16_swap_b32, as
+// pair_max_f)
 PISA_DEV float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+PISA_DEV float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // accumulator float index of (row, 16-byte chunk): chunks of a row permuted
@@ -140,8 +148,8 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
   const bool causal = dm.causal != 0;
 
   float *acc = reinterpret_cast<float *>(lds + ly.acc);
-  float *mrun = reinterpret_cast<float *>(lds + ly.ml);   // [4][256]
-  float *lrun = mrun + kPvWaves * kPvRows;                 // [256]
+  float *mrun = reinterpret_cast<float *>(lds + ly.ml);   // [4][257]
+  float *lrun = mrun + kPvWaves * kPvRowsA;                // [257]
   uint8_t *px = lds + ly.px;
   uint8_t *bkt = lds + ly.bkt;
   uint32_t *til = reinterpret_cast<uint32_t *>(lds + ly.til);
@@ -249,9 +257,9 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
   const int n_tiles = small[1];
   __syncthreads();   // the set-up arrays are dead: the accumulators take their place
   // ---- 5. accumulators 0, running maxima -inf, sums 0
-  for (int i = tid; i < kPvRows * D / 4; i += kPvThreads) reinterpret_cast<f32x4_t *>(acc)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int i = tid; i < kPvWaves * kPvRows; i += kPvThreads) mrun[i] = kNegInf;
-  lrun[tid] = 0.f;
+  for (int i = tid; i < kPvRowsA * D / 4; i += kPvThreads) reinterpret_cast<f32x4_t *>(acc)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = tid; i < kPvWaves * kPvRowsA; i += kPvThreads) mrun[i] = kNegInf;
+  for (int i = tid; i < kPvRowsA; i += kPvThreads) lrun[i] = 0.f;
   __syncthreads();
 
   const int p = w;
@@ -259,13 +267,11 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
   const uint16_t *Qb = static_cast<const uint16_t *>(a.Q);
   // this kv head's units: 16 D chunks each, KF then VF
   const u32x4_t *KVh = KVF + (size_t)bk * dm.n_blk * NH * 16 * D;
-  float *mown = mrun + p * kPvRows;
-  const uint32_t one2 = 0x3F803F80u;   // two bf16 ones
-  const u32x4_t ones = {one2, one2, one2, one2};
+  float *mown = mrun + p * kPvRowsA;
 
-  // Operands of a round: the own tile (phase 1: block, half, lane's token,
-  // Q rows and K) and the round's tiles (phase 2: lane's row, -1 for none,
-  // and V^T of quarter p).  Two sets alternate, each loaded two rounds ahead.
+  // Operands of a round, loaded one round ahead: the own tile (phase 1:
+  // block, half, lane's token, Q rows and K) and the round's tiles (phase 2:
+  // lane's row, -1 for none, and V^T of quarter p).
   struct Set {
     Tile ot;
     int ott;
@@ -273,14 +279,19 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
     int rrow[4];
     u32x4_t vq[4][MQ][2];
   };
+  // Q rows are read four lanes to a row (lane l: row l / 4, bytes
+  // 16 (l % 4) of each 64-byte chunk) and moved to the MFMA layout (lane
+  // c + 16 g: row c, chunk g) at use
   auto load_own = [&](Set &S, int ti) {
     S.ot = tile_of(til[ti]);
     const int orow = bkt[S.ot.start + min(c, S.ot.n - 1)];
-    const int t = T0 + orow % TT, h = hk * R + orow / TT;
-    S.ott = t;
+    S.ott = T0 + orow % TT;
+    const int qrow = bkt[S.ot.start + min(l >> 2, S.ot.n - 1)];
+    const int tq = T0 + qrow % TT, hq = hk * R + qrow / TT;
 #pragma unroll
     for (int ks = 0; ks < KQ; ++ks)
-      S.qf[ks] = *reinterpret_cast<const u32x4_t *>(Qb + ((size_t)(b * dm.Hq + h) * dm.L + t) * D + 32 * ks + 8 * g);
+      S.qf[ks] =
+          *reinterpret_cast<const u32x4_t *>(Qb + ((size_t)(b * dm.Hq + hq) * dm.L + tq) * D + 32 * ks + 8 * (l & 3));
     const u32x4_t *kfu = KVh + (size_t)(S.ot.j * NH + S.ot.hh) * 16 * D;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -302,152 +313,163 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
         for (int s2 = 0; s2 < 2; ++s2) S.vq[s][mq][s2] = vfu[((MQ * p + mq) * 2 + s2) * 64 + l];
     }
   };
+  // A round's O^T quarters wait in registers and fold into the accumulators
+  // during the next round's phase 1, in tile order.  Entries that fold
+  // nothing (no row, or no visible key) go to a dummy row, so the folds have
+  // no branches and their LDS traffic can overlap the softmax.
+  f32x4_t po[4][MQ];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq) po[s][mq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int prow[4] = {kPvRows, kPvRows, kPvRows, kPvRows};
+  float pmt[4] = {0.f, 0.f, 0.f, 0.f}, plt[4] = {0.f, 0.f, 0.f, 0.f};
+  auto fold = [&]() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int row = prow[s];
+      // every read of the row before any write: one LDS round trip per tile
+      f32x4_t *ap[MQ];
+      f32x4_t av[MQ];
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        ap[mq] = reinterpret_cast<f32x4_t *>(acc + acc_at<D>(row, (QF * p + 16 * mq + 4 * g) / 4));
+        av[mq] = *ap[mq];
+      }
+      const float mo = mown[row];
+      const float lo = p == 0 ? lrun[row] : 0.f;
+      const float mn = fmaxf(mo, pmt[s]);
+      const float ca = fast_exp2(mo - mn), cb = fast_exp2(pmt[s] - mn);
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        f32x4_t nv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nv[r] = av[mq][r] * ca + po[s][mq][r] * cb;
+        *ap[mq] = nv;
+      }
+      // the four lanes of a row store the same values
+      mown[row] = mn;
+      if (p == 0) lrun[row] = lo * ca + plt[s] * cb;
+    }
+  };
   auto round = [&](Set &S, int rd) {
-      const int t0 = kPvWaves * rd, ti = t0 + p;
-      const bool act = ti < n_tiles;
-      uint8_t *slot = px + p * (64 * 32 + 64);
-      // ================= phase 1: tile t0 + p
-      // S^T = K Q^T per 16-key tile: lane holds keys 16 m + 4 g + r of row c
-      f32x4_t sacc[4];
+    const int t0 = kPvWaves * rd, ti = t0 + p;
+    const bool act = ti < n_tiles;
+    uint8_t *slot = px + p * kPivotSlotBytes;
+    // ================= phase 1: tile t0 + p, and the folds of the last round
+    u32x4_t qm[KQ];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        f32x4_t sa = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KQ; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KQ; ++ks) sa = mfma16(S.kf[m][ks], S.qf[ks], sa);
-        sacc[m] = sa;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const int j = S.ot.j, hh = S.ot.hh, t = S.ott;
-      const bool rv = c < S.ot.n;
-      // the own tile two rounds on, in flight during this round and the next
-      load_own(S, min(ti + 2 * kPvWaves, n_tiles - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      if (act) {
-        // masks: the last visible key of the unit is the sequence end or, in
-        // the token's own block (causal), the token itself
-        const int kbase = j * BS + 64 * hh;
-        const bool diag = causal && j == t / BS;
-        const int lim = (diag ? t : dm.L - 1) - kbase;
-        float mx = kNegInf;
-        if (ballot64(lim < 63) == 0) {
+      for (int i = 0; i < 4; ++i) qm[ks][i] = __builtin_amdgcn_ds_bpermute((4 * c + g) << 2, (int)S.qf[ks][i]);
+    // S^T = K Q^T per 16-key tile: lane holds keys 16 m + 4 g + r of row c
+    f32x4_t sacc[4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+      f32x4_t sa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              sacc[m][r] *= sl2;
-              mx = fmaxf(mx, sacc[m][r]);
-            }
-        } else {
+      for (int ks = 0; ks < KQ; ++ks) sa = mfma16(S.kf[m][ks], qm[ks], sa);
+      sacc[m] = sa;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int j = S.ot.j, hh = S.ot.hh, t = S.ott;
+    const bool rv = act && c < S.ot.n;
+    // the next round's own tile, in flight during the rest of this round
+    load_own(S, min(ti + kPvWaves, n_tiles - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    fold();
+    // masks: the last visible key of the unit is the sequence end or, in the
+    // token's own block (causal), the token itself
+    const int kbase = j * BS + 64 * hh;
+    const bool diag = causal && j == t / BS;
+    const int lim = (diag ? t : dm.L - 1) - kbase;
+    float mx = kNegInf;
+    if (ballot64(lim < 63) == 0) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float x = 16 * m + 4 * g + r <= lim ? sacc[m][r] * sl2 : kNegInf;
-              sacc[m][r] = x;
-              mx = fmaxf(mx, x);
-            }
+        for (int r = 0; r < 4; ++r) {
+          sacc[m][r] *= sl2;
+          mx = fmaxf(mx, sacc[m][r]);
         }
-        mx = pair_max_f(max_xor16(mx));
-        // a row with no visible key in this unit (the future half of its own
-        // 128-key block) folds nothing
-        const bool any = rv && mx != kNegInf;
-        const float mref = mx != kNegInf ? mx : 0.f;
-        // P^T as the B operand of O^T = V^T P^T: K-step s takes the 16-key
-        // tiles 2 s and 2 s + 1
+    } else {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          float e[8];
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e[r] = fast_exp2(sacc[2 * s][r] - mref);
-            e[4 + r] = fast_exp2(sacc[2 * s + 1][r] - mref);
-          }
-          const u32x4_t pb = u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                                     pack_bf16x2(e[6], e[7])};
-          *reinterpret_cast<u32x4_t *>(slot + l * 32 + 16 * s) = pb;
+        for (int r = 0; r < 4; ++r) {
+          const float x = 16 * m + 4 * g + r <= lim ? sacc[m][r] * sl2 : kNegInf;
+          sacc[m][r] = x;
+          mx = fmaxf(mx, x);
         }
-        if (g == 0) reinterpret_cast<float *>(slot + 64 * 32)[c] = any ? mx : kNegInf;
+    }
+    mx = pair_max_f(max_xor16(mx));
+    // a row with no visible key in this unit (the future half of its own
+    // 128-key block) folds nothing
+    const bool any = rv && mx != kNegInf;
+    const float mref = mx != kNegInf ? mx : 0.f;
+    // P^T as the B operand of O^T = V^T P^T: K-step s takes the 16-key tiles
+    // 2 s and 2 s + 1; the row sum from the same bf16 weights
+    u32x4_t pb[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float e[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e[r] = fast_exp2(sacc[2 * s][r] - mref);
+        e[4 + r] = fast_exp2(sacc[2 * s + 1][r] - mref);
       }
-      lds_barrier();
-      // ================= phase 2: quarter p of the round's tiles.  The slots'
-      // P^T and maxima and every MFMA first, then the next round's V^T goes in
-      // flight, then the tiles fold into the accumulators in order (a row may
-      // sit in several tiles of a round, at different lanes)
-      u32x4_t pbs[4][2];
-      float mts[4];
-      f32x4_t o[4][MQ];
-      float lts[4];
-      int rows[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        rows[s] = t0 + s < n_tiles ? S.rrow[s] : -1;
-        const uint8_t *sl = px + s * (64 * 32 + 64);
-        pbs[s][0] = *reinterpret_cast<const u32x4_t *>(sl + l * 32);
-        pbs[s][1] = *reinterpret_cast<const u32x4_t *>(sl + l * 32 + 16);
-        mts[s] = reinterpret_cast<const float *>(sl + 64 * 32)[c];
+      pb[s] = u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                      pack_bf16x2(e[6], e[7])};
+      ls = sum_bf16x8_f(pb[s], ls);
+    }
+    ls = pair_sum_f(sum_xor16(ls));
+    if (act) {
+      *reinterpret_cast<u32x4_t *>(slot + l * 32) = pb[0];
+      *reinterpret_cast<u32x4_t *>(slot + l * 32 + 16) = pb[1];
+      if (g == 0) {
+        reinterpret_cast<float *>(slot + 64 * 32)[c] = any ? mx : kNegInf;
+        reinterpret_cast<float *>(slot + 64 * 32)[16 + c] = ls;
       }
+    }
+    lds_barrier();
+    // ================= phase 2: quarter p of the round's tiles; the
+    // products wait in registers for the next round's phase 1
+    u32x4_t pbs[4][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 4; ++s) {
+      const uint8_t *sl = px + s * kPivotSlotBytes;
+      pbs[s][0] = *reinterpret_cast<const u32x4_t *>(sl + l * 32);
+      pbs[s][1] = *reinterpret_cast<const u32x4_t *>(sl + l * 32 + 16);
+      const float mt = reinterpret_cast<const float *>(sl + 64 * 32)[c];
+      const bool ok = t0 + s < n_tiles && S.rrow[s] >= 0 && mt != kNegInf;
+      prow[s] = ok ? S.rrow[s] : kPvRows;
+      pmt[s] = ok ? mt : 0.f;
+      plt[s] = p == 0 && ok ? reinterpret_cast<const float *>(sl + 64 * 32)[16 + c] : 0.f;
+    }
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          f32x4_t oa = {0.f, 0.f, 0.f, 0.f};
-          oa = mfma16(S.vq[s][mq][0], pbs[s][0], oa);
-          oa = mfma16(S.vq[s][mq][1], pbs[s][1], oa);
-          o[s][mq] = oa;
-        }
-        lts[s] = 0.f;
-        if (p == 0) {   // row sums of P from an all-ones V^T tile
-          f32x4_t la = {0.f, 0.f, 0.f, 0.f};
-          la = mfma16(ones, pbs[s][0], la);
-          la = mfma16(ones, pbs[s][1], la);
-          lts[s] = la[0];
-        }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        f32x4_t oa = {0.f, 0.f, 0.f, 0.f};
+        oa = mfma16(S.vq[s][mq][0], pbs[s][0], oa);
+        oa = mfma16(S.vq[s][mq][1], pbs[s][1], oa);
+        po[s][mq] = oa;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // V^T quarters and rows two rounds on, in flight during this round's
-      // folds and the whole next round
-      load_round(S, t0 + 2 * kPvWaves);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int row = rows[s];
-        const float mt = mts[s];
-        if (row >= 0 && mt != kNegInf) {
-          const float mo = mown[row];
-          const float mn = fmaxf(mo, mt);
-          const float ca = fast_exp2(mo - mn), cb = fast_exp2(mt - mn);
-#pragma unroll
-          for (int mq = 0; mq < MQ; ++mq) {
-            f32x4_t *ap = reinterpret_cast<f32x4_t *>(acc + acc_at<D>(row, (QF * p + 16 * mq + 4 * g) / 4));
-            const f32x4_t av = *ap;
-            f32x4_t nv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) nv[r] = av[r] * ca + o[s][mq][r] * cb;
-            *ap = nv;
-          }
-          if (g == 0) {
-            mown[row] = mn;
-            if (p == 0) lrun[row] = lrun[row] * ca + lts[s] * cb;
-          }
-        }
-      }
-      lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // the next round's V^T quarters and rows, in flight during its phase 1
+    load_round(S, t0 + kPvWaves);
+    lds_barrier();
   };
 
-  // an even number of rounds (a last empty round computes nothing), so both
-  // sets take part in every loop trip
-  const int rounds = 2 * ((n_tiles + 2 * kPvWaves - 1) / (2 * kPvWaves));
-  Set A, Bs;
+  const int rounds = (n_tiles + kPvWaves - 1) / kPvWaves;
+  Set A;
   if (n_tiles > 0) {
     load_own(A, min(p, n_tiles - 1));
     load_round(A, 0);
-    load_own(Bs, min(kPvWaves + p, n_tiles - 1));
-    load_round(Bs, kPvWaves);
   }
-  for (int rd = 0; rd < rounds; rd += 2) {
-    round(A, rd);
-    round(Bs, rd + 1);
-  }
+  for (int rd = 0; rd < rounds; ++rd) round(A, rd);
+  fold();
   __syncthreads();
   // ---- epilogue: O = N / D in bf16 (16 lanes per row), lse
   for (int i = tid; i < NR * (D / 8); i += kPvThreads) {

@@ -129,17 +129,19 @@ hipError_t launch_attn(const PisaDims &dm, const void *Q, const void *K, const v
 // their kept sets into per-block row lists and accumulates every row's
 // output in LDS; the workspace holds K and V^T of every 64-key unit in MFMA
 // fragment order, 4 B Hkv n_blk block d bytes.  The LDS layout depends on the problem:
-//   acc    fp32 [kPivotRows][d] output accumulators (the set-up's bitmaps
-//          [32 words][kPivotRows] and four int[1024] block arrays overlay it)
-//   ml     fp32 running maxima, one copy per wave [4][kPivotRows], and the
-//          running sums [kPivotRows]
-//   px     four tile slots: P^T fragments (64 lanes x 32 bytes) and the 16
-//          row maxima
+//   acc    fp32 [kPivotRows + 1][d] output accumulators, the last row a
+//          dummy target (the set-up's bitmaps [32 words][kPivotRows] and four
+//          int[1024] block arrays overlay it)
+//   ml     fp32 running maxima, one copy per wave [4][kPivotRows + 1], and
+//          the running sums [kPivotRows + 1]
+//   px     four tile slots of kPivotSlotBytes: P^T fragments (64 lanes x 32
+//          bytes), the 16 row maxima and the 16 row sums
 //   bkt    u8 row ids of the per-block lists, ent_cap entries
 //   til    u32 tiles, tile_cap entries
 //   small  int[4]: list entries, tiles
 constexpr int kPivotRows = 256;
 constexpr int kPivotLdsMax = 160 * 1024;
+constexpr int kPivotSlotBytes = 64 * 32 + 32 * 4;
 struct PivotLds {
   int acc, ml, px, bkt, til, small, total;
   int ent_cap, tile_cap;
@@ -157,9 +159,9 @@ inline PivotLds pivot_lds(const PisaDims &dm) {
   const int used = dm.n_blk < y.ent_cap ? dm.n_blk : y.ent_cap;   // blocks with a non-empty list
   y.tile_cap = nh * (y.ent_cap / 16 + used);
   y.acc = 0;
-  y.ml = kPivotRows * dm.d * 4;
-  y.px = y.ml + 5 * kPivotRows * 4;
-  y.bkt = y.px + 4 * (64 * 32 + 16 * 4);
+  y.ml = (kPivotRows + 1) * dm.d * 4;                 // one dummy row
+  y.px = y.ml + ((5 * (kPivotRows + 1) * 4 + 15) & ~15);
+  y.bkt = y.px + 4 * kPivotSlotBytes;
   y.til = y.bkt + ((y.ent_cap + 15) & ~15);
   y.small = y.til + y.tile_cap * 4;
   y.total = y.small + 16;
