@@ -91,6 +91,46 @@ def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
                                         taylor_pairs=taylor_pairs).items()}
 
 
+def pivot_executed(knobs: dict, idx: np.ndarray, flop_exact: int) -> dict:
+    """Executed MFMA FLOPs of the key-gathered PIVOT kernel and u = executed /
+    algorithmic exact FLOPs.  A workgroup pools 256 rows (256 / (Hq / Hkv)
+    tokens x the query heads of one kv head); every block one of its rows
+    keeps becomes ceil(rows keeping it / 16) tiles per 64-key half, and a tile
+    runs 16 rows x 64 keys through S = Q K^T and O = P V (4 d FLOPs a pair)."""
+    B, Hq, Hkv, L, d, bs = (knobs[k] for k in ("B", "Hq", "Hkv", "L", "d", "block"))
+    causal, window = knobs["causal"], knobs["window"]
+    n_blk = -(-L // bs)
+    R = Hq // Hkv
+    TT = 256 // R
+    n_pool = -(-L // TT)
+    t = np.arange(L)
+    own = t // bs
+    if causal:
+        lo = (np.maximum(0, t - window + 1) // bs) if window > 0 else own
+        nc = lo
+    else:
+        lo, nc = np.full(L, n_blk), np.full(L, n_blk)
+    pool = t // TT
+    tiles = 0
+    for b in range(B):
+        for hk in range(Hkv):
+            keys = []
+            for h in range(hk * R, hk * R + R):
+                lst = np.sort(idx[b, h], axis=1)                         # [L, k]
+                ok = (lst >= 0) & (lst < nc[:, None])
+                ok[:, 1:] &= lst[:, 1:] != lst[:, :-1]                   # a repeated entry counts once
+                keys.append((pool[:, None] * n_blk + lst)[ok])
+                if causal:                                               # the range [lo, own]
+                    for off in range(int((own - lo).max()) + 1):
+                        j = lo + off
+                        m = j <= own
+                        keys.append(pool[m] * n_blk + j[m])
+            cnt = np.bincount(np.concatenate(keys), minlength=n_pool * n_blk)
+            tiles += int(((cnt + 15) // 16).sum()) * (bs // 64)
+    executed = tiles * 16 * 64 * 4 * d
+    return {"tiles": tiles, "flop_executed": executed, "u": round(executed / max(flop_exact, 1), 3)}
+
+
 def cpu_baseline(wl, q, k, v, budget_s: float) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the same
     workload: block statistics and selection for query head 0 of batch 0
@@ -370,6 +410,8 @@ def main():
     lse = torch.empty((wl.B, wl.Hq, wl.L), dtype=torch.float32, device="cuda")
     ws_need = pisa.workspace_size(p, 0)
     ws = torch.empty(max(ws_need, 16), dtype=torch.uint8, device="cuda")
+    ws_attn_need = pisa.workspace_size(p, 2)   # key-gathered PIVOT: K, V^T in fragment order
+    ws_attn = torch.empty(max(ws_attn_need, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -381,7 +423,7 @@ def main():
         pisa.indexer_topk(p, dq, st, idx, None, want_cand=False)
         if ev:
             ev[2].record(stream)
-        pisa.sparse_attn_fwd(p, dq, dk, dv, st, idx, out, lse)
+        pisa.sparse_attn_fwd(p, dq, dk, dv, st, idx, out, lse, ws=ws_attn)
         if ev:
             ev[3].record(stream)
 
@@ -436,7 +478,8 @@ def main():
         torch.cuda.empty_cache()
         extras["peaks"] = measured_peaks(torch, pisa)
 
-    work = algorithmic_work(knobs, idx.cpu().numpy())
+    idx_host = idx.cpu().numpy()
+    work = algorithmic_work(knobs, idx_host)
     # bf16 runs on the matrix cores; the fp32 path is plain fp32 FMA on the
     # VALU (no packed fp32): 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz
     peak_kind, peak = ("mfma", PEAK_BF16_TFLOPS) if wl.dtype == "bf16" else ("alu", PEAK_F32_VALU_TFLOPS)
@@ -480,6 +523,8 @@ def main():
         },
         "host": {"cpu_model": cpu_model(), "cpus": len(os.sched_getaffinity(0))},
     }
+    if ws_attn_need:
+        line["kernels"]["sparse_attn_fwd"]["executed"] = pivot_executed(knobs, idx_host, work["flop_exact"])
     names = ("block_stats", "indexer_topk", "sparse_attn_fwd")
     if extras:
         for c, nm in enumerate(names):

@@ -29,7 +29,9 @@
 //     uses; per-row masks handle PIVOT rows whose lists differ within a wave;
 //   * row maxima move only when a logit exceeds them by more than 2^8, so the
 //     output accumulators (MFMA-only registers) are rarely rescaled.
-#include "attn_common.h"
+#include "attn_tiles.h"
+
+using namespace pisa_attn;
 
 namespace {
 
@@ -37,22 +39,6 @@ constexpr int kStage = 64;       // keys per pipeline stage
 constexpr int kTyBatch = 32;     // Taylor blocks per logits batch
 constexpr float kRescale = 8.f;  // lazy max threshold (log2 units)
 constexpr int kRingKV = 4, kRingH = 3;
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void glb_void_t;
-
-// wait until at most N vector-memory loads of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14)
-template <int N>
-PISA_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-PISA_DEV void dma16(const void *src, uint8_t *lds_chunk) {
-  __builtin_amdgcn_global_load_lds((glb_void_t *)src, (lds_void_t *)lds_chunk, 16, 0, 0);
-}
 
 // A tile of R rows x D bf16 into LDS, row-major, 16-byte chunks XOR-swizzled:
 // SWZ 0: chunk ^ (row & 7)  (rows read with ds_read_b128 by 8-row lane groups)
@@ -100,18 +86,8 @@ struct Lay {
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-PISA_DEV u32x4_t pack8(const f32x16_t &v, int off) {
-  u32x4_t w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[off + 2 * i], v[off + 2 * i + 1]);
-  return w;
-}
-
-PISA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Sigma^T tile [D][32 entries]: entry e sits at position perm16 within its
 // group of 16 so the alpha accumulator layout is the MFMA B operand as is.
-PISA_DEV int perm16(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 PISA_DEV u32x4_t frag_st(const uint8_t *base, int e, int ch) {
   const int phys = ch ^ ((e >> 1) & 3);
   return *reinterpret_cast<const u32x4_t *>(base + e * 64 + (phys << 4));
