@@ -461,8 +461,8 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
 //   3. each member's top-k of its proxy's list: MFMA of the gathered list
 //      rows against up to 8 member queries, then the same selection.
 // Selection of one row by one wave, in three tiers:
-//   fast    keys ord(fp32 score); the n-th largest key found by radix
-//           select over 7-bit digits in a per-wave LDS histogram (radix32);
+//   fast    keys ord(fp32 score); the n-th largest key found by bisection
+//           over the key bits with ballot counts (bisect32);
 //           the set is accepted when it is certified: every kept
 //           lower bound s - e exceeds every dropped upper bound s + e, with
 //           e = D 2^-22 |p| |k| + 2^-110 (see pivot_bound below);
@@ -532,72 +532,41 @@ PISA_DEV uint32_t wave_ureduce_xl(uint32_t v) {
   return op(r32[0], r32[1]);
 }
 
-// Largest threshold t with at least `need` keys >= t, by radix select: 7-bit
-// digits counted in a 128-bin LDS histogram of this wave (hist), starting
-// below the bits every candidate key shares, and stopping as soon as the bin
-// that holds the boundary holds exactly the keys still to take.  Keys of 0
-// (invalid slots) are no candidates; slots s >= nsl (uniform) hold none.
-// Returns true with t such that exactly `need` keys are >= t (the top set is
-// unique at 32 bits), false when keys tie across the boundary at 32 bits or
-// fewer than `need` candidates exist.
+// Largest threshold t with at least `need` keys >= t, by bisection over the
+// 32 key bits: each step counts the keys at or above a trial threshold with
+// one ballot per slot (no LDS, no cross-lane scan), and stops as soon as the
+// count is exactly `need`.  Keys of 0 (invalid slots) are no candidates;
+// slots s >= nsl (uniform) hold none.  Returns true with t such that exactly
+// `need` keys are >= t (the top set is unique at 32 bits), false when keys tie
+// across the boundary at 32 bits or fewer than `need` candidates exist.
 template <int NS>
-PISA_DEV bool radix32(const uint32_t (&key)[NS], int nsl, int need, uint32_t &t, uint32_t *hist) {
-  const int l = lane_id();
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < nsl && key[s] != 0u) {
-      kmax = key[s] > kmax ? key[s] : kmax;
-      kmin = key[s] < kmin ? key[s] : kmin;
-    }
-  kmax = wave_ureduce_xl<true>(kmax);
-  kmin = wave_ureduce_xl<false>(kmin);
-  const uint32_t diff = kmax ^ kmin;
-  int hi = diff ? 32 - __builtin_clz(diff) : 1;   // bits >= hi are shared by every key
-  uint32_t prefix = hi >= 32 ? 0u : (kmax >> hi) << hi;
-  for (;;) {
-    const int width = hi < 7 ? hi : 7, lo = hi - width;
-    hist[2 * l] = 0u;
-    hist[2 * l + 1] = 0u;
-    wave_lds_sync();
+PISA_DEV bool bisect32(const uint32_t (&key)[NS], int nsl, int need, uint32_t &t) {
+  t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int cnt = 0;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      if (s < nsl && key[s] != 0u && (hi >= 32 || (key[s] >> hi) == (prefix >> hi)))
-        atomicAdd(&hist[(key[s] >> lo) & ((1u << width) - 1u)], 1u);
-    wave_lds_sync();
-    // bins from the top: lane l holds bins 127 - 2 l and 126 - 2 l
-    const int h0 = (int)hist[127 - 2 * l], h1 = (int)hist[126 - 2 * l];
-    const int incl = wave_incl_scan(h0 + h1);
-    const int excl = incl - h0 - h1;
-    const uint64_t bal = ballot64(excl < need && need <= incl);
-    if (!bal) return false;   // fewer candidates than need
-    const int owner = __builtin_amdgcn_readfirstlane(__builtin_ffsll((long long)bal) - 1);
-    const bool first = excl + h0 >= need;
-    const int bin = __builtin_amdgcn_readlane(first ? 127 - 2 * l : 126 - 2 * l, owner);
-    const int above = __builtin_amdgcn_readlane(first ? excl : excl + h0, owner);
-    const int hb = __builtin_amdgcn_readlane(first ? h0 : h1, owner);
-    wave_lds_sync();   // every lane has read the bins before the next round clears them
-    need -= above;
-    prefix |= (uint32_t)bin << lo;
-    if (hb == need) {   // this bin's keys all in, every lower key out
-      t = prefix;
-      return true;
+      if (s < nsl) cnt += __builtin_popcountll(ballot64(key[s] >= c));
+    if (cnt >= need) {
+      t = c;
+      if (cnt == need) return true;
     }
-    if (lo == 0) return false;   // keys equal to prefix straddle the boundary
-    hi = lo;
   }
+  // t is the largest threshold with at least need keys >= t: more than need
+  // (keys equal to t straddle the boundary), or t = 0 with too few keys
+  return false;
 }
 
 // Fast tier: select the `need` best of fp32 scores sc (bounds dl) and certify.
-// hist: 128 words of LDS of this wave, free while the tier runs.
 template <int NS>
 PISA_DEV bool fast_select(const float (&sc)[NS], const float (&dl)[NS], const bool (&valid)[NS], int nsl,
-                          int need, bool (&sel)[NS], uint32_t *hist) {
+                          int need, bool (&sel)[NS]) {
   uint32_t key[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) key[s] = valid[s] ? ord32(sc[s]) : 0u;
   uint32_t t;
-  if (!radix32<NS>(key, nsl, need, t, hist)) return false;
+  if (!bisect32<NS>(key, nsl, need, t)) return false;
   float t_out = -__builtin_huge_valf();
   bool bad = false;
 #pragma unroll
@@ -656,6 +625,41 @@ PISA_DEV void provisional64(const double (&sc)[NS], const bool (&valid)[NS], int
   }
 }
 
+// Provisional top `need` of the same scores on 32-bit keys (the float
+// rounding of the float64 score): bisection over the key bits, keys equal at
+// the threshold taken in slot order.  Any set of `need` works as a provisional
+// set: the float64 bounds decide which candidates stay undecided.
+template <int NS>
+PISA_DEV void provisional32(const double (&sc)[NS], const bool (&valid)[NS], int need, bool (&sel)[NS]) {
+  const int l = lane_id();
+  uint32_t key[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) key[s] = valid[s] ? ord32((float)sc[s]) : 0u;
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) cnt += __builtin_popcountll(ballot64(valid[s] && key[s] >= c));
+    if (cnt >= need) {
+      t = c;
+      if (cnt == need) break;
+    }
+  }
+  int above = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) above += __builtin_popcountll(ballot64(valid[s] && key[s] > t));
+  const int rem = need - above;
+  const uint64_t lt = (1ull << l) - 1;
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint64_t tie = ballot64(valid[s] && key[s] == t);
+    sel[s] = valid[s] && (key[s] > t || (key[s] == t && base + __builtin_popcountll(tie & lt) < rem));
+    base += __builtin_popcountll(tie);
+  }
+}
+
 // Lowest kept lower bound and highest dropped upper bound (float64); false
 // if any bound is not finite.
 template <int NS>
@@ -676,25 +680,37 @@ PISA_DEV bool bounds64(const double (&sc)[NS], const double (&dl)[NS], const boo
   return ballot64(bad) == 0;
 }
 
-// float64 score of row vector p (fp32 copy in LDS) against ksel row kr, by
-// the whole wave: exact products, a float64 tree sum; *bound receives a
-// rigorous bound on its error (depth 8 tree, doubled).
+// float64 score p . k of one candidate row by one lane (features in order,
+// p from LDS, the row's 16-byte chunks loaded together) and a bound on its
+// rounding: the products are exact in float64, so the error is that of D - 1
+// sequential additions, at most (D - 1) 2^-53 sum |x| (first order; D + 2
+// covers the rest and the rounding of the sum of |x| itself).
 template <int D>
-PISA_DEV double rescore64(const float *p, const uint16_t *kr, double *bound) {
-  const int l = lane_id();
-  double s = 0.0, a = 0.0;
-  for (int c = l; c < D; c += 64) {
-    const double x = (double)p[c] * (double)bf16_to_f32(kr[c]);
-    s += x;
-    a += fabs(x);
-  }
+PISA_DEV double rescore64_lane(const float *p, const uint16_t *kr, double *bound) {
+  u32x4_t kk[D / 8];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    s += __shfl_xor(s, o);
-    a += __shfl_xor(a, o);
-  }
-  *bound = 16.0 * 0x1p-53 * a + 0x1p-1000;
+  for (int c = 0; c < D / 8; ++c) kk[c] = *reinterpret_cast<const u32x4_t *>(kr + 8 * c);
+  double s = 0.0, a = 0.0;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double x0 = (double)p[8 * c + 2 * i] * (double)bf16lo(kk[c][i]);
+      const double x1 = (double)p[8 * c + 2 * i + 1] * (double)bf16hi(kk[c][i]);
+      s += x0;
+      a += fabs(x0);
+      s += x1;
+      a += fabs(x1);
+    }
+  *bound = (double)(D + 2) * 0x1p-53 * a + 0x1p-1000;
   return s;
+}
+
+PISA_DEV double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // ids of the selected slots, ascending, to LDS (uint16) and optionally to
@@ -759,28 +775,104 @@ __device__ __attribute__((noinline)) bool rescore_select(const float *srow, cons
 #pragma unroll
   for (int s = 0; s < NS; ++s) add_route(s);
   load_vec_f32<D>(pv, vec);
-  provisional64<NS>(sc, valid, n_take, sel);
+  provisional32<NS>(sc, valid, n_take, sel);
   double t_in, t_out;
   bounds64<NS>(sc, dl, valid, sel, t_in, t_out);
   // undecided: kept ones not above every dropped bound and vice versa (a
-  // non-finite bound counts as undecided)
+  // non-finite bound counts as undecided).  A kept candidate that is not
+  // undecided is above every dropped one, so it is in the top set; a dropped
+  // one that is not undecided is below every kept one, so it is out.  Only
+  // the undecided are ranked again, among themselves, on float64 scores
+  // computed side by side: undecided candidate k (in slot, lane order) on
+  // lane k % 64.
+  bool amb[NS];
+  uint64_t ambm[NS];
+  int namb = 0, n_in = 0;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const double lo = sc[s] - dl[s], hi = sc[s] + dl[s];
-    const bool amb = valid[s] && (sel[s] ? !(lo > t_out) : !(hi < t_in));
-    uint64_t m = ballot64(amb);
-    while (m) {
-      const int lb = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int j = __builtin_amdgcn_readlane(cj[s], lb);
-      double bnd;
-      const double v = rescore64<D>(pv, kbase + (size_t)j * D, &bnd);
-      if (l == lb) {
-        sc[s] = v;
-        dl[s] = bnd;
+    amb[s] = valid[s] && (sel[s] ? !(lo > t_out) : !(hi < t_in));
+    ambm[s] = ballot64(amb[s]);
+    namb += __popcll(ambm[s]);
+    n_in += __popcll(ballot64(valid[s] && sel[s] && !amb[s]));
+  }
+  auto score_undecided = [&](int k0, double &v, double &bnd) -> int {
+    int myj = -1, k = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      for (uint64_t m = ambm[s]; m; m &= m - 1, ++k) {
+        const int lb = __ffsll((unsigned long long)m) - 1;
+        if (k >= k0 && k < k0 + 64) {
+          const int j = __builtin_amdgcn_readlane(cj[s], lb);
+          if (l == k - k0) myj = j;
+        }
+      }
+    v = 0.0;
+    bnd = 0.0;
+    if (myj >= 0) {
+      v = rescore64_lane<D>(pv, kbase + (size_t)myj * D, &bnd);
+      if (mc) {   // as add_route
+        v += (double)lam * (double)mc[myj];
+        bnd += 0x1p-52 * fabs(v);
       }
     }
-    if (amb) add_route(s);
+    return myj;
+  };
+  if (namb <= 64) {
+    double v, bnd;
+    const bool act = score_undecided(0, v, bnd) >= 0;
+    // the need2 best of the undecided by float64 score, certified among them
+    const int need2 = n_take - n_in;
+    const uint64_t key = act ? ord64(v) : 0ull;
+    uint64_t t = 0;
+    bool found = need2 <= 0;
+    if (!found)
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t c = t | (1ull << bit);
+        const int cnt = __popcll(ballot64(act && key >= c));
+        if (cnt >= need2) {
+          t = c;
+          if (cnt == need2) {
+            found = true;
+            break;
+          }
+        }
+      }
+    if (!found) return false;   // equal float64 scores across the boundary
+    const bool ch = act && need2 > 0 && key >= t;
+    const double lo = v - bnd, hi = v + bnd;
+    const bool bad = act && !(__builtin_isfinite(lo) && __builtin_isfinite(hi));
+    const double lo_in = wave_min_f64(ch ? lo : __builtin_huge_val());
+    const double hi_out = wave_max_f64(act && !ch ? hi : -__builtin_huge_val());
+    if (ballot64(bad) != 0 || !(lo_in > hi_out)) return false;
+    int k = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      for (uint64_t m = ambm[s]; m; m &= m - 1, ++k) {
+        const int lb = __ffsll((unsigned long long)m) - 1;
+        const int c = __builtin_amdgcn_readlane(ch ? 1 : 0, k);
+        if (l == lb) sel[s] = c != 0;
+      }
+    write_sorted_lds<NS>(sel, cj, lout, gout, len);
+    return true;
+  }
+  // many undecided: rescore them all, select the row again on float64 keys
+  for (int k0 = 0; k0 < namb; k0 += 64) {
+    double v, bnd;
+    score_undecided(k0, v, bnd);
+    int k = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      for (uint64_t m = ambm[s]; m; m &= m - 1, ++k) {
+        const int lb = __ffsll((unsigned long long)m) - 1;
+        if (k >= k0 && k < k0 + 64) {
+          const double vv = readlane_f64(v, k - k0), bb = readlane_f64(bnd, k - k0);
+          if (l == lb) {
+            sc[s] = vv;
+            dl[s] = bb;
+          }
+        }
+      }
   }
   provisional64<NS>(sc, valid, n_take, sel);
   if (!bounds64<NS>(sc, dl, valid, sel, t_in, t_out) || !(t_in > t_out)) return false;
@@ -944,7 +1036,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
           dl[s] = fmaf(0x1p-22f, fabsf(sc[s]), dl[s]);
         }
       }
-      if (fast_select<NS>(sc, dl, valid, nsl, C, sel, reinterpret_cast<uint32_t *>(PVw))) {
+      if (fast_select<NS>(sc, dl, valid, nsl, C, sel)) {
         write_sorted_lds<NS>(sel, cid, lout, gout, dm.n_cand);
       } else {
         const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
@@ -1069,7 +1161,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         }
         int ct;
         int32_t *out = member_row(qrow0, t, ct);
-        if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel, reinterpret_cast<uint32_t *>(PVw))) {
+        if (fast_select<NS>(sc, dl, valid, nsl, n_take, sel)) {
           write_sorted_lds<NS>(sel, cj, nullptr, out, dm.klist - ct);
         } else if (!rescore_select<D, NS>(Mw + m * LY::MLD, list, 0, C, n_take, cb, SKN, route ? MC : nullptr, lam,
                                           Q + (qrow0 + t) * D, PVw, kbase, nullptr, out, dm.klist - ct, diag) &&
