@@ -25,8 +25,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12   # fp32 FMA on the VALU, not packed: 78.6
 # source of the attention kernel that runs for block rows (True) / PIVOT rows
-ATTN_SRC = {True: os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn_blocks.hip"),
-            False: os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn.hip")}
+ATTN_SRC = {"blocks": os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn_blocks.hip"),
+            "pivot_union": os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn.hip"),
+            "pivot_kg": os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn_pivot.hip")}
 
 
 def algorithmic_work(knobs: dict, idx: np.ndarray) -> dict:
@@ -509,7 +510,9 @@ def main():
         "roofline": {"bound": peak_kind, "kernel": "pisa_sparse_attn_fwd",
                      "achieved": round(attn_achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / peak, 4),
-                     "traffic": hbm_traffic(ATTN_SRC[wl.group == 0], wl.name) if wl.dtype == "bf16" else None},
+                     "traffic": hbm_traffic(ATTN_SRC["blocks" if wl.group == 0 else
+                                                     "pivot_kg" if ws_attn_need else "pivot_union"], wl.name)
+                     if wl.dtype == "bf16" else None},
         "kernels": {
             "block_stats": {"ms": round(ms_stats, 4), "bytes": work["stats_bytes"], "GB/s": round(stats_gbs, 1),
                             "hbm_frac": round(stats_gbs / PEAK_HBM_GBS, 4)},
