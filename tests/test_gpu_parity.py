@@ -86,6 +86,11 @@ def test_parity_cases(name):
     dict(L=1300, block=128, topk=2, group=8, n_cand=5, causal=True, taylor="none", d=64, Hq=2, Hkv=2),
     dict(L=700, block=64, topk=3, group=2, n_cand=6, causal=False, taylor="none", Hq=4, Hkv=2),
     dict(L=1100, block=64, topk=5, group=8, n_cand=5, causal=True, window=64, taylor="none", Hq=4, Hkv=2, sink=1),
+    # pools of 32 tokens at d 64 (GQA 8), of 256 tokens (one query head per
+    # kv head, 128-token blocks, a window), and a sequence shorter than one pool
+    dict(L=700, block=64, topk=3, group=4, n_cand=6, causal=True, taylor="none", d=64, Hq=8, Hkv=1),
+    dict(L=1500, block=128, topk=2, group=8, n_cand=4, causal=True, window=300, taylor="none", Hq=2, Hkv=2),
+    dict(L=100, block=64, topk=1, group=4, n_cand=2, causal=True, taylor="none", Hq=4, Hkv=1),
     # d 64 first order takes four Taylor entries per barrier: two batches of
     # entries, the last group short
     dict(L=1500, block=64, topk=2, d=64, taylor="order1"),
