@@ -365,6 +365,9 @@ def main():
     ap.add_argument("--taylor", default=None, choices=["none", "order0", "order1", "hybrid"],
                     help="run the workload with another treatment of the non-kept blocks "
                          "(reported as workload <name>_<mode>)")
+    ap.add_argument("--topk", type=int, default=None,
+                    help="run the workload with another top-k (reported as workload <name>_k<topk>); "
+                         "topk >= the block count keeps every block: dense attention through the sparse kernel")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -400,6 +403,8 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.taylor and args.taylor != wl.taylor:
         wl = wl.replace(name=f"{wl.name}_{args.taylor}", taylor=args.taylor)
+    if args.topk is not None and args.topk != wl.topk:
+        wl = wl.replace(name=f"{wl.name}_k{args.topk}", topk=args.topk)
     knobs = wl.knobs()
     print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
     q, k, v = W.make_inputs(wl)

@@ -104,7 +104,7 @@ typedef struct {
   int32_t sink;     /* attention sinks ([SWA] glossary): the first min(sink,
                        |cand_r|) candidate blocks of every row are always kept
                        exactly and head its kept list; the top-k is chosen
-                       among the other candidates.  topk + sink <= 64. */
+                       among the other candidates.  topk + sink <= 256. */
   float route_lambda; /* covariance-aware routing ([PISA] section 2): >= 0;
                        when > 0 every selection score (block rows, PIVOT
                        proxies and members) is the attention score plus

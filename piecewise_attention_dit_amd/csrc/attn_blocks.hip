@@ -46,7 +46,7 @@ constexpr int NT = NW * 64;
 constexpr int ROWS = NW * 32;      // query rows per workgroup
 constexpr int kNB = 16;            // Taylor entries per logits batch
 constexpr float kRescale = 8.f;    // lazy max threshold (log2 units)
-constexpr int kMaxK = 64;          // kept-list capacity per part
+constexpr int kMaxK = 256;         // kept-list capacity per part
 
 template <int D, int BS>
 struct Cfg {
@@ -128,7 +128,9 @@ struct Item {
   bool full;   // no causal or ragged-tail mask needed
 };
 
-template <int D, int BS>
+// LONG: kept lists of more than 64 blocks (entries past 64 read from LDS);
+// shorter lists take the variant without that path.
+template <int D, int BS, bool LONG>
 __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
   using C = Cfg<D, BS>;
   constexpr int P = C::P, WPP = C::WPP, SK = C::SK, SPB = C::SPB, NQT = C::NQT, NE = C::NE;
@@ -286,8 +288,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       offk[u] = (row * D + ((phys ^ kswz<D>(row)) << 3)) * 2;
       offv[u] = (row * D + ((phys ^ vswz<D>(row)) << 3)) * 2;
     }
-    // the block lists live in VGPRs, entry e in lane e; a step reads its
-    // entry with v_readlane
+    // the block lists' first 64 entries live in VGPRs, entry e in lane e; a
+    // step reads its entry with v_readlane (entries past 64, for lists of
+    // more than 64 blocks, from LDS)
     int cnt_s[P], vprv[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -303,14 +306,17 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     // then the shared blocks
     auto key0_one = [&](int s) -> int {
       const int s1 = s - n_w;
-      const int jw = wlo + s / SPB, js = __builtin_amdgcn_readlane(vshl, (s1 / SPB) & 63);
+      const int e = s1 / SPB;
+      const int jw = wlo + s / SPB;
+      const int js = (!LONG || e < 64) ? __builtin_amdgcn_readlane(vshl, e & 63) : (int)shl[e];
       return (s < n_w ? jw * BS + (s % SPB) * SK : js * BS + (s1 % SPB) * SK);
     };
     // ... of part p's sub-tile in a private step (idle parts load block 0,
     // finite data that their zero weights ignore)
-    auto key0_prv = [&](int s, int vlist, int count) -> int {
+    auto key0_prv = [&](int s, int vlist, int count, int p) -> int {
       const int s2 = s - n_one, bi = s2 / SPB;
-      const int j = __builtin_amdgcn_readlane(vlist, bi & 63);
+      const int j = (!LONG || bi < 64) ? __builtin_amdgcn_readlane(vlist, bi & 63)
+                                       : bi < count ? (int)prv[p * kMaxK + bi] : 0;
       return (bi < count ? j : 0) * BS + (s2 % SPB) * SK;
     };
     // K (isv false) or V sub-tiles of step s into the ring slot at byte offset base
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       } else {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const int k0 = key0_prv(s, vprv[p], cnt_s[p]);
+          const int k0 = key0_prv(s, vprv[p], cnt_s[p], p);
 #pragma unroll
           for (int u = 0; u < UPP; ++u)
             dma16_buf(g + (size_t)k0 * D, max(dm.L - k0, 0) * D * 2, isv ? offv[u] : offk[u],
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       Item it;
       const bool win = s < n_w, one = s < n_one;
       const int jw = wlo + s / SPB;
-      it.key0 = one ? key0_one(s) : key0_prv(s, vme, cnt_me);
+      it.key0 = one ? key0_one(s) : key0_prv(s, vme, cnt_me, part);
       it.reg = one ? 0 : part;
       it.mem = win ? (pvalid && jw >= lo && jw <= own) : (one ? pvalid : (s - n_one) / SPB < cnt_me);
       it.full = it.key0 + SK <= dm.L && !(win && causal && jw == own);
@@ -808,8 +814,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
   }
 }
 
-template <int D, int BS>
-hipError_t launch(const AttnArgs &a, hipStream_t st) {
+template <int D, int BS, bool LONG>
+hipError_t launch_v(const AttnArgs &a, hipStream_t st) {
   using C = Cfg<D, BS>;
   const PisaDims &dm = a.dm;
   const int G = dm.ratio < C::P ? dm.ratio : C::P;
@@ -817,13 +823,19 @@ hipError_t launch(const AttnArgs &a, hipStream_t st) {
   const unsigned grid = (unsigned)dm.B * dm.Hkv * (dm.ratio / G) * ((dm.n_blk + TB - 1) / TB);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_blocks<D, BS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_blocks<D, BS, LONG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::TOTAL);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_blocks<D, BS><<<grid, NT, C::TOTAL, st>>>(a);
+  attn_blocks<D, BS, LONG><<<grid, NT, C::TOTAL, st>>>(a);
   return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch(const AttnArgs &a, hipStream_t st) {
+  // the kernels take topk as the width of a kept list (topk + sink)
+  return a.dm.topk > 64 ? launch_v<D, BS, true>(a, st) : launch_v<D, BS, false>(a, st);
 }
 
 }  // namespace

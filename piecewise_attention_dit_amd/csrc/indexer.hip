@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
 // ---------------------------------------------------------------------------
 // PIVOT rows on the matrix cores (bf16, d 64 or 128).
 //
-// A workgroup of 16 waves takes up to 32 proxies that share a KV head and a
+// A workgroup of kPW waves takes up to 32 proxies that share a KV head and a
 // query block (the query heads of the KV head times the groups of the
 // block), so they share the candidate blocks up to their causal limit:
 //   1. proxy scores S[p][j] = qsel_p . ksel_j for all candidates at once on

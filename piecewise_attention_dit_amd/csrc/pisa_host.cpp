@@ -25,7 +25,7 @@ pisa_status fail(pisa_status s, const char *fmt, ...) {
 }
 
 constexpr int kMaxBlocks = 1024;   // candidates per selection row (indexer registers)
-constexpr int kMaxTopk = 64;
+constexpr int kMaxTopk = 256;
 constexpr int kMaxCand = 256;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

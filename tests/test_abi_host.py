@@ -66,9 +66,9 @@ def _p(**kw):
     (dict(route_lambda=0.5, taylor="none"), pisa.PISA_E_ARG),
     (dict(route_lambda=0.5, causal=True), pisa.PISA_E_UNSUPPORTED),      # routing is non-causal only
     (dict(route_lambda=0.5, causal=True, group=8, n_cand=8), pisa.PISA_E_UNSUPPORTED),
-    (dict(topk=40, sink=25), pisa.PISA_E_UNSUPPORTED),
+    (dict(topk=240, sink=25), pisa.PISA_E_UNSUPPORTED),
     (dict(topk=-1), pisa.PISA_E_ARG),
-    (dict(topk=65), pisa.PISA_E_UNSUPPORTED),
+    (dict(topk=257), pisa.PISA_E_UNSUPPORTED),
     (dict(window=64, causal=False), pisa.PISA_E_UNSUPPORTED),
     (dict(group=3, n_cand=8, causal=True), pisa.PISA_E_ARG),    # block % g
     (dict(group=8, n_cand=2, causal=True), pisa.PISA_E_ARG),    # n_cand < topk

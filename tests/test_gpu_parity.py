@@ -91,6 +91,11 @@ def test_parity_cases(name):
     dict(L=700, block=64, topk=3, group=4, n_cand=6, causal=True, taylor="none", d=64, Hq=8, Hkv=1),
     dict(L=1500, block=128, topk=2, group=8, n_cand=4, causal=True, window=300, taylor="none", Hq=2, Hkv=2),
     dict(L=100, block=64, topk=1, group=4, n_cand=2, causal=True, taylor="none", Hq=4, Hkv=1),
+    # kept lists longer than 64 blocks (entries past 64 read from LDS), and
+    # every block kept (the dense case through the sparse kernel)
+    dict(L=64 * 90 - 17, block=64, topk=75, d=64, taylor="order1"),
+    dict(L=128 * 70, block=128, topk=70, d=128, taylor="order1", causal=True, window=300),
+    dict(L=128 * 80, block=128, topk=80, d=128, taylor="order1"),
     # d 64 first order takes four Taylor entries per barrier: two batches of
     # entries, the last group short
     dict(L=1500, block=64, topk=2, d=64, taylor="order1"),
