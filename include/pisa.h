@@ -85,7 +85,7 @@ typedef enum {
 } pisa_taylor;
 
 /* Problem statement.  Supported today: d in {64, 128}; block in {64, 128};
- * 1 <= Hq/Hkv <= 8 with Hq % Hkv == 0; n_blk <= 1024; topk + sink <= 256;
+ * Hq / Hkv in {1, 2, 4, 8}; n_blk <= 1024; topk + sink <= 256;
  * n_cand <= 256. */
 typedef struct {
   int32_t B, Hq, Hkv, L, d;
