@@ -21,6 +21,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["pisa_host.cpp", "stats.hip", "indexer.hip", "attn.hip", "attn_blocks.hip", "attn_f32.hip",
            "decode.hip", "roofline.hip", "attn_pivot.hip"]
 ARCH = "gfx950"
+# sources whose MFMA results are consumed by VALU code right away: let the
+# compiler give MFMAs VGPR destinations instead of AGPRs, which would need a
+# v_accvgpr_read per result register
+VGPR_MFMA = {"attn_pivot.hip"}
 
 
 def _hipcc() -> str:
@@ -36,6 +40,8 @@ def _flags(src: str) -> list[str]:
     if src.endswith(".hip"):
         # never let the compiler form packed fp32 arithmetic (v_pk_*_f32)
         f += ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+        if src in VGPR_MFMA:
+            f += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     else:
         f += ["-x", "hip"]
     return f

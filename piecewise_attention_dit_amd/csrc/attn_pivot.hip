@@ -22,9 +22,14 @@
 //   phase 2  wave p takes the quarter p of the features for all four tiles:
 //            O^T = V^T P^T.  During the next round's phase 1 each tile row
 //            folds into the row's fp32 accumulator in LDS (rescale by the
-//            running maximum), so the folds' LDS latency overlaps that
-//            round's softmax.  The row sums of the bf16 weights come from
-//            phase 1; wave 0 folds them.
+//            running maximum); the softmax of that round's tile runs in
+//            four steps while the folds wait on LDS.  The row sums of the
+//            bf16 weights come from phase 1; wave 0 folds them.
+// With one wave per SIMD every wait is exposed, and a kilobyte load ties up
+// the CU's load path for about 16 cycles, so no round issues its loads in
+// one burst: the next own tile's Q and K go out between the folds, the next
+// round's V^T quarters between the phase-2 MFMAs that free their registers,
+// and the list lookups behind those addresses one phase earlier still.
 // K and V^T come from a copy of every 64-key unit in MFMA fragment order
 // (V^T keys in the order the MFMA takes P^T from the S^T registers): an
 // operand load reads one contiguous kilobyte, where loading a fragment from
@@ -269,48 +274,51 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
   const u32x4_t *KVh = KVF + (size_t)bk * dm.n_blk * NH * 16 * D;
   float *mown = mrun + p * kPvRowsA;
 
-  // Operands of a round, loaded one round ahead: the own tile (phase 1:
-  // block, half, lane's token, Q rows and K) and the round's tiles (phase 2:
-  // lane's row, -1 for none, and V^T of quarter p).
-  struct Set {
+  // A tile as its own-tile wave sees it: block, half, rows, the lane's token
+  // (row c), and where the lane's Q and K loads read.  Q rows are read four
+  // lanes to a row (lane l: row l / 4, bytes 16 (l % 4) of each 64-byte
+  // chunk) and moved to the MFMA layout (lane c + 16 g: row c, chunk g) at use.
+  struct Own {
     Tile ot;
     int ott;
-    u32x4_t qf[KQ], kf[4][KQ];
-    int rrow[4];
-    u32x4_t vq[4][MQ][2];
+    const uint16_t *qp;
+    const u32x4_t *kp;
   };
-  // Q rows are read four lanes to a row (lane l: row l / 4, bytes
-  // 16 (l % 4) of each 64-byte chunk) and moved to the MFMA layout (lane
-  // c + 16 g: row c, chunk g) at use
-  auto load_own = [&](Set &S, int ti) {
-    S.ot = tile_of(til[ti]);
-    const int orow = bkt[S.ot.start + min(c, S.ot.n - 1)];
-    S.ott = T0 + orow % TT;
-    const int qrow = bkt[S.ot.start + min(l >> 2, S.ot.n - 1)];
+  auto own_of = [&](const Tile &ot, int orow, int qrow) {
+    Own o;
+    o.ot = ot;
+    o.ott = T0 + orow % TT;
     const int tq = T0 + qrow % TT, hq = hk * R + qrow / TT;
-#pragma unroll
-    for (int ks = 0; ks < KQ; ++ks)
-      S.qf[ks] =
-          *reinterpret_cast<const u32x4_t *>(Qb + ((size_t)(b * dm.Hq + hq) * dm.L + tq) * D + 32 * ks + 8 * (l & 3));
-    const u32x4_t *kfu = KVh + (size_t)(S.ot.j * NH + S.ot.hh) * 16 * D;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int ks = 0; ks < KQ; ++ks) S.kf[m][ks] = kfu[(m * KQ + ks) * 64 + l];
+    o.qp = Qb + ((size_t)(b * dm.Hq + hq) * dm.L + tq) * D + 8 * (l & 3);
+    o.kp = KVh + (size_t)(ot.j * NH + ot.hh) * 16 * D + l;
+    return o;
   };
-  // Every round issues the same loads in the same order (tiles past the end
-  // of the list load the last tile again and are not used), so the
-  // compiler's wait counts see later loads as younger on every path.
-  auto load_round = [&](Set &S, int t0) {
+  auto own_read = [&](int ti) {
+    const Tile ot = tile_of(til[ti]);
+    return own_of(ot, bkt[ot.start + min(c, ot.n - 1)], bkt[ot.start + min(l >> 2, ot.n - 1)]);
+  };
+  // operands of the current round: the own tile's Q and K (phase 1), the
+  // lane's row of each tile (-1 for none) and V^T quarter p (phase 2)
+  constexpr int NOWN = 5 * KQ;   // loads of an own tile: KQ of Q, 4 KQ of K
+  u32x4_t qf[KQ], kf[4][KQ], vq[4][MQ][2];
+  int rrow[4];
+  auto own_load = [&](const Own &o, int i) {
+    if (i < KQ)
+      qf[i] = *reinterpret_cast<const u32x4_t *>(o.qp + 32 * i);
+    else
+      kf[(i - KQ) / KQ][(i - KQ) % KQ] = o.kp[(i - KQ) * 64];
+  };
+  // rows and V^T quarter of tile t0 + s (tiles past the end of the list
+  // repeat the last one and are not used: every round issues the same loads
+  // in the same order, so the compiler's wait counts see later loads as
+  // younger on every path)
+  auto round_rows = [&](int t0, const uint32_t (&tw)[4], int (&rr)[4], const u32x4_t *(&vp)[4]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const Tile tt = tile_of(til[min(t0 + s, n_tiles - 1)]);
-      S.rrow[s] = t0 + s < n_tiles && c < tt.n ? bkt[tt.start + c] : -1;
-      const u32x4_t *vfu = KVh + (size_t)(tt.j * NH + tt.hh) * 16 * D + 8 * D;
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) S.vq[s][mq][s2] = vfu[((MQ * p + mq) * 2 + s2) * 64 + l];
+      const Tile tt = tile_of(tw[s]);
+      const int r = bkt[tt.start + min(c, tt.n - 1)];
+      rr[s] = c < tt.n ? r : -1;   // tiles past the end: phase 2 drops them
+      vp[s] = KVh + (size_t)(tt.j * NH + tt.hh) * 16 * D + 8 * D + MQ * p * 2 * 64 + l;
     }
   };
   // A round's O^T quarters wait in registers and fold into the accumulators
@@ -324,7 +332,8 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
     for (int mq = 0; mq < MQ; ++mq) po[s][mq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int prow[4] = {kPvRows, kPvRows, kPvRows, kPvRows};
   float pmt[4] = {0.f, 0.f, 0.f, 0.f}, plt[4] = {0.f, 0.f, 0.f, 0.f};
-  auto fold = [&]() {
+  // between(s) runs while the reads of tile s's rows are in flight
+  auto fold = [&](auto &&between) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int row = prow[s];
@@ -338,6 +347,9 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
       }
       const float mo = mown[row];
       const float lo = p == 0 ? lrun[row] : 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+      between(s);
+      __builtin_amdgcn_sched_barrier(0);
       const float mn = fmaxf(mo, pmt[s]);
       const float ca = fast_exp2(mo - mn), cb = fast_exp2(pmt[s] - mn);
 #pragma unroll
@@ -352,7 +364,9 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
       if (p == 0) lrun[row] = lo * ca + plt[s] * cb;
     }
   };
-  auto round = [&](Set &S, int rd) {
+  // own tiles of this round (m0) and the next (m1, loaded during this round)
+  Own m0, m1;
+  auto round = [&](int rd) {
     const int t0 = kPvWaves * rd, ti = t0 + p;
     const bool act = ti < n_tiles;
     uint8_t *slot = px + p * kPivotSlotBytes;
@@ -361,69 +375,89 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
 #pragma unroll
     for (int ks = 0; ks < KQ; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qm[ks][i] = __builtin_amdgcn_ds_bpermute((4 * c + g) << 2, (int)S.qf[ks][i]);
+      for (int i = 0; i < 4; ++i) qm[ks][i] = __builtin_amdgcn_ds_bpermute((4 * c + g) << 2, (int)qf[ks][i]);
+    const int j = m0.ot.j, hh = m0.ot.hh, t = m0.ott;
+    const bool rv = act && c < m0.ot.n;
     // S^T = K Q^T per 16-key tile: lane holds keys 16 m + 4 g + r of row c
     f32x4_t sacc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       f32x4_t sa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KQ; ++ks) sa = mfma16(S.kf[m][ks], qm[ks], sa);
+      for (int ks = 0; ks < KQ; ++ks) sa = mfma16(kf[m][ks], qm[ks], sa);
       sacc[m] = sa;
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int j = S.ot.j, hh = S.ot.hh, t = S.ott;
-    const bool rv = act && c < S.ot.n;
-    // the next round's own tile, in flight during the rest of this round
-    load_own(S, min(ti + kPvWaves, n_tiles - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    fold();
     // masks: the last visible key of the unit is the sequence end or, in the
     // token's own block (causal), the token itself
     const int kbase = j * BS + 64 * hh;
     const bool diag = causal && j == t / BS;
     const int lim = (diag ? t : dm.L - 1) - kbase;
-    float mx = kNegInf;
-    if (ballot64(lim < 63) == 0) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sacc[m][r] *= sl2;
-          mx = fmaxf(mx, sacc[m][r]);
-        }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = 16 * m + 4 * g + r <= lim ? sacc[m][r] * sl2 : kNegInf;
-          sacc[m][r] = x;
-          mx = fmaxf(mx, x);
-        }
-    }
-    mx = pair_max_f(max_xor16(mx));
-    // a row with no visible key in this unit (the future half of its own
-    // 128-key block) folds nothing
-    const bool any = rv && mx != kNegInf;
-    const float mref = mx != kNegInf ? mx : 0.f;
-    // P^T as the B operand of O^T = V^T P^T: K-step s takes the 16-key tiles
-    // 2 s and 2 s + 1; the row sum from the same bf16 weights
+    float mx = kNegInf, mref = 0.f, ls = 0.f;
+    bool any = false;
     u32x4_t pb[2];
-    float ls = 0.f;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    // P^T as the B operand of O^T = V^T P^T: K-step h takes the 16-key tiles
+    // 2 h and 2 h + 1; the row sum from the same bf16 weights
+    auto weights = [&](int h) {
       float e[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        e[r] = fast_exp2(sacc[2 * s][r] - mref);
-        e[4 + r] = fast_exp2(sacc[2 * s + 1][r] - mref);
+        e[r] = fast_exp2(sacc[2 * h][r] - mref);
+        e[4 + r] = fast_exp2(sacc[2 * h + 1][r] - mref);
       }
-      pb[s] = u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+      pb[h] = u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                       pack_bf16x2(e[6], e[7])};
-      ls = sum_bf16x8_f(pb[s], ls);
-    }
-    ls = pair_sum_f(sum_xor16(ls));
+      ls = sum_bf16x8_f(pb[h], ls);
+    };
+    // the softmax in four steps, each while a fold waits on LDS
+    auto softmax_step = [&](int s) {
+      if (s == 0) {
+        if (ballot64(lim < 63) == 0) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sacc[m][r] *= sl2;
+              mx = fmaxf(mx, sacc[m][r]);
+            }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float x = 16 * m + 4 * g + r <= lim ? sacc[m][r] * sl2 : kNegInf;
+              sacc[m][r] = x;
+              mx = fmaxf(mx, x);
+            }
+        }
+      } else if (s == 1) {
+        mx = pair_max_f(max_xor16(mx));
+        // a row with no visible key in this unit (the future half of its
+        // own 128-key block) folds nothing
+        any = rv && mx != kNegInf;
+        mref = mx != kNegInf ? mx : 0.f;
+        weights(0);
+      } else if (s == 2) {
+        weights(1);
+      } else {
+        ls = pair_sum_f(sum_xor16(ls));
+      }
+    };
+    // the next round's tiles: list words now, rows during the folds; the
+    // next own tile's loads and this tile's softmax go between the folds,
+    // while the folds wait on LDS
+    uint32_t tw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) tw[s] = til[min(t0 + kPvWaves + s, n_tiles - 1)];
+    int rrow_n[4];
+    const u32x4_t *vp[4];
+    const Own nx = m1;
+    fold([&](int s) {
+#pragma unroll
+      for (int i = (s * NOWN) / 4; i < ((s + 1) * NOWN) / 4; ++i) own_load(nx, i);
+      if (s == 1) round_rows(t0 + kPvWaves, tw, rrow_n, vp);
+      softmax_step(s);
+    });
     if (act) {
       *reinterpret_cast<u32x4_t *>(slot + l * 32) = pb[0];
       *reinterpret_cast<u32x4_t *>(slot + l * 32 + 16) = pb[1];
@@ -435,41 +469,87 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
     lds_barrier();
     // ================= phase 2: quarter p of the round's tiles; the
     // products wait in registers for the next round's phase 1
+    // every LDS read of the phase first: the slots, and the list word of the
+    // own tile two rounds ahead
     u32x4_t pbs[4][2];
+    float mt[4], lt[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint8_t *sl = px + s * kPivotSlotBytes;
       pbs[s][0] = *reinterpret_cast<const u32x4_t *>(sl + l * 32);
       pbs[s][1] = *reinterpret_cast<const u32x4_t *>(sl + l * 32 + 16);
-      const float mt = reinterpret_cast<const float *>(sl + 64 * 32)[c];
-      const bool ok = t0 + s < n_tiles && S.rrow[s] >= 0 && mt != kNegInf;
-      prow[s] = ok ? S.rrow[s] : kPvRows;
-      pmt[s] = ok ? mt : 0.f;
-      plt[s] = p == 0 && ok ? reinterpret_cast<const float *>(sl + 64 * 32)[16 + c] : 0.f;
+      mt[s] = reinterpret_cast<const float *>(sl + 64 * 32)[c];
+      lt[s] = reinterpret_cast<const float *>(sl + 64 * 32)[16 + c];
+    }
+    const uint32_t tw2 = til[min(ti + 2 * kPvWaves, n_tiles - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bool ok = t0 + s < n_tiles && rrow[s] >= 0 && mt[s] != kNegInf;
+      prow[s] = ok ? rrow[s] : kPvRows;
+      pmt[s] = ok ? mt[s] : 0.f;
+      plt[s] = p == 0 && ok ? lt[s] : 0.f;
+    }
+    // its rows now, its addresses after the products
+    const Tile t2 = tile_of(tw2);
+    const int orow2 = bkt[t2.start + min(c, t2.n - 1)], qrow2 = bkt[t2.start + min(l >> 2, t2.n - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    // the next round's V^T quarters: each pair of loads follows the two
+    // MFMAs that free its registers
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        o = mfma16(vq[s][mq][0], pbs[s][0], o);
+        o = mfma16(vq[s][mq][1], pbs[s][1], o);
+        po[s][mq] = o;
+        vq[s][mq][0] = vp[s][(2 * mq) * 64];
+        vq[s][mq][1] = vp[s][(2 * mq + 1) * 64];
+      }
+#pragma unroll
+    for (int i = 0; i < 4 * MQ; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const Own m2 = own_of(t2, orow2, qrow2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) rrow[s] = rrow_n[s];
+    m0 = m1;
+    m1 = m2;
+    lds_barrier();
+  };
+
+  const int rounds = (n_tiles + kPvWaves - 1) / kPvWaves;
+  if (n_tiles > 0) {
+    m0 = own_read(min(p, n_tiles - 1));
+    m1 = own_read(min(p + kPvWaves, n_tiles - 1));
+    uint32_t tw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) tw[s] = til[min(s, n_tiles - 1)];
+    const u32x4_t *vp[4];
+    round_rows(0, tw, rrow, vp);
+    // the loads in the order the rounds issue them, so the wait counts at
+    // the top of the loop hold for every round
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NOWN; ++i) {
+      own_load(m0, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int mq = 0; mq < MQ; ++mq) {
-        f32x4_t oa = {0.f, 0.f, 0.f, 0.f};
-        oa = mfma16(S.vq[s][mq][0], pbs[s][0], oa);
-        oa = mfma16(S.vq[s][mq][1], pbs[s][1], oa);
-        po[s][mq] = oa;
+        vq[s][mq][0] = vp[s][(2 * mq) * 64];
+        __builtin_amdgcn_sched_barrier(0);
+        vq[s][mq][1] = vp[s][(2 * mq + 1) * 64];
+        __builtin_amdgcn_sched_barrier(0);
       }
-    __builtin_amdgcn_sched_barrier(0);
-    // the next round's V^T quarters and rows, in flight during its phase 1
-    load_round(S, t0 + kPvWaves);
-    lds_barrier();
-  };
-
-  const int rounds = (n_tiles + kPvWaves - 1) / kPvWaves;
-  Set A;
-  if (n_tiles > 0) {
-    load_own(A, min(p, n_tiles - 1));
-    load_round(A, 0);
   }
-  for (int rd = 0; rd < rounds; ++rd) round(A, rd);
-  fold();
+  for (int rd = 0; rd < rounds; ++rd) round(rd);
+  fold([](int) {});
   __syncthreads();
   // ---- epilogue: O = N / D in bf16 (16 lanes per row), lse
   for (int i = tid; i < NR * (D / 8); i += kPvThreads) {
