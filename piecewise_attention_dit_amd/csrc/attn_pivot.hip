@@ -27,9 +27,9 @@
 //            bf16 weights come from phase 1; wave 0 folds them.
 // With one wave per SIMD every wait is exposed, and a kilobyte load ties up
 // the CU's load path for about 16 cycles, so no round issues its loads in
-// one burst: the next own tile's Q and K go out between the folds, the next
-// round's V^T quarters between the phase-2 MFMAs that free their registers,
-// and the list lookups behind those addresses one phase earlier still.
+// one burst: this round's V^T quarters, then the next own tile's Q and K, go
+// out between the folds of phase 1 (phase 2 issues no loads), and the list
+// lookups behind those addresses come one phase earlier still.
 // K and V^T come from a copy of every 64-key unit in MFMA fragment order
 // (V^T keys in the order the MFMA takes P^T from the S^T registers): an
 // operand load reads one contiguous kilobyte, where loading a fragment from
@@ -366,6 +366,7 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
   };
   // own tiles of this round (m0) and the next (m1, loaded during this round)
   Own m0, m1;
+  const u32x4_t *vpc[4];   // this round's V^T quarters
   auto round = [&](int rd) {
     const int t0 = kPvWaves * rd, ti = t0 + p;
     const bool act = ti < n_tiles;
@@ -450,12 +451,24 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
 #pragma unroll
     for (int s = 0; s < 4; ++s) tw[s] = til[min(t0 + kPvWaves + s, n_tiles - 1)];
     int rrow_n[4];
-    const u32x4_t *vp[4];
+    const u32x4_t *vp_n[4];
     const Own nx = m1;
+    // this round's V^T quarters first (phase 2 takes them), two tiles per
+    // fold; the next own tile's Q and K after them
     fold([&](int s) {
+      if (s < 2) {
 #pragma unroll
-      for (int i = (s * NOWN) / 4; i < ((s + 1) * NOWN) / 4; ++i) own_load(nx, i);
-      if (s == 1) round_rows(t0 + kPvWaves, tw, rrow_n, vp);
+        for (int s2 = 2 * s; s2 < 2 * s + 2; ++s2)
+#pragma unroll
+          for (int mq = 0; mq < MQ; ++mq) {
+            vq[s2][mq][0] = vpc[s2][(2 * mq) * 64];
+            vq[s2][mq][1] = vpc[s2][(2 * mq + 1) * 64];
+          }
+      } else {
+#pragma unroll
+        for (int i = ((s - 2) * NOWN) / 2; i < ((s - 1) * NOWN) / 2; ++i) own_load(nx, i);
+      }
+      if (s == 1) round_rows(t0 + kPvWaves, tw, rrow_n, vp_n);
       softmax_step(s);
     });
     if (act) {
@@ -494,8 +507,7 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
     const Tile t2 = tile_of(tw2);
     const int orow2 = bkt[t2.start + min(c, t2.n - 1)], qrow2 = bkt[t2.start + min(l >> 2, t2.n - 1)];
     __builtin_amdgcn_sched_barrier(0);
-    // the next round's V^T quarters: each pair of loads follows the two
-    // MFMAs that free its registers
+    // O^T quarter p of each tile (no loads in this phase)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -504,18 +516,14 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
         o = mfma16(vq[s][mq][0], pbs[s][0], o);
         o = mfma16(vq[s][mq][1], pbs[s][1], o);
         po[s][mq] = o;
-        vq[s][mq][0] = vp[s][(2 * mq) * 64];
-        vq[s][mq][1] = vp[s][(2 * mq + 1) * 64];
       }
-#pragma unroll
-    for (int i = 0; i < 4 * MQ; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
-    }
     __builtin_amdgcn_sched_barrier(0);
     const Own m2 = own_of(t2, orow2, qrow2);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) rrow[s] = rrow_n[s];
+    for (int s = 0; s < 4; ++s) {
+      rrow[s] = rrow_n[s];
+      vpc[s] = vp_n[s];
+    }
     m0 = m1;
     m1 = m2;
     lds_barrier();
@@ -528,8 +536,7 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
     uint32_t tw[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) tw[s] = til[min(s, n_tiles - 1)];
-    const u32x4_t *vp[4];
-    round_rows(0, tw, rrow, vp);
+    round_rows(0, tw, rrow, vpc);
     // the loads in the order the rounds issue them, so the wait counts at
     // the top of the loop hold for every round
     __builtin_amdgcn_sched_barrier(0);
@@ -538,15 +545,6 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
       own_load(m0, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
-        vq[s][mq][0] = vp[s][(2 * mq) * 64];
-        __builtin_amdgcn_sched_barrier(0);
-        vq[s][mq][1] = vp[s][(2 * mq + 1) * 64];
-        __builtin_amdgcn_sched_barrier(0);
-      }
   }
   for (int rd = 0; rd < rounds; ++rd) round(rd);
   fold([](int) {});
