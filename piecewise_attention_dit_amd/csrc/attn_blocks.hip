@@ -622,7 +622,8 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       }
     };
     uint32_t tmask = 0;
-    for (int eg = 0; eg < n_ty; ++eg) {
+    // one Taylor entry (first order), or one batch start (the other orders)
+    auto entry = [&](int eg) {
       const int e = eg % kNB;
       if (e == 0) {
         const int nb = min(kNB, n_ty - eg);
@@ -637,6 +638,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
           lds_barrier();   // the previous batch's tables are consumed; staging landed
           build(eg);
           lds_barrier();
+          // without first order the next batch's rows go to the staging
+          // area now (build read this batch's), to land during this batch
+          if (!order1 && eg + kNB < n_ty) stage(eg + kNB);
         }
         {   // lane en < nb decides entry en for this wave's part
           bool mine = false;
@@ -705,9 +709,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       }
       // the next batch's kbar / vsum rows, about half a batch ahead (this
       // batch's tables were built before the batch-start barrier)
-      const bool staging = e == C::SG * C::GE && eg - e + kNB < n_ty;
+      const bool staging = order1 && e == C::SG * C::GE && eg - e + kNB < n_ty;
       if (staging) stage(eg - e + kNB);
-      if (!order1) continue;
+      if (!order1) return;
       // first order for entry eg: H ring of groups of GE entries, the group
       // in use and AHEAD groups in flight; one barrier per group
       if (e % C::GE == 0) {
@@ -762,6 +766,13 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       // following group's H tiles), this batch's tables were read before the
       // batch's first barrier, and the barrier of group SG + 2 publishes them
       if (e == (C::SG + 1) * C::GE + C::GE - 1 && eg - e + kNB < n_ty) build(eg - e + kNB);
+    };
+    // first order walks the entries one by one; the other orders only have
+    // batch starts, so they step a batch at a time
+    if (order1) {
+      for (int eg = 0; eg < n_ty; ++eg) entry(eg);
+    } else {
+      for (int eg = 0; eg < n_ty; eg += kNB) entry(eg);
     }
     if (hybrid) {   // O^T += (scale sum alpha) Hbar^T Q^T, once per row
       wait_vmcnt<0>();
