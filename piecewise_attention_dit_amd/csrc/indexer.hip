@@ -465,7 +465,7 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
 //           over the key bits with ballot counts (bisect32);
 //           the set is accepted when it is certified: every kept
 //           lower bound s - e exceeds every dropped upper bound s + e, with
-//           e = D 2^-22 |p| |k| + 2^-110 (see pivot_bound below);
+//           e = (d / 4 + 3) 2^-22 |p| |k| + 2^-110 (see pivot_bound below);
 //   re-score  (rare, a function of its own) candidates whose intervals
 //           straddle the threshold get float64 scores with a float64 bound,
 //           the row is selected again on float64 keys and certified;
@@ -481,19 +481,49 @@ constexpr int kPG = 16;        // group size capacity (members per proxy)
 constexpr int kPM = 8;         // members scored per MFMA pass
 
 // Rounding bound of an fp32 score computed by MFMA from bf16 operands.  The
-// products are exact in fp32; a sum of D of them in fp32 (any order, round
-// to nearest or toward zero) is off by at most 2 D 2^-24 sum|p_i k_i| <=
-// D 2^-23 |p| |k|.  The factor used, D 2^-22, is twice that, which also
-// covers the rounding of the norms (fp32 sums of squares, square roots), of
-// the bound's own products and of the subtraction s - e / addition s + e in
-// the certification (each a few units of 2^-24 |p| |k|).  The norms are
-// taken of |x|^2 + 2^-118, so squares that underflow cannot make them too
-// small, and the absolute term 2^-110 covers products and partial sums
-// flushed to zero (at most 2 D 2^-126).
+// products are exact in fp32.  A score is taken as NP = 4 partial sums, each
+// an MFMA 32x32x16 chain over KS / 4 K-steps of 16 products (n = d / 4
+// products), added in fp32 one after the other (mfma32_split).  A
+// sum of n exact products in fp32 (any order, round to nearest or toward
+// zero) is off by at most 2 n 2^-24 sum|p_i k_i|, so each partial errs by at
+// most n 2^-23 of its own sum|p_i k_i|, and each of the NP - 1 additions by
+// at most 2^-23 of the sum of all |p_i k_i|: in all (n + NP - 1) 2^-23
+// sum|p_i k_i| <= (n + NP - 1) 2^-23 |p| |k|.  The factor used,
+// (n + NP - 1) 2^-22, is twice that, which also covers the rounding of the
+// norms (fp32 sums of squares, square roots), of the bound's own products
+// and of the subtraction s - e / addition s + e in the certification (each
+// a few units of 2^-24 |p| |k|).  The norms are taken of |x|^2 + 2^-118, so
+// squares that underflow cannot make them too small, and the absolute term
+// 2^-110 covers products and partial sums flushed to zero (at most
+// 2 d 2^-126).  One chain over all d products would need d 2^-22: at d = 128,
+// 35 against 128 units, and that many times more rows left to the float64
+// tier.  Eight one-step partials (23 units) ran out of registers.
 constexpr float kAbsBound = 0x1p-110f;
 constexpr float kSqFloor = 0x1p-118f;
-template <int D>
-constexpr float pivot_bound() { return (float)D * 0x1p-22f; }
+constexpr int kNP = 4;   // partial sums of a score
+template <int KS>
+constexpr float pivot_bound() { return (float)(16 * KS / kNP + kNP - 1) * 0x1p-22f; }
+
+// A . B over KS K-steps as kNP partial sums (MFMA chains of KS / kNP K-steps
+// of 16 products each), added in fp32 in K-step order
+template <int KS>
+PISA_DEV f32x16_t mfma32_split(const u32x4_t (&a)[KS], const u32x4_t (&b)[KS]) {
+  static_assert(KS % kNP == 0, "whole K-steps per partial sum");
+  constexpr int PK = KS / kNP;
+  f32x16_t part[kNP];
+#pragma unroll
+  for (int q = 0; q < kNP; ++q) {
+    part[q] = f32x16_t{};
+#pragma unroll
+    for (int k = 0; k < PK; ++k) part[q] = mfma32(a[q * PK + k], b[q * PK + k], part[q]);
+  }
+  f32x16_t acc = part[0];
+#pragma unroll
+  for (int q = 1; q < kNP; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += part[q][r];
+  return acc;
+}
 
 struct PivotLayout {
   static constexpr int SLD = kPNc + 4;                 // floats per proxy row of S (padded)
@@ -914,7 +944,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
                                                                  int32_t *__restrict__ cand, int32_t *diag) {
   using LY = PivotLayout;
   constexpr int KS = D / 16;
-  constexpr float kG = pivot_bound<D>();
+  constexpr float kG = pivot_bound<KS>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -985,9 +1015,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
     }
     k2 = pair_sum_f(k2);
     if (hl == 0 && j < kPNc) SKN[j] = sqrtf(k2 + kSqFloor);
-    f32x16_t acc = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], pf[ks], acc);
+    const f32x16_t acc = mfma32_split<KS>(ka, pf);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int j0 = t * 32 + 8 * g4 + 4 * hl;
@@ -1132,9 +1160,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         // keep the gathered row's loads together (otherwise they are issued
         // one at a time, each waited for before its MFMA)
         __builtin_amdgcn_sched_barrier(0);
-        f32x16_t acc = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma32(ka[ks], mq[ks], acc);
+        const f32x16_t acc = mfma32_split<KS>(ka, mq);
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int p0 = ct * 32 + 8 * g4 + 4 * hl;
