@@ -149,7 +149,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16(AttnArgs a) {
   const int tpw = ROWS / hpw;
   const int ntile = (dm.L + tpw - 1) / tpw;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = logical % ntile;
+  // causal rows: the longest tiles (latest tokens) first
+  const int tile = dm.causal ? ntile - 1 - logical % ntile : logical % ntile;
   const int rest = logical / ntile;
   const int grp = rest % ngrp;
   const int bk = rest / ngrp;

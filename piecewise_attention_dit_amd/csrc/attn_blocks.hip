@@ -145,7 +145,9 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
   const int ngrp = dm.ratio / G;
   const int ntile = (dm.n_blk + TB - 1) / TB;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = logical % ntile;
+  // causal rows take longer the later their tokens (more Taylor blocks):
+  // the longest tiles first, so the grid does not end on them
+  const int tile = dm.causal ? ntile - 1 - logical % ntile : logical % ntile;
   const int rest = logical / ntile;
   const int grp = rest % ngrp;
   const int bk = rest / ngrp;

@@ -146,7 +146,9 @@ __global__ __launch_bounds__(kPvThreads, 1) void attn_pivot_kg(AttnArgs a, const
   const int TT = kPvRows / R, NR = R * TT;
   const int ntile = (dm.L + TT - 1) / TT;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = logical % ntile;
+  // causal pools see more blocks the later their tokens: the longest first,
+  // so the grid does not end on them
+  const int tile = dm.causal ? ntile - 1 - logical % ntile : logical % ntile;
   const int bk = logical / ntile;
   const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
   const int T0 = tile * TT;

@@ -380,7 +380,8 @@ __global__ __launch_bounds__(64) void indexer_blockrows(PisaDims dm, const T *__
                                                         int32_t *__restrict__ idx, int32_t *diag) {
   __shared__ Shared sh;
   const int unit = blockIdx.x;
-  const int i = unit % dm.n_blk;
+  // causal rows have more candidates the later their block: the longest first
+  const int i = dm.causal ? dm.n_blk - 1 - unit % dm.n_blk : unit % dm.n_blk;
   const int bh = unit / dm.n_blk;  // b * Hq + h
   const int b = bh / dm.Hq, h = bh % dm.Hq;
   const int hk = h * dm.Hkv / dm.Hq;
@@ -406,7 +407,8 @@ __global__ __launch_bounds__(64) void indexer_pivot(PisaDims dm, const T *__rest
                                                     int32_t *__restrict__ cand, int32_t *diag) {
   __shared__ Shared sh;
   const int unit = blockIdx.x;
-  const int gm = unit % dm.n_sel;
+  // causal rows have more candidates the later their group: the longest first
+  const int gm = dm.causal ? dm.n_sel - 1 - unit % dm.n_sel : unit % dm.n_sel;
   const int bh = unit / dm.n_sel;
   const int b = bh / dm.Hq, h = bh % dm.Hq;
   const int hk = h * dm.Hkv / dm.Hq;
@@ -955,7 +957,8 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int cq = logical % nchunk;
   const int rest = logical / nchunk;
-  const int iblk = rest % dm.n_blk;
+  // causal rows have more candidates the later their block: the longest first
+  const int iblk = dm.causal ? dm.n_blk - 1 - rest % dm.n_blk : rest % dm.n_blk;
   const int bk = rest / dm.n_blk;
   const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
   const uint16_t *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
