@@ -102,7 +102,7 @@ struct Cfg {
   static constexpr int STGCH = STG_BYTES / 1024;               // staging kilobytes per batch
   static_assert(CPS % (NW / 2) == 0 && HCH % (NW / 2) == 0 && STGCH % (NW / 2) == 0,
                 "DMA must split evenly over the issuing waves");
-  static_assert(kNB * (D / 8) <= NT, "one table unit per thread");
+  static_assert(kNB * (D / 8) <= NT / 2 && 2 * D <= NT / 2, "a table unit per thread, in either half");
 };
 
 // Instruction order of a pipelined step, for the scheduler: a few LDS reads
@@ -569,38 +569,56 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
     const float *stg = reinterpret_cast<const float *>(stgb);
     // Taylor tables of the batch that starts at entry b0, from its staged
     // kbar / vsum rows: kbar as bf16 hi + lo rows (swizzled like K tiles),
-    // Sigma^T as bf16 hi and lo in the perm16 layout, and n_j.  Built by the
-    // waves that issue no DMA first (thread (tid + NT / 2) % NT).  Every
+    // Sigma^T as bf16 hi and lo in the perm16 layout, and n_j.  At first
+    // order the waves that issue no DMA build both tables (thread
+    // (tid + NT / 2) % NT), between the group barriers; otherwise the two
+    // tables are split between the two halves of the workgroup.  Every
     // thread calls it: at first order the staged rows overlay the tables, so
     // all of them are read before the workgroup meets and any is written.
     auto build = [&](int b0) {
       const int nb = min(kNB, n_ty - b0);
       const int bt = (tid + NT / 2) % NT;
-      const bool act = bt < kNB * (D / 8);
-      const int en = bt / (D / 8), ch = bt % (D / 8);
+      // without first order every wave builds: the kbar rows on waves 0 ..
+      // NW / 2 - 1, Sigma^T on the others
+      const int bk2 = order1 ? bt : tid, bs2 = order1 ? bt : tid - NT / 2;
+      // kbar rows: thread (entry en, 16-byte chunk ch)
+      const bool act = bk2 >= 0 && bk2 < kNB * (D / 8) && (order1 || tid < NT / 2);
+      const int en = bk2 / (D / 8), ch = bk2 % (D / 8);
       u32x4_t hi = {0, 0, 0, 0}, lo4 = {0, 0, 0, 0};
-      float sv[8];
       float njv = 0.f;
-      {
-        if (act && en < nb) {
-          const int j = tyl[b0 + en];
-          const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8);
-          const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8 + 4);
-          const f32x4_t v0 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8);
-          const f32x4_t v1 = *reinterpret_cast<const f32x4_t *>(stg + (kNB + en) * D + ch * 8 + 4);
-          const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      if (act && en < nb) {
+        const int j = tyl[b0 + en];
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t *>(stg + en * D + ch * 8 + 4);
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t pk = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-            hi[i] = pk;
-            lo4[i] = pack_bf16x2(x[2 * i] - bf16lo(pk), x[2 * i + 1] - bf16hi(pk));
-          }
-          sv[0] = v0[0]; sv[1] = v0[1]; sv[2] = v0[2]; sv[3] = v0[3];
-          sv[4] = v1[0]; sv[5] = v1[1]; sv[6] = v1[2]; sv[7] = v1[3];
-          njv = (float)min(dm.bs, dm.L - j * dm.bs);
-        } else {
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t pk = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+          hi[i] = pk;
+          lo4[i] = pack_bf16x2(x[2 * i] - bf16lo(pk), x[2 * i + 1] - bf16hi(pk));
+        }
+        njv = (float)min(dm.bs, dm.L - j * dm.bs);
+      }
+      // Sigma^T [feature][16 entries]: entry en at K position perm16(en),
+      // the two 16-byte halves of a row swapped on odd groups of 8 rows.
+      // Thread (feature f, physical half ph) gathers the eight entries of
+      // that half from the staged vsum rows and writes them in one piece.
+      const bool acts = bs2 >= 0 && bs2 < 2 * D && (order1 || tid >= NT / 2);
+      const int f = bs2 >> 1, ph = bs2 & 1;
+      const int lh = ph ^ ((f >> 3) & 1);   // logical half: K positions 8 lh .. 8 lh + 7
+      u32x4_t shi = {0, 0, 0, 0}, slo = {0, 0, 0, 0};
+      if (acts) {
+        float sv[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) sv[i] = 0.f;
+        for (int k = 0; k < 8; ++k) {
+          const int e2 = perm16(8 * lh + k);
+          sv[k] = e2 < nb ? stg[(kNB + e2) * D + f] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t pk = pack_bf16x2(sv[2 * i], sv[2 * i + 1]);
+          shi[i] = pk;
+          slo[i] = pack_bf16x2(sv[2 * i] - bf16lo(pk), sv[2 * i + 1] - bf16hi(pk));
         }
       }
       if (order1) lds_barrier();
@@ -609,18 +627,10 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
         const int sw = (ch ^ kswz<D>(en)) << 4;
         *reinterpret_cast<u32x4_t *>(kbh + en * (2 * D) + sw) = hi;
         *reinterpret_cast<u32x4_t *>(kbl + en * (2 * D) + sw) = lo4;
-        // Sigma^T [feature][16 entries]: entry en at K position perm16(en),
-        // the two 16-byte halves of a row swapped on odd groups of 8 rows
-        const int pos = perm16(en);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int f = ch * 8 + i;
-          const uint32_t shi = f32_to_bf16(sv[i]);
-          const uint32_t slo = f32_to_bf16(sv[i] - bf16_to_f32(shi));
-          const int off = f * (2 * kNB) + (((pos >> 3) ^ ((f >> 3) & 1)) << 4) + ((pos & 7) << 1);
-          *reinterpret_cast<uint16_t *>(sth + off) = (uint16_t)shi;
-          *reinterpret_cast<uint16_t *>(stl + off) = (uint16_t)slo;
-        }
+      }
+      if (acts) {
+        *reinterpret_cast<u32x4_t *>(sth + f * (2 * kNB) + (ph << 4)) = shi;
+        *reinterpret_cast<u32x4_t *>(stl + f * (2 * kNB) + (ph << 4)) = slo;
       }
     };
     uint32_t tmask = 0;
