@@ -937,7 +937,12 @@ __device__ __attribute__((noinline)) void exact_select(Shared &sh, const uint16_
   wave_lds_sync();
 }
 
-template <int D>
+// ROWS: the same kernel for block rows (no groups): a workgroup takes 32
+// block rows of one KV head, in (query block, head) order, and writes each
+// row's kept list (sinks, then the top-k ascending) instead of a proxy list;
+// there is no member pass.  NSX: 64-candidate slots per lane (n_blk <= 64 NSX),
+// which sizes the selection's per-lane arrays.
+template <int D, bool ROWS, int NSX>
 __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, const uint16_t *__restrict__ Q,
                                                                  const uint16_t *__restrict__ qsel,
                                                                  const uint16_t *__restrict__ ksel,
@@ -950,16 +955,17 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, l = tid & 63, lq = l & 31, hl = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = dm.group;
+  const int g = ROWS ? dm.bs : dm.group;
   const int gpb = dm.bs / g;                  // groups per block
-  const int npb = dm.ratio * gpb;             // proxies per (KV head, block)
+  // proxies per (KV head, block); block rows: rows per KV head
+  const int npb = ROWS ? dm.ratio * dm.n_blk : dm.ratio * gpb;
   const int nchunk = (npb + kPX - 1) / kPX;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int cq = logical % nchunk;
-  const int rest = logical / nchunk;
   // causal rows have more candidates the later their block: the longest first
-  const int iblk = dm.causal ? dm.n_blk - 1 - rest % dm.n_blk : rest % dm.n_blk;
-  const int bk = rest / dm.n_blk;
+  const int cq = (ROWS && dm.causal) ? nchunk - 1 - logical % nchunk : logical % nchunk;
+  const int rest = logical / nchunk;
+  const int iblk = ROWS ? 0 : dm.causal ? dm.n_blk - 1 - rest % dm.n_blk : rest % dm.n_blk;
+  const int bk = ROWS ? rest : rest / dm.n_blk;
   const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
   const uint16_t *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
   float *S = reinterpret_cast<float *>(lds + LY::S);
@@ -978,8 +984,14 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   // proxy pp of this workgroup -> (query head, group), candidate count
   auto proxy = [&](int pl, int &h, int &gm, int &nc) -> bool {
     const int pp = cq * kPX + pl;
-    h = hk * dm.ratio + pp / gpb;
-    gm = iblk * gpb + pp % gpb;
+    if constexpr (ROWS) {   // row pp: query block pp / ratio of head pp % ratio
+      const int ppc = pp < npb ? pp : npb - 1;
+      h = hk * dm.ratio + ppc % dm.ratio;
+      gm = ppc / dm.ratio;
+    } else {
+      h = hk * dm.ratio + pp / gpb;
+      gm = iblk * gpb + pp % gpb;
+    }
     int own, lo;
     nc = pisa_row_geometry(dm, gm * g, &own, &lo);
     return pp < npb && gm * g < dm.L;
@@ -1031,7 +1043,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
 
   // ---- 2. proxy top-C
   {
-    constexpr int NS = kMaxSlots;
+    constexpr int NS = NSX;
     float skr[NS];   // |ksel_c| of this lane's slots, shared by every proxy
     int cid[NS];
 #pragma unroll
@@ -1043,14 +1055,27 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       int h, gm, nc;
       if (!proxy(pl, h, gm, nc)) continue;
       const int c0 = min(dm.sink, nc);   // sink blocks are no candidates of the list
-      const int C = min(dm.n_cand, nc - c0);
-      int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
-      uint16_t *lout = LIST + pl * kPCap;
+      const int C = min(ROWS ? dm.topk : dm.n_cand, nc - c0);
+      int32_t *gout;
+      int glen;
+      uint16_t *lout;
+      if constexpr (ROWS) {   // the row's kept list: sinks, then the selection
+        int32_t *row = idx + ((size_t)(b * dm.Hq + h) * dm.n_rows + gm) * dm.klist;
+        for (int c = l; c < c0; c += 64) row[c] = c;
+        gout = row + c0;
+        glen = dm.klist - c0;
+        lout = nullptr;
+      } else {
+        gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
+        glen = dm.n_cand;
+        lout = LIST + pl * kPCap;
+      }
       if (diag && l == 0) atomicAdd(&diag[0], 1);
-      if (C >= nc - c0) {   // every candidate
-        for (int c = l; c < C; c += 64) lout[c] = (uint16_t)(c0 + c);
+      if (C == 0 || C >= nc - c0) {   // no candidate to take, or every one
+        if (lout)
+          for (int c = l; c < C; c += 64) lout[c] = (uint16_t)(c0 + c);
         if (gout)
-          for (int c = l; c < dm.n_cand; c += 64) gout[c] = c < C ? c0 + c : -1;
+          for (int c = l; c < glen; c += 64) gout[c] = c < C ? c0 + c : -1;
         continue;
       }
       const float cb = kG * SPN[pl];
@@ -1068,11 +1093,11 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
         }
       }
       if (fast_select<NS>(sc, dl, valid, nsl, C, sel)) {
-        write_sorted_lds<NS>(sel, cid, lout, gout, dm.n_cand);
+        write_sorted_lds<NS>(sel, cid, lout, gout, glen);
       } else {
         const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
         if (!rescore_select<D, NS>(S + pl * LY::SLD, nullptr, c0, nc, C, cb, SKN, route ? MC : nullptr, lam,
-                                   vec, PVw, kbase, lout, gout, dm.n_cand, diag) &&
+                                   vec, PVw, kbase, lout, gout, glen, diag) &&
             l == 0)
           defp[atomicAdd(&defn[0], 1)] = pl;
       }
@@ -1086,13 +1111,20 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       int h, gm, nc;
       proxy(pl, h, gm, nc);
       const int c0 = min(dm.sink, nc);
-      const int C = min(dm.n_cand, nc - c0);
-      int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
-      exact_select<D, kMaxSlots>(sh, kbase, nullptr, c0, nc - c0, C, route ? MC : nullptr, lam,
-                                 qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D, LIST + pl * kPCap, gout,
-                                 dm.n_cand, diag);
+      const int C = min(ROWS ? dm.topk : dm.n_cand, nc - c0);
+      const uint16_t *vec = qsel + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * D;
+      if constexpr (ROWS) {   // the sinks are written already
+        int32_t *row = idx + ((size_t)(b * dm.Hq + h) * dm.n_rows + gm) * dm.klist;
+        exact_select<D, NSX>(sh, kbase, nullptr, c0, nc - c0, C, route ? MC : nullptr, lam, vec, nullptr,
+                                   row + c0, dm.klist - c0, diag);
+      } else {
+        int32_t *gout = cand ? cand + ((size_t)(b * dm.Hq + h) * dm.n_sel + gm) * dm.n_cand : nullptr;
+        exact_select<D, NSX>(sh, kbase, nullptr, c0, nc - c0, C, route ? MC : nullptr, lam, vec,
+                             LIST + pl * kPCap, gout, dm.n_cand, diag);
+      }
     }
   }
+  if (ROWS) return;
   __syncthreads();
   if (dm.klist == 0) return;
 
@@ -1281,27 +1313,41 @@ __global__ void zero_diag(int32_t *d) {
   if (threadIdx.x < 16) d[threadIdx.x] = 0;
 }
 
+// PIVOT proxies and members, or block rows (ROWS), on the matrix cores: 32
+// proxies (rows) per workgroup
+template <int D, bool ROWS, int NSX>
+hipError_t launch_pivot_mfma(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
+                             const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st) {
+  using LY = PivotLayout;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&indexer_pivot_mfma<D, ROWS, NSX>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::TOTAL);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int npb = ROWS ? dm.ratio * dm.n_blk : dm.ratio * (dm.bs / dm.group);
+  const unsigned chunks = (unsigned)((npb + kPX - 1) / kPX);
+  const unsigned grid = ROWS ? (unsigned)dm.B * dm.Hkv * chunks : (unsigned)dm.B * dm.Hkv * dm.n_blk * chunks;
+  indexer_pivot_mfma<D, ROWS, NSX><<<grid, kPW * 64, LY::TOTAL, st>>>(
+      dm, static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(qsel),
+      static_cast<const uint16_t *>(ksel), mcov, idx, cand, diag);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel, const float *mcov,
                     int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st) {
   if (diag) zero_diag<<<1, 64, 0, st>>>(diag);
   if constexpr (sizeof(T) == 2) {
-    if (dm.group >= 1 && dm.n_cand <= kPCap && dm.group <= kPG) {
-      using LY = PivotLayout;
-      static bool attr_set = false;
-      if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&indexer_pivot_mfma<D>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LY::TOTAL);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-      }
-      const int npb = dm.ratio * (dm.bs / dm.group);
-      const unsigned grid = (unsigned)dm.B * dm.Hkv * dm.n_blk * ((npb + kPX - 1) / kPX);
-      indexer_pivot_mfma<D><<<grid, kPW * 64, LY::TOTAL, st>>>(dm, static_cast<const uint16_t *>(Q),
-                                                               static_cast<const uint16_t *>(qsel),
-                                                               static_cast<const uint16_t *>(ksel), mcov, idx,
-                                                               cand, diag);
-      return hipGetLastError();
+    if ((dm.group >= 1 && dm.n_cand <= kPCap && dm.group <= kPG) || (dm.group == 0 && dm.n_blk <= kPNc)) {
+      const bool rows = dm.group == 0;
+      if (dm.n_blk <= 256) return rows ? launch_pivot_mfma<D, true, 4>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
+                                       : launch_pivot_mfma<D, false, 4>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st);
+      if (dm.n_blk <= 512) return rows ? launch_pivot_mfma<D, true, 8>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
+                                       : launch_pivot_mfma<D, false, 8>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st);
+      return rows ? launch_pivot_mfma<D, true, 16>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
+                  : launch_pivot_mfma<D, false, 16>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st);
     }
   }
   if (dm.group >= 1) {
