@@ -537,7 +537,8 @@ struct PivotLayout {
   static constexpr int MC = SPN + kPX * 4;             // fp32 [kPNc] covariance norms (routing)
   static constexpr int PV = MC + kPNc * 4;             // fp32 [kPW][128] row vector under re-score
   static constexpr int LIST = PV + kPW * 128 * 4;      // uint16 [kPX][kPCap] proxy lists, ascending
-  static constexpr int DEFN = LIST + kPX * kPCap * 2;  // int [4]: deferred proxies, deferred members
+  static constexpr int DEFN = LIST + kPX * kPCap * 2;  // int [4]: deferred proxies, deferred members,
+                                                       // next proxy of passes 2 and 3
   static constexpr int DEFP = DEFN + 16;               // int [kPX]
   static constexpr int DEFM = DEFP + kPX * 4;          // int [kPX * kPG] (token * 64 + proxy)
   static constexpr int TOTAL = DEFM + kPX * kPG * 4;
@@ -1000,6 +1001,13 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   const bool pval = proxy(lq, ph, pgm, pnc);
   const int ncmax = __builtin_amdgcn_readfirstlane(wave_max_f32(pval ? (float)pnc : 0.f));
   if (tid < 4) defn[tid] = 0;
+  // passes 2 and 3 hand proxies to the waves one at a time from a counter, so
+  // a wave held up by a re-score does not hold up the workgroup's last proxy
+  auto next_proxy = [&](int *ctr) -> int {
+    int v = 0;
+    if (l == 0) v = atomicAdd(ctr, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
   if (route)   // this kv head's covariance norms (routing term lam * MC[j])
     for (int j = tid; j < dm.n_blk; j += kPW * 64) MC[j] = mcov[((size_t)b * dm.Hkv + hk) * dm.n_blk + j];
 
@@ -1051,7 +1059,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
       cid[s] = s * 64 + l;
       skr[s] = cid[s] < ncmax ? SKN[cid[s]] : 0.f;
     }
-    for (int pl = w; pl < kPX; pl += kPW) {
+    for (int pl = next_proxy(&defn[2]); pl < kPX; pl = next_proxy(&defn[2])) {
       int h, gm, nc;
       if (!proxy(pl, h, gm, nc)) continue;
       const int c0 = min(dm.sink, nc);   // sink blocks are no candidates of the list
@@ -1138,7 +1146,7 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
     return out + ct;
   };
   float *Mw = S + w * kPM * LY::MLD;
-  for (int pl = w; pl < kPX; pl += kPW) {
+  for (int pl = next_proxy(&defn[3]); pl < kPX; pl = next_proxy(&defn[3])) {
     int h, gm, nc;
     if (!proxy(pl, h, gm, nc)) continue;
     const int C = min(dm.n_cand, nc - min(dm.sink, nc));
