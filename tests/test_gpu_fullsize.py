@@ -10,10 +10,16 @@ recomputes what it can afford:
 * the outputs of whole query blocks of that head, every row of them: the
   first block, the last (ragged where L is not a multiple of the block) and
   two seeded blocks in between (each row of them takes its Taylor terms in
-  several batches of the kernel), with the mean-abs bar over those rows.
+  several batches of the kernel), with the mean-abs bar over those rows;
+* for head (0, 0), every row of the head: outputs and lse of all L tokens,
+  the oracle's attention split into chunks of 1024 tokens on a thread pool,
+  max-abs per chunk and mean-abs over the whole head.
 Bar: selections and pooled vectors bit-exact; outputs within max-abs 2e-2 /
 mean-abs 2e-3 (bf16) or 1e-4 (fp32); lse within 1e-2 / 1e-5.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -109,6 +115,24 @@ def test_fullsize(name):
         assert d.max() <= tol["max_abs"], f"max abs error {d.max()}"
         assert d.mean() <= tol["mean_abs"], f"mean abs error {d.mean()}"
         assert np.abs(l_gpu - l_ref).max() <= tol["lse"], f"lse error {np.abs(l_gpu - l_ref).max()}"
+        if (b, h) == (0, 0):   # the whole head, every row
+            chunks = [np.arange(t0, min(wl.L, t0 + 1024)) for t0 in range(0, wl.L, 1024)]
+            print(f"[fullsize] {name}: oracle attention of the whole head ({wl.L} rows, "
+                  f"{len(chunks)} chunks)", flush=True)
+            with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+                refs = list(ex.map(lambda tk: po.attend_tokens(qa, ka, va, ref, r_idx, P1, 0, 0, tk), chunks))
+            o_all = out[b, h].cpu().double().numpy()
+            l_all = lse[b, h].cpu().double().numpy()
+            assert np.isfinite(o_all).all()
+            s_abs, n_el = 0.0, 0
+            for tk, (o_ref, l_ref) in zip(chunks, refs):
+                d = np.abs(o_all[tk] - o_ref)
+                assert d.max() <= tol["max_abs"], f"rows {tk[0]}..{tk[-1]}: max abs error {d.max()}"
+                assert np.abs(l_all[tk] - l_ref).max() <= tol["lse"], f"rows {tk[0]}..{tk[-1]}: lse error"
+                s_abs += d.sum()
+                n_el += d.size
+            print(f"[fullsize] {name} b=0 h=0 whole head: mean_abs={s_abs / n_el:.3e}", flush=True)
+            assert s_abs / n_el <= tol["mean_abs"], f"whole head: mean abs error {s_abs / n_el}"
         # whole query blocks, every row
         for i in _blocks(wl, rng):
             toks = np.arange(i * wl.block, min(wl.L, (i + 1) * wl.block))
