@@ -132,6 +132,20 @@ PARITY_CASES = {
     "llm_pivot_s_hyb": WORKLOADS["llm_pivot"].replace(name="llm_pivot_s_hyb", Hq=4, Hkv=2,
                                                       L=1024 + 40, topk=4, n_cand=8,
                                                       taylor="hybrid"),
+    # zero order / hybrid order over more than two batches of 16 Taylor
+    # entries (the staged batch tables run two batches ahead)
+    "video_dit_m_o0": WORKLOADS["video_dit"].replace(name="video_dit_m_o0", Hq=2, Hkv=2,
+                                                     L=5120, grid=(1, 40, 128), topk=4,
+                                                     taylor="order0"),
+    "video_dit_m_hyb": WORKLOADS["video_dit"].replace(name="video_dit_m_hyb", Hq=2, Hkv=2,
+                                                      L=5120, grid=(1, 40, 128), topk=4,
+                                                      taylor="hybrid"),
+    "image_dit_m_hyb": WORKLOADS["image_dit"].replace(name="image_dit_m_hyb", B=1, Hq=2,
+                                                      Hkv=2, L=4096, grid=(64, 64), topk=8,
+                                                      taylor="hybrid"),
+    "llm_swa_m_hyb": WORKLOADS["llm_swa"].replace(name="llm_swa_m_hyb", B=1, Hq=4, Hkv=1,
+                                                  L=6400 + 24, window=384, topk=4,
+                                                  taylor="hybrid"),
     # attention sinks: block-row and PIVOT indexers, every attention kernel
     "llm_swa_s_sink": WORKLOADS["llm_swa"].replace(name="llm_swa_s_sink", B=1, Hq=8, Hkv=2,
                                                    L=2048 + 24, window=384, topk=4, sink=2),
