@@ -90,8 +90,7 @@ struct Cfg {
   static_assert(STG_BYTES == TY_AL - TY_KBH, "the staging area overlays the four batch tables");
   static_assert(STG_BYTES <= HT, "the staging area fits a ring slot");
   static constexpr int MAIN = EX_END > TY_END ? EX_END : TY_END;
-  static constexpr int LST = MAIN;                            // uint16 [P][kMaxK] kept lists
-  static constexpr int PRV = LST + P * kMaxK * 2;             // uint16 [P][kMaxK] private parts
+  static constexpr int PRV = MAIN;                            // uint16 [P][kMaxK] private parts
   static constexpr int SHL = PRV + P * kMaxK * 2;             // uint16 [kMaxK] shared by all parts
   static constexpr int KBM = SHL + kMaxK * 2;                 // u32 [P][32] kept bitmaps
   static constexpr int ITB = KBM + P * 32 * 4;                // u32 [32] intersection bitmap
@@ -164,37 +163,44 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
   int own, lo;
   const int nc = pisa_row_geometry(dm, iblk * BS, &own, &lo);
 
-  uint16_t *lst = reinterpret_cast<uint16_t *>(lds + C::LST);
   uint16_t *prv = reinterpret_cast<uint16_t *>(lds + C::PRV);
   uint16_t *shl = reinterpret_cast<uint16_t *>(lds + C::SHL);
   uint32_t *kbm = reinterpret_cast<uint32_t *>(lds + C::KBM);
   uint32_t *itb = reinterpret_cast<uint32_t *>(lds + C::ITB);
   uint16_t *tyl = reinterpret_cast<uint16_t *>(lds + C::TYL);
-  int *cnt = reinterpret_cast<int *>(lds + C::CNT);   // [p] private counts, [4] shared, [7] Taylor, [8 + p] kept
+  int *cnt = reinterpret_cast<int *>(lds + C::CNT);   // [p] private counts, [4] shared, [7] Taylor
 
   // ---- 1. kept lists per part; blocks kept by every part (walked once, in
   // one shared LDS region) and each part's private rest; union of the
-  // parts' Taylor sets
+  // parts' Taylor sets.  The kept set is the set of list entries that are
+  // candidates of the row, 0 <= j < nc: other entries (padding, blocks of the
+  // window range or past it, garbage in a caller's list) are dropped, and the
+  // lists are rebuilt ascending from bitmaps, so order and repeats do not
+  // matter.  The part's first wave reads the list, one entry per lane.
   for (int i = tid; i < P * 32; i += NT) kbm[i] = 0;
-  __syncthreads();
-  if (rg == 0 && l == 0) {
-    // the kept set is the set of list entries that are candidates of the
-    // row, 0 <= j < nc: other entries (padding, blocks of the window range or
-    // past it, garbage in a caller's list) are dropped, and the list is
-    // rebuilt ascending from the bitmap, so order and repeats do not matter
-    int c = 0;
-    if (pvalid && a.idx && dm.topk > 0) {
-      const int32_t *row = a.idx + ((size_t)(b * dm.Hq + h) * dm.n_rows + iblk) * dm.topk;
-      for (int k = 0; k < dm.topk; ++k) {
-        const int j = row[k];
-        if (pisa_list_entry_kept(j, nc)) kbm[part * 32 + (j >> 5)] |= 1u << (j & 31);
+  const bool lister = rg == 0 && pvalid && a.idx && dm.topk > 0;
+  const int32_t *lrow = lister ? a.idx + ((size_t)(b * dm.Hq + h) * dm.n_rows + iblk) * dm.topk : nullptr;
+  const int j0 = lister && l < dm.topk ? lrow[l] : -1;
+
+  // ---- 2. Q fragments (B operand: query lq, features 16 ks + 8 hl .. + 7),
+  // issued here so that they land during the list work (the barriers below
+  // wait for LDS operations only)
+  const uint16_t *Qh = static_cast<const uint16_t *>(a.Q) + ((size_t)(b * dm.Hq + h) * dm.L) * D;
+  u32x4_t qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = valid ? *reinterpret_cast<const u32x4_t *>(Qh + (size_t)t * D + ks * 16 + hl * 8)
+                   : u32x4_t{0, 0, 0, 0};
+  lds_barrier();   // the bitmaps are cleared
+  if (lister) {
+    if (pisa_list_entry_kept(j0, nc)) atomicOr(&kbm[part * 32 + (j0 >> 5)], 1u << (j0 & 31));
+    if (LONG)
+      for (int k = 64 + l; k < dm.topk; k += 64) {
+        const int j = lrow[k];
+        if (pisa_list_entry_kept(j, nc)) atomicOr(&kbm[part * 32 + (j >> 5)], 1u << (j & 31));
       }
-      for (int wd = 0; wd * 32 < nc; ++wd)
-        for (uint32_t m = kbm[part * 32 + wd]; m; m &= m - 1) lst[part * kMaxK + c++] = (uint16_t)(wd * 32 + __ffs(m) - 1);
-    }
-    cnt[8 + part] = c;
   }
-  __syncthreads();
+  lds_barrier();
   if (w == 0) {
     const int nwords = (dm.n_blk + 31) >> 5;
     uint32_t ib = l < nwords ? 0xFFFFFFFFu : 0u, tb = 0;
@@ -222,25 +228,15 @@ __global__ __launch_bounds__(NT, 1) void attn_blocks(AttnArgs a) {
       cnt[7] = it;
     }
   }
-  __syncthreads();
-  if (rg == 0 && l == 0) {
-    int c = 0;
-    const int nk = cnt[8 + part];
-    for (int k = 0; k < nk; ++k) {
-      const int j = lst[part * kMaxK + k];
-      if (!((itb[j >> 5] >> (j & 31)) & 1u)) prv[part * kMaxK + c++] = (uint16_t)j;
-    }
-    cnt[part] = c;
+  lds_barrier();
+  if (rg == 0) {   // the part's private blocks: kept, not by every part; word l on lane l
+    const uint32_t pw = l < 32 ? kbm[part * 32 + l] & ~itb[l] : 0u;
+    const int cp = __popc(pw), ip = wave_incl_scan(cp);
+    int pos = ip - cp;
+    for (uint32_t m = pw; m; m &= m - 1) prv[part * kMaxK + pos++] = (uint16_t)(l * 32 + __ffs(m) - 1);
+    if (l == 63) cnt[part] = ip;
   }
-
-  // ---- 2. Q fragments (B operand: query lq, features 16 ks + 8 hl .. + 7)
-  const uint16_t *Qh = static_cast<const uint16_t *>(a.Q) + ((size_t)(b * dm.Hq + h) * dm.L) * D;
-  u32x4_t qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qf[ks] = valid ? *reinterpret_cast<const u32x4_t *>(Qh + (size_t)t * D + ks * 16 + hl * 8)
-                   : u32x4_t{0, 0, 0, 0};
-  __syncthreads();
+  lds_barrier();
   const int cnt_me = __builtin_amdgcn_readfirstlane(cnt[part]);   // private blocks of this part
   const int n_ty = __builtin_amdgcn_readfirstlane(cnt[7]);
   const int n_s = __builtin_amdgcn_readfirstlane(cnt[4]) * SPB;      // shared steps
