@@ -7,8 +7,13 @@
 // queries) scores the candidates once and keeps C of them; each member of the
 // group re-ranks only that list with its own query.
 //
-// One wavefront per selection unit (a block row, or a PIVOT group with its
-// members).  Selection is bit-exact with respect to the exact real scores:
+// bf16 (indexer_pivot_mfma): a workgroup takes 32 selection rows of one KV
+// head (block rows, or PIVOT proxies followed by their members), scores them
+// on MFMA and selects each row on one wave in three tiers (fast fp32 with a
+// certified bound, float64 re-score of the straddling candidates, exact);
+// see the comment above that kernel.  fp32 (indexer_blockrows,
+// indexer_pivot): one wavefront per selection unit, select_row below.
+// Selection is bit-exact with respect to the exact real scores; select_row:
 //   1. float64 scores (the bf16 / fp32 products are exact in float64) with a
 //      rigorous rounding bound  |s - S| <= gamma_D ||p|| ||k||;
 //   2. radix select (8-bit digits, LDS histograms) of the n-th largest unique
