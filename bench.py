@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_F32_VALU_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12   # fp32 FMA on the VALU, not packed: 78.6
+PEAK_F32_DATASHEET_TFLOPS = 157.3                     # the datasheet's fp32 vector figure (packed fp32)
 # source of the attention kernel that runs for block rows (True) / PIVOT rows
 ATTN_SRC = {"blocks": os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn_blocks.hip"),
             "pivot_union": os.path.join(ROOT, "piecewise_attention_dit_amd", "csrc", "attn.hip"),
@@ -515,6 +516,10 @@ def main():
         "roofline": {"bound": peak_kind, "kernel": "pisa_sparse_attn_fwd",
                      "achieved": round(attn_achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / peak, 4),
+                     **({} if wl.dtype == "bf16" else
+                        {"peak_datasheet": PEAK_F32_DATASHEET_TFLOPS,
+                         "peak_note": "the path never forms packed fp32 (v_pk_*_f32), so its peak is the "
+                                      "non-packed VALU rate 256 CUs x 64 lanes x 2 FLOP x 2.4 GHz"}),
                      "traffic": hbm_traffic(ATTN_SRC["blocks" if wl.group == 0 else
                                                      "pivot_kg" if ws_attn_need else "pivot_union"], wl.name)
                      if wl.dtype == "bf16" else None},
