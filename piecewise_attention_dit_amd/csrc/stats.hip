@@ -296,16 +296,54 @@ __global__ __launch_bounds__(kStatsThreads) void kv_stats_f32(PisaDims dm, const
   }
   if (dm.taylor != 2) return;
   __syncthreads();
-  // HT[e][c] = sum_n v[n][e] (k[n][c] - kbar_c): each thread owns outputs
-  // (e, c) with c = tid % D and e stepping by kStatsThreads / D.
-  float *Hb = HT + ((size_t)bh * dm.n_blk + j) * D * D;
-  const int c = tid % D;
-  const float mc = kmean[c];
-  for (int e = tid / D; e < D; e += PARTS) {
-    float s = 0.f;
-    for (int t = 0; t < n; ++t) s = fmaf(Vb[(size_t)t * D + e], Kb[(size_t)t * D + c] - mc, s);
-    Hb[(size_t)e * D + c] = s;
+  // HT[e][c] = sum_n v[n][e] (k[n][c] - kbar_c), summed over n in order.
+  // The block's rows pass through LDS kTC tokens at a time (keys centred
+  // there); thread (te, tc) of a 16 x 16 grid owns the RT x RT outputs
+  // e in [RT te, RT te + RT), c in [RT tc, RT tc + RT).
+  constexpr int kTC = 32, RT = D / 16;
+  static_assert(kStatsThreads == 256, "a 16 x 16 thread grid");
+  __shared__ __attribute__((aligned(16))) float kc[kTC * D];
+  __shared__ __attribute__((aligned(16))) float vr[kTC * D];
+  const int e0 = RT * (tid / 16), c0 = RT * (tid % 16);
+  float s[RT][RT];
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b2 = 0; b2 < RT; ++b2) s[a][b2] = 0.f;
+  for (int t0 = 0; t0 < n; t0 += kTC) {
+    const int nt = min(kTC, n - t0);
+    __syncthreads();   // the previous tokens are consumed
+    for (int i = tid; i < nt * D; i += kStatsThreads) {
+      const size_t g = (size_t)(t0 + i / D) * D + i % D;
+      kc[i] = Kb[g] - kmean[i % D];
+      vr[i] = Vb[g];
+    }
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      float ve[RT], kk[RT];
+#pragma unroll
+      for (int a = 0; a < RT; a += 4) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(vr + t * D + e0 + a);
+        const f32x4_t y = *reinterpret_cast<const f32x4_t *>(kc + t * D + c0 + a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ve[a + i] = x[i];
+          kk[a + i] = y[i];
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < RT; ++b2) s[a][b2] = fmaf(ve[a], kk[b2], s[a][b2]);
+    }
   }
+  float *Hb = HT + ((size_t)bh * dm.n_blk + j) * D * D;
+#pragma unroll
+  for (int a = 0; a < RT; ++a)
+#pragma unroll
+    for (int b2 = 0; b2 < RT; b2 += 4)
+      *reinterpret_cast<f32x4_t *>(Hb + (size_t)(e0 + a) * D + c0 + b2) =
+          f32x4_t{s[a][b2], s[a][b2 + 1], s[a][b2 + 2], s[a][b2 + 3]};
 }
 
 // ---------------------------------------------------------------------------
