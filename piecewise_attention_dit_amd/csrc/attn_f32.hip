@@ -345,17 +345,28 @@ __global__ __launch_bounds__(256) void attn_f32_rows(AttnArgs a) {
       }
     }
   };
-  // a D x D matrix (row-major) into ht, rows padded
-  auto stage_h = [&](const float *src) {
+  // a D x D matrix (row-major) into ht, rows padded: fetch_h loads this
+  // thread's share into registers (the loads stay in flight), put_h waits
+  // for the tile in use to be consumed and writes the share
+  constexpr int HS = D * D4 / 256;   // 16-byte pieces per thread
+  f32x4_t hreg[HS];
+  auto fetch_h = [&](const float *src) {
+#pragma unroll
+    for (int u = 0; u < HS; ++u) {
+      const int i = tid + 256 * u, e = i / D4, c4 = i % D4;
+      hreg[u] = *reinterpret_cast<const f32x4_t *>(src + (size_t)e * D + 4 * c4);
+    }
+  };
+  auto put_h = [&]() {
     __syncthreads();   // the previous tile is consumed
-    for (int i = tid; i < D * D4; i += 256) {
-      const int e = i / D4, c4 = i % D4;
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(src + (size_t)e * D + 4 * c4);
+#pragma unroll
+    for (int u = 0; u < HS; ++u) {
+      const int i = tid + 256 * u, e = i / D4, c4 = i % D4;
       float *d = ht + e * KP + 4 * c4;
-      d[0] = v[0];
-      d[1] = v[1];
-      d[2] = v[2];
-      d[3] = v[3];
+      d[0] = hreg[u][0];
+      d[1] = hreg[u][1];
+      d[2] = hreg[u][2];
+      d[3] = hreg[u][3];
     }
     __syncthreads();
   };
@@ -421,9 +432,12 @@ __global__ __launch_bounds__(256) void attn_f32_rows(AttnArgs a) {
     for (int q = 0; q < kFW; ++q) ok[q] = l < nb;
     update(x, ok, njf, true, cr);
     pv(cr, nb);   // zero order: alpha sigma_j
-    if (taylor == 2) {   // first order: alpha scale q H_j, one H^T tile at a time
+    if (taylor == 2) {   // first order: alpha scale q H_j, one H^T tile at a time, the next in flight
+      const float *HTf = static_cast<const float *>(a.HT);
+      fetch_h(HTf + (soff + tl[tb0]) * D * D);
       for (int en = 0; en < nb; ++en) {
-        stage_h(static_cast<const float *>(a.HT) + (soff + tl[tb0 + en]) * D * D);
+        put_h();
+        if (en + 1 < nb) fetch_h(HTf + (soff + tl[tb0 + en + 1]) * D * D);
         float u[kFW][NE];
         qht(u);
 #pragma unroll
@@ -436,7 +450,8 @@ __global__ __launch_bounds__(256) void attn_f32_rows(AttnArgs a) {
     }
   }
   if (taylor == 3 && nt > 0) {   // hybrid: + (scale sum alpha) q Hbar (causal: the mean over [0, lo))
-    stage_h(static_cast<const float *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, lo));
+    fetch_h(static_cast<const float *>(a.HT) + hbar_offset(dm, b * dm.Hkv + hk, lo));
+    put_h();
     float u[kFW][NE];
     qht(u);
 #pragma unroll
