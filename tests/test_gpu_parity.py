@@ -101,6 +101,12 @@ def test_parity_cases(name):
     dict(L=1500, block=64, topk=2, d=64, taylor="order1"),
     dict(L=1700, block=64, topk=2, d=64, taylor="order1", causal=True, window=200),
     dict(L=2900, block=128, topk=2, d=64, taylor="order1"),
+    # fp32 block rows at d 128 (8 x 8 moment tiles per thread, two output
+    # features per lane), causal GQA with a window, and more than 64 Taylor
+    # blocks (two Taylor batches of the row-block kernel)
+    dict(L=700, block=128, topk=2, d=128, dtype="f32"),
+    dict(L=650, block=64, topk=3, d=128, dtype="f32", causal=True, window=100, Hq=4, Hkv=2),
+    dict(L=64 * 80 - 9, block=64, topk=2, d=64, dtype="f32"),
 ])
 def test_edge_cases(kw):
     base = dict(B=1, Hq=2, Hkv=2, L=256, d=128, dtype="bf16", block=64, topk=2, window=0, group=0,
