@@ -954,7 +954,8 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
                                                                  const uint16_t *__restrict__ ksel,
                                                                  const float *__restrict__ mcov,
                                                                  int32_t *__restrict__ idx,
-                                                                 int32_t *__restrict__ cand, int32_t *diag) {
+                                                                 int32_t *__restrict__ cand, int32_t *diag,
+                                                                 int blo, int nbr) {
   using LY = PivotLayout;
   constexpr int KS = D / 16;
   constexpr float kG = pivot_bound<KS>();
@@ -970,8 +971,9 @@ __global__ __launch_bounds__(kPW * 64, 1) void indexer_pivot_mfma(PisaDims dm, c
   // causal rows have more candidates the later their block: the longest first
   const int cq = (ROWS && dm.causal) ? nchunk - 1 - logical % nchunk : logical % nchunk;
   const int rest = logical / nchunk;
-  const int iblk = ROWS ? 0 : dm.causal ? dm.n_blk - 1 - rest % dm.n_blk : rest % dm.n_blk;
-  const int bk = ROWS ? rest : rest / dm.n_blk;
+  // PIVOT: query blocks [blo, blo + nbr) of the launch
+  const int iblk = ROWS ? 0 : blo + (dm.causal ? nbr - 1 - rest % nbr : rest % nbr);
+  const int bk = ROWS ? rest : rest / nbr;
   const int b = bk / dm.Hkv, hk = bk % dm.Hkv;
   const uint16_t *kbase = ksel + ((size_t)b * dm.Hkv + hk) * dm.n_blk * D;
   float *S = reinterpret_cast<float *>(lds + LY::S);
@@ -1330,7 +1332,9 @@ __global__ void zero_diag(int32_t *d) {
 // proxies (rows) per workgroup
 template <int D, bool ROWS, int NSX>
 hipError_t launch_pivot_mfma(const PisaDims &dm, const void *Q, const void *qsel, const void *ksel,
-                             const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st) {
+                             const float *mcov, int32_t *idx, int32_t *cand, int32_t *diag, hipStream_t st,
+                             int blo = 0, int nbr = -1) {
+  if (nbr < 0) nbr = dm.n_blk;
   using LY = PivotLayout;
   static bool attr_set = false;
   if (!attr_set) {
@@ -1341,10 +1345,10 @@ hipError_t launch_pivot_mfma(const PisaDims &dm, const void *Q, const void *qsel
   }
   const int npb = ROWS ? dm.ratio * dm.n_blk : dm.ratio * (dm.bs / dm.group);
   const unsigned chunks = (unsigned)((npb + kPX - 1) / kPX);
-  const unsigned grid = ROWS ? (unsigned)dm.B * dm.Hkv * chunks : (unsigned)dm.B * dm.Hkv * dm.n_blk * chunks;
+  const unsigned grid = ROWS ? (unsigned)dm.B * dm.Hkv * chunks : (unsigned)dm.B * dm.Hkv * nbr * chunks;
   indexer_pivot_mfma<D, ROWS, NSX><<<grid, kPW * 64, LY::TOTAL, st>>>(
       dm, static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(qsel),
-      static_cast<const uint16_t *>(ksel), mcov, idx, cand, diag);
+      static_cast<const uint16_t *>(ksel), mcov, idx, cand, diag, blo, nbr);
   return hipGetLastError();
 }
 
@@ -1355,6 +1359,19 @@ hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const v
   if constexpr (sizeof(T) == 2) {
     if ((dm.group >= 1 && dm.n_cand <= kPCap && dm.group <= kPG) || (dm.group == 0 && dm.n_blk <= kPNc)) {
       const bool rows = dm.group == 0;
+      if (!rows && dm.causal && dm.n_blk > 256) {
+        // causal proxies of query block i have at most i candidates: blocks
+        // [0, 256) take the 4-slot build, [256, 512) the 8-slot one, the
+        // rest 16 slots (fewer registers held, fewer spilled)
+        hipError_t e = hipSuccess;
+        if (dm.n_blk > 512)
+          e = launch_pivot_mfma<D, false, 16>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 512, dm.n_blk - 512);
+        if (e != hipSuccess) return e;
+        e = launch_pivot_mfma<D, false, 8>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 256,
+                                           (dm.n_blk < 512 ? dm.n_blk : 512) - 256);
+        if (e != hipSuccess) return e;
+        return launch_pivot_mfma<D, false, 4>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 0, 256);
+      }
       if (dm.n_blk <= 256) return rows ? launch_pivot_mfma<D, true, 4>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
                                        : launch_pivot_mfma<D, false, 4>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st);
       if (dm.n_blk <= 512) return rows ? launch_pivot_mfma<D, true, 8>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st)
