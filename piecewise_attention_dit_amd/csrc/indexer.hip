@@ -1361,11 +1361,16 @@ hipError_t launch_t(const PisaDims &dm, const void *Q, const void *qsel, const v
       const bool rows = dm.group == 0;
       if (!rows && dm.causal && dm.n_blk > 256) {
         // causal proxies of query block i have at most i candidates: blocks
-        // [0, 256) take the 4-slot build, [256, 512) the 8-slot one, the
-        // rest 16 slots (fewer registers held, fewer spilled)
+        // [0, 256) take the 4-slot build, [256, 512) the 8-slot one,
+        // [512, 768) 12 slots, the rest 16 (fewer registers held, fewer
+        // spilled)
         hipError_t e = hipSuccess;
+        if (dm.n_blk > 768)
+          e = launch_pivot_mfma<D, false, 16>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 768, dm.n_blk - 768);
+        if (e != hipSuccess) return e;
         if (dm.n_blk > 512)
-          e = launch_pivot_mfma<D, false, 16>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 512, dm.n_blk - 512);
+          e = launch_pivot_mfma<D, false, 12>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 512,
+                                              (dm.n_blk < 768 ? dm.n_blk : 768) - 512);
         if (e != hipSuccess) return e;
         e = launch_pivot_mfma<D, false, 8>(dm, Q, qsel, ksel, mcov, idx, cand, diag, st, 256,
                                            (dm.n_blk < 512 ? dm.n_blk : 512) - 256);
